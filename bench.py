@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the chain-and-schedule step on one MI355X.
+
+One step = the whole pass (schedule kernels + chain kernels + verified-token
+gather) through dspark_step on one batch of synthetic inputs already resident in
+HBM.  Per-step inputs (base logits, prev0, confidences) cycle through a pool of
+distinct seeded draws (far larger together than the 256 MB last-level cache);
+the Markov-head factors and cost tables stay fixed, as weights and start-up
+profiles do.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chain+schedule steps/sec at R=256,K=7,V=129280,r=256; % HBM roofline; sched µs"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def step_bytes(w) -> dict:
+    """Algorithmic HBM bytes of one step: every input read once, every output written once."""
+    e = 2 if w.dtype == 1 else 4
+    n = w.R * w.K
+    bmax = min(n, w.verify_len - 1 - w.T)
+    d = dict(base=w.R * w.K * w.V * e, factor_B=w.V * w.rank * e, factor_A_rows=n * w.rank * e,
+             prev0=w.R * 4, conf=n * 4, cost=(bmax + 1) * 4 + 4,
+             outputs=n * 4 * 6 + w.R * 4 + (w.R + 1) * 4 + 12)
+    d["total"] = sum(d.values())
+    return d
+
+
+def chain_launch_bytes(w) -> int:
+    """Algorithmic bytes of one chain-position launch: its base slice, the whole second
+    factor, the gathered key rows, the argmax keys and the previous tokens."""
+    e = 2 if w.dtype == 1 else 4
+    return w.R * w.V * e + w.V * w.rank * e + w.R * w.rank * e + w.R * 8 * 2 + w.R * 4
+
+
+def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
+    """The oracle as it stands, timed on this host: the chain of `rows` requests (all
+    positions, whole vocabulary) scaled to R requests, plus the full schedule."""
+    import oracle
+    from oracle import sched
+    sel = np.linspace(0, w.R - 1, rows).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.chain(step_in["base"], ins.A, ins.Bmat, w.dtype, step_in["prev0"], rows=sel)
+    t_chain = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sched.schedule(step_in["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
+    t_sched = time.perf_counter() - t0
+    per_step = t_chain * (w.R / rows) + t_sched
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 chain of {rows} of {w.R} requests (all {w.K} positions, V={w.V}) timed "
+                      f"{t_chain:.2f} s and scaled x{w.R / rows:.0f}; schedule of all {w.R * w.K} slots "
+                      f"timed {t_sched:.2f} s; single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="headline", choices=["tiny", "small", "mid", "headline", "large"])
+    ap.add_argument("--pool", type=int, default=4, help="distinct per-step input sets cycled through")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="requests in the oracle's timed chain sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the chain-and-schedule step has "
+                                   "no multi-GPU path in this build (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from confidence_scheduled_verification_amd import binding as B
+    from confidence_scheduled_verification_amd import inputs
+    from oracle import sched as osched
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(3)
+    B.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    log(f"bench: workload {w.name} R={w.R} K={w.K} V={w.V} rank={w.rank}; generating inputs")
+    ins = inputs.generate(w)
+    vc = B.dspark_force_monotone(ins.verify_cost_raw)
+    dc = B.dspark_force_monotone(ins.draft_cost_raw)
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    A = dev_t(ins.A)
+    Bm = dev_t(ins.Bmat)
+    Bt = torch.empty((w.V, w.rank), dtype=Bm.dtype, device=dev)
+    B.dspark_markov_prepare(Bm, w.dtype, Bt)
+    del Bm
+    vc_d, dc_d = dev_t(vc), dev_t(dc)
+    pool, host_steps = [], []
+    for k in range(args.pool):
+        st = inputs.generate_step(w, k)
+        host_steps.append(st)
+        pool.append((dev_t(st["base"]), dev_t(st["prev0"]), dev_t(st["conf"])))
+        log(f"bench: pool entry {k} uploaded")
+    ws = B.workspace(w.R, w.K, w.V, w.rank, w.dtype, device=dev)
+    out = B.StepBuffers(w.R, w.K, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(k):
+        base, prev0, conf = pool[k % len(pool)]
+        B.dspark_step(base, A, Bt, w.dtype, prev0, conf, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
+
+    for k in range(args.warmup):
+        run(k)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done; timing {args.steps}")
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        e0, e1, e2, e3 = ev[k]
+        e0.record(stream)
+        B.dspark_set_timing_events(e1, e2)
+        run(k)
+        e3.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.dspark_set_timing_events(None, None)
+    step_ms = np.array([ev[k][0].elapsed_time(ev[k][3]) for k in range(K)])
+    sched_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
+    chain_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
+    log(f"bench: wall {wall * 1e3 / K:.2f} ms/step, events {step_ms.mean() * 1e3:.1f} us/step "
+        f"(sched {sched_ms.mean() * 1e3:.1f} us, chain {chain_ms.mean() * 1e3:.1f} us)")
+
+    # Parity of the last timed step against the oracle (two sampled rows + the whole schedule).
+    import oracle
+    last = (K - 1) % len(pool)
+    parity = "not checked"
+    if True:
+        st = host_steps[last]
+        tok = out.tokens.cpu().numpy()
+        rows = [0, w.R - 1]
+        otok, olog, _ = oracle.chain(st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=rows, forced=tok,
+                                     want_logits=True)
+        ok = True
+        for q, r in enumerate(rows):
+            for i in range(w.K):
+                if otok[q, i] != tok[r, i]:
+                    xo, xg = olog[q, i, otok[q, i]], olog[q, i, tok[r, i]]
+                    ok &= bool(xo - xg <= 1e-4 * max(abs(xo), 1.0))
+        want = osched.schedule(st["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
+        ok &= int(out.b_star.item()) == want["b_star"]
+        ok &= float(out.best_obj.item()) == want["best_obj"]
+        ok &= np.array_equal(out.ver_idx.cpu().numpy(), want["ver_idx"])
+        ok &= np.array_equal(out.order.cpu().numpy(), want["order"])
+        parity = "ok" if ok else "MISMATCH"
+    log(f"bench: parity of the last step: {parity}")
+
+    sb = step_bytes(w)
+    launch_b = chain_launch_bytes(w)
+    launch_s = chain_ms.mean() * 1e-3 / w.K          # chain phase per step / launches per step
+    achieved = launch_b / launch_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "chain_pos_bf16_kernel" if w.dtype == 1 else "chain_pos_f32_kernel",
+                "bytes_per_launch": launch_b, "launches_per_step": w.K}
+    ms_per_step = wall * 1e3 / K
+    res = {
+        "metric": METRIC,
+        "value": round(K / wall, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: R={w.R} (of {w.R_all}), K={w.K}, V={w.V}, r={w.rank}, T={w.T}, "
+                               f"N_sampling={w.n_sampling}", "input_pool": len(pool)},
+        "roofline": roofline,
+        "step_bytes": sb["total"],
+        "step_hbm_frac": round(sb["total"] / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "step_us_events": round(float(step_ms.mean()) * 1e3, 2),
+        "sched_us": round(float(sched_ms.mean()) * 1e3, 2),
+        "chain_us": round(float(chain_ms.mean()) * 1e3, 2),
+        "parity_last_step": parity,
+        "status": int(status.item()),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(w, ins, host_steps[0], vc, dc, min(args.cpu_rows, w.R))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+"""Thin Python binding of libdspark.so (include/dspark.h).
+
+Argument marshalling only: every function here checks shapes, takes device
+pointers from torch tensors and calls the C entry point of the same name on the
+current (or given) HIP stream.  No step of the method runs in Python.  The
+library is loaded on first use and a missing library raises immediately -- there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdspark.so")
+
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+STATUS_PREV_CLAMPED = 1
+STATUS_CONF_SANITIZED = 2
+STATUS_COST_INVALID = 4
+MAX_SLOTS = 16384
+
+EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
+           "dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
+           "dspark_step", "dspark_set_timing_events", "dspark_force_monotone"]
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdspark error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libdspark.so (built in-tree by build.py).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m "
+                               "confidence_scheduled_verification_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.dspark_last_error.restype = ctypes.c_char_p
+        L.dspark_last_error.argtypes = []
+        L.dspark_version.restype = ctypes.c_char_p
+        L.dspark_version.argtypes = []
+        L.dspark_workspace_bytes.restype = sz
+        L.dspark_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.dspark_markov_prepare.argtypes = [p, i, i, i, p, p]
+        L.dspark_chain.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, p, sz, p]
+        L.dspark_survival.argtypes = [p, i, i, p, p, p]
+        L.dspark_topb_select.argtypes = [p, i, i, p, p, p, p]
+        L.dspark_choose_budget.argtypes = [p, i, i, i, i, p, i, p, i, p, p, p, p, p]
+        L.dspark_allocate.argtypes = [p, p, i, i, p, p, p, p, p, p]
+        L.dspark_step.argtypes = [p, p, p, i, p, i, i, i, i, p, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p, p,
+                                  p, p, p, sz, p]
+        L.dspark_set_timing_events.argtypes = [p, p]
+        L.dspark_force_monotone.argtypes = [p, i]
+        for name in EXPORTS:
+            if name not in ("dspark_last_error", "dspark_version", "dspark_workspace_bytes"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DSparkError(rc, lib().dspark_last_error().decode())
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libdspark takes densely packed (contiguous) tensors")
+
+
+def _elem_ok(t, dtype: int, what: str):
+    want = 2 if dtype == DSPARK_BF16 else 4
+    if t.element_size() != want:
+        raise ValueError(f"{what}: expected {want}-byte elements for dtype {dtype}")
+
+
+def dspark_version() -> str:
+    return lib().dspark_version().decode()
+
+
+def dspark_workspace_bytes(R: int, K: int, V: int, rank: int, dtype: int) -> int:
+    return int(lib().dspark_workspace_bytes(R, K, V, rank, dtype))
+
+
+def dspark_markov_prepare(Bmat, dtype: int, Bt, stream=None):
+    """Bt [V, rank] = Bmat [rank, V] transposed (start-up weight layout)."""
+    rank, V = Bmat.shape
+    if tuple(Bt.shape) != (V, rank):
+        raise ValueError("Bt must be [V, rank]")
+    _contig(Bmat, Bt)
+    _elem_ok(Bmat, dtype, "Bmat")
+    _elem_ok(Bt, dtype, "Bt")
+    _check(lib().dspark_markov_prepare(_p(Bmat), rank, V, dtype, _p(Bt), _stream(stream)))
+
+
+def dspark_chain(base, A, Bt, dtype: int, prev0, tokens, chained_logits=None, status=None, ws=None, stream=None):
+    R, K, V = base.shape
+    rank = A.shape[1]
+    if tuple(A.shape) != (V, rank) or tuple(Bt.shape) != (V, rank) or tuple(prev0.shape) != (R,) \
+            or tuple(tokens.shape) != (R, K):
+        raise ValueError("dspark_chain: inconsistent shapes")
+    if chained_logits is not None and tuple(chained_logits.shape) != (R, K, V):
+        raise ValueError("dspark_chain: chained_logits must be [R, K, V]")
+    _contig(base, A, Bt, prev0, tokens, chained_logits)
+    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
+        _elem_ok(t, dtype, n)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dspark_chain(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(tokens),
+                              _p(chained_logits), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_survival(conf, surv, status=None, stream=None):
+    R, K = conf.shape
+    if tuple(surv.shape) != (R, K):
+        raise ValueError("dspark_survival: surv must match conf")
+    _contig(conf, surv)
+    _check(lib().dspark_survival(_p(conf), R, K, _p(surv), _p(status), _stream(stream)))
+
+
+def dspark_topb_select(surv, order, sorted_surv, rank=None, stream=None):
+    R, K = surv.shape
+    _contig(surv, order, sorted_surv, rank)
+    if order.numel() != R * K or sorted_surv.numel() != R * K or (rank is not None and rank.numel() != R * K):
+        raise ValueError("dspark_topb_select: outputs need R*K entries")
+    _check(lib().dspark_topb_select(_p(surv), R, K, _p(order), _p(sorted_surv), _p(rank), _stream(stream)))
+
+
+def dspark_choose_budget(sorted_surv, n_sampling: int, T: int, num_reqs: int, verify_cost, draft_cost, b_star,
+                         best_obj, obj=None, status=None, stream=None):
+    n = sorted_surv.numel()
+    _contig(sorted_surv, verify_cost, draft_cost, obj)
+    _check(lib().dspark_choose_budget(_p(sorted_surv), n, n_sampling, T, num_reqs, _p(verify_cost),
+                                      verify_cost.numel(), _p(draft_cost), draft_cost.numel(), _p(b_star),
+                                      _p(best_obj), _p(obj), _p(status), _stream(stream)))
+
+
+def dspark_allocate(order, b_star, R: int, K: int, prefix_len, offsets, ver_idx, tokens=None, ver_tokens=None,
+                    stream=None):
+    _contig(order, prefix_len, offsets, ver_idx, tokens, ver_tokens)
+    if order.numel() != R * K or prefix_len.numel() != R or offsets.numel() != R + 1 or ver_idx.numel() != R * K:
+        raise ValueError("dspark_allocate: inconsistent sizes")
+    _check(lib().dspark_allocate(_p(order), _p(b_star), R, K, _p(tokens), _p(prefix_len), _p(offsets),
+                                 _p(ver_idx), _p(ver_tokens), _stream(stream)))
+
+
+def dspark_step(base, A, Bt, dtype: int, prev0, conf, n_sampling: int, T: int, num_reqs: int, verify_cost,
+                draft_cost, out: "StepBuffers", ws, status=None, stream=None):
+    """The whole pass (chain + schedule) into the buffers of `out`."""
+    R, K, V = base.shape
+    rank = A.shape[1]
+    if tuple(conf.shape) != (R, K):
+        raise ValueError("dspark_step: conf must be [R, K]")
+    _contig(base, A, Bt, prev0, conf, verify_cost, draft_cost)
+    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
+        _elem_ok(t, dtype, n)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dspark_step(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(conf), n_sampling, T,
+                             num_reqs, _p(verify_cost), verify_cost.numel(), _p(draft_cost), draft_cost.numel(),
+                             _p(out.tokens), _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
+                             _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
+                             _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_set_timing_events(before_chain=None, after_chain=None):
+    """Events (torch.cuda.Event or raw handles) that later dspark_step calls record around the chain."""
+    def h(e):
+        return None if e is None else (e if isinstance(e, int) else e.cuda_event)
+    _check(lib().dspark_set_timing_events(h(before_chain), h(after_chain)))
+
+
+def dspark_force_monotone(table: np.ndarray) -> np.ndarray:
+    """Host-side start-up forcing of a cost table; returns the forced copy."""
+    t = np.ascontiguousarray(table, dtype=np.float32).copy()
+    _check(lib().dspark_force_monotone(t.ctypes.data_as(ctypes.c_void_p), int(t.size)))
+    return t
+
+
+class StepBuffers:
+    """Device output buffers of one step (torch tensors on `device`)."""
+
+    def __init__(self, R: int, K: int, device="cuda"):
+        import torch
+        i32 = dict(dtype=torch.int32, device=device)
+        self.tokens = torch.empty((R, K), **i32)
+        self.surv = torch.empty((R, K), dtype=torch.float32, device=device)
+        self.order = torch.empty(R * K, **i32)
+        self.sorted_surv = torch.empty(R * K, dtype=torch.float32, device=device)
+        self.b_star = torch.empty(1, **i32)
+        self.best_obj = torch.empty(1, dtype=torch.float64, device=device)
+        self.prefix_len = torch.empty(R, **i32)
+        self.offsets = torch.empty(R + 1, **i32)
+        self.ver_idx = torch.empty(R * K, **i32)
+        self.ver_tokens = torch.empty(R * K, **i32)
+
+
+def workspace(R: int, K: int, V: int, rank: int, dtype: int, device="cuda"):
+    import torch
+    n = max(dspark_workspace_bytes(R, K, V, rank, dtype), 8)
+    return torch.empty((n + 7) // 8, dtype=torch.int64, device=device)

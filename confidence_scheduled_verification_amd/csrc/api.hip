@@ -1,0 +1,224 @@
+// C ABI of libdspark: argument checks, workspace layout and kernel launches.
+// Semantics of every entry point are documented in include/dspark.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "dspark.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_before_chain = nullptr;
+thread_local hipEvent_t g_ev_after_chain = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(DSPARK_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Compute units of the current device, cached per device ordinal.
+int num_cu() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t keys_bytes(int R, int K) { return round_up((size_t)R * (size_t)K * sizeof(uint64_t), 256); }
+
+int check_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
+                int V, int rank, const int32_t* tokens) {
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "chain: negative R (%d) or K (%d)", R, K);
+    if (R > 0 && K > 0 && (!base || !A || !Bt || !prev0 || !tokens))
+        return fail(DSPARK_EINVAL, "chain: a required pointer is NULL");
+    if (V < 1 || rank < 1) return fail(DSPARK_EINVAL, "chain: V (%d) and rank (%d) must be >= 1", V, rank);
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_EINVAL, "chain: unknown dtype %d", dtype);
+    if (dtype == DSPARK_BF16 && (rank % 32 != 0 || rank > DSPARK_MAX_RANK_BF16))
+        return fail(DSPARK_EUNSUPPORTED, "chain: bf16 rank %d must be a multiple of 32 and <= %d", rank,
+                    DSPARK_MAX_RANK_BF16);
+    if (dtype == DSPARK_F32 && rank > DSPARK_MAX_RANK_F32)
+        return fail(DSPARK_EUNSUPPORTED, "chain: fp32 rank %d exceeds %d", rank, DSPARK_MAX_RANK_F32);
+    if ((size_t)R * (size_t)K > (size_t)INT32_MAX) return fail(DSPARK_ERANGE, "chain: R*K overflows int32");
+    return DSPARK_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, int R, int K) {
+    const size_t need = keys_bytes(R, K);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                    ws ? "" : " (NULL)");
+    if (((uintptr_t)ws & 7u) != 0) return fail(DSPARK_EINVAL, "workspace must be 8-byte aligned");
+    return DSPARK_OK;
+}
+
+int check_sched_scalars(int n, int n_sampling, int T, int num_reqs, const float* vc, int verify_len,
+                        const float* dc, int draft_len) {
+    if (n > DSPARK_MAX_SLOTS) return fail(DSPARK_EUNSUPPORTED, "schedule: %d slots exceed %d", n, DSPARK_MAX_SLOTS);
+    if (!vc || !dc) return fail(DSPARK_EINVAL, "schedule: cost tables must not be NULL");
+    if (verify_len < 1 || draft_len < 1) return fail(DSPARK_EINVAL, "schedule: empty cost table");
+    if (n_sampling < 0) return fail(DSPARK_ERANGE, "schedule: n_sampling %d < 0", n_sampling);
+    if (T < 0 || T >= verify_len) return fail(DSPARK_ERANGE, "schedule: T %d outside [0, %d)", T, verify_len);
+    if (num_reqs < 0 || num_reqs >= draft_len)
+        return fail(DSPARK_ERANGE, "schedule: num_reqs %d outside [0, %d)", num_reqs, draft_len);
+    return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_last_error(void) { return g_err; }
+
+const char* dspark_version(void) { return "dspark-gfx950 0.1"; }
+
+size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype) {
+    (void)V;
+    (void)rank;
+    (void)dtype;
+    if (R <= 0 || K <= 0) return 0;
+    return keys_bytes(R, K);
+}
+
+int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt, void* stream) {
+    if (!Bmat || !Bt) return fail(DSPARK_EINVAL, "markov_prepare: NULL pointer");
+    if (rank < 1 || V < 1) return fail(DSPARK_EINVAL, "markov_prepare: rank %d and V %d must be >= 1", rank, V);
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16)
+        return fail(DSPARK_EINVAL, "markov_prepare: unknown dtype %d", dtype);
+    const hipError_t e = dspark::launch_transpose(Bmat, rank, V, dtype == DSPARK_BF16 ? 2 : 4, Bt,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "markov_prepare");
+}
+
+int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
+                 int V, int rank, int32_t* tokens, float* chained_logits, uint32_t* status, void* ws,
+                 size_t ws_bytes, void* stream) {
+    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+    if (rc != DSPARK_OK) return rc;
+    if (R == 0 || K == 0) return DSPARK_OK;
+    if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    dspark::ChainArgs a{base, A, Bt, dtype, prev0, R, K, V, rank, tokens, chained_logits, status, (uint64_t*)ws};
+    hipError_t e = dspark::launch_zero_keys(a.keys, (size_t)R * K, s);
+    if (e != hipSuccess) return hip_fail(e, "chain (zero keys)");
+    e = dspark::launch_chain_positions(a, num_cu(), s);
+    if (e != hipSuccess) return hip_fail(e, "chain");
+    e = dspark::launch_chain_finalize(a.keys, tokens, R, K, nullptr, nullptr, nullptr, s);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain (finalize)");
+}
+
+int dspark_survival(const float* conf, int R, int K, float* surv, uint32_t* status, void* stream) {
+    if (!conf || !surv) return fail(DSPARK_EINVAL, "survival: NULL pointer");
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "survival: negative R (%d) or K (%d)", R, K);
+    if (R == 0 || K == 0) return DSPARK_OK;
+    const hipError_t e = dspark::launch_survival(conf, R, K, surv, status, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "survival");
+}
+
+int dspark_topb_select(const float* surv, int R, int K, int32_t* order, float* sorted_surv, int32_t* rank,
+                       void* stream) {
+    if (!surv || !order || !sorted_surv) return fail(DSPARK_EINVAL, "topb_select: NULL pointer");
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "topb_select: negative R (%d) or K (%d)", R, K);
+    if ((long long)R * K > DSPARK_MAX_SLOTS)
+        return fail(DSPARK_EUNSUPPORTED, "topb_select: %lld slots exceed %d", (long long)R * K, DSPARK_MAX_SLOTS);
+    if (R == 0 || K == 0) return DSPARK_OK;
+    const hipError_t e = dspark::launch_topb(surv, R, K, order, sorted_surv, rank, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "topb_select");
+}
+
+int dspark_choose_budget(const float* sorted_surv, int n_slots, int n_sampling, int T, int num_reqs,
+                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                         int32_t* b_star, double* best_obj, double* obj, uint32_t* status, void* stream) {
+    if (!b_star || !best_obj) return fail(DSPARK_EINVAL, "choose_budget: NULL output");
+    if (n_slots < 0) return fail(DSPARK_EINVAL, "choose_budget: negative n_slots %d", n_slots);
+    if (n_slots > 0 && !sorted_surv) return fail(DSPARK_EINVAL, "choose_budget: NULL sorted_surv");
+    int rc = check_sched_scalars(n_slots, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
+    if (rc != DSPARK_OK) return rc;
+    const int bmax = std::min(n_slots, verify_len - 1 - T);
+    dspark::BudgetArgs a{sorted_surv, n_slots, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax,
+                         b_star, best_obj, obj, status};
+    const hipError_t e = dspark::launch_budget(a, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "choose_budget");
+}
+
+int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, const int32_t* tokens,
+                    int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens, void* stream) {
+    if (!b_star || !offsets) return fail(DSPARK_EINVAL, "allocate: NULL pointer");
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "allocate: negative R (%d) or K (%d)", R, K);
+    if ((long long)R * K > DSPARK_MAX_SLOTS)
+        return fail(DSPARK_EUNSUPPORTED, "allocate: %lld slots exceed %d", (long long)R * K, DSPARK_MAX_SLOTS);
+    if (R > 0 && (!prefix_len || (K > 0 && (!order || !ver_idx))))
+        return fail(DSPARK_EINVAL, "allocate: NULL pointer");
+    if (ver_tokens && !tokens) return fail(DSPARK_EINVAL, "allocate: ver_tokens needs tokens");
+    const hipError_t e = dspark::launch_allocate(order, b_star, R, K, tokens, prefix_len, offsets, ver_idx,
+                                                 ver_tokens, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "allocate");
+}
+
+int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
+                int V, int rank, const float* conf, int n_sampling, int T, int num_reqs, const float* verify_cost,
+                int verify_len, const float* draft_cost, int draft_len, int32_t* tokens, float* surv,
+                int32_t* order, float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len,
+                int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws,
+                size_t ws_bytes, void* stream) {
+    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+    if (rc != DSPARK_OK) return rc;
+    const long long n = (long long)R * K;
+    if (n > DSPARK_MAX_SLOTS) return fail(DSPARK_EUNSUPPORTED, "step: %lld slots exceed %d", n, DSPARK_MAX_SLOTS);
+    if (!b_star || !best_obj || !offsets || (R > 0 && !prefix_len) || (n > 0 && (!ver_idx || !conf)))
+        return fail(DSPARK_EINVAL, "step: a required schedule pointer is NULL");
+    rc = check_sched_scalars((int)n, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
+    if (rc != DSPARK_OK) return rc;
+    if (n > 0 && (rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int bmax = std::min((int)n, verify_len - 1 - T);
+    dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order,
+                              sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, status,
+                              (uint64_t*)ws, (int)n};
+    hipError_t e = dspark::launch_sched_fused(sa, s);
+    if (e != hipSuccess) return hip_fail(e, "step (schedule)");
+    if (n == 0) return DSPARK_OK;
+    dspark::ChainArgs a{base, A, Bt, dtype, prev0, R, K, V, rank, tokens, nullptr, status, (uint64_t*)ws};
+    if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
+        return hip_fail(e, "step (timing event)");
+    e = dspark::launch_chain_positions(a, num_cu(), s);
+    if (e != hipSuccess) return hip_fail(e, "step (chain)");
+    if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
+        return hip_fail(e, "step (timing event)");
+    e = dspark::launch_chain_finalize(a.keys, tokens, R, K, ver_idx, b_star, ver_tokens, s);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (finalize)");
+}
+
+int dspark_set_timing_events(void* before_chain, void* after_chain) {
+    g_ev_before_chain = (hipEvent_t)before_chain;
+    g_ev_after_chain = (hipEvent_t)after_chain;
+    return DSPARK_OK;
+}
+
+int dspark_force_monotone(float* table, int len) {
+    if (!table || len < 0) return fail(DSPARK_EINVAL, "force_monotone: NULL table or negative length");
+    for (int t = 0; t < len; ++t)
+        if (!isfinite(table[t])) return fail(DSPARK_EINVAL, "force_monotone: entry %d is not finite", t);
+    for (int t = 1; t < len; ++t)
+        if (table[t] < table[t - 1]) table[t] = table[t - 1];
+    return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal helpers shared by the gfx950 kernels of libdspark (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kStatusPrevClamped = 1u;
+constexpr uint32_t kStatusConfSanitized = 2u;
+constexpr uint32_t kStatusCostInvalid = 4u;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Argmax key.  A 64-bit value whose unsigned order is the argmax order: larger
+// logit first, NaN above every number, and among equal logits the lower index
+// (the low word holds the bitwise complement of the index).  -0 is read as +0 so
+// that equal numbers compare equal.  Every key built here is non-zero, so 0 is
+// the identity of the max-reduction and never decodes to an index.
+__device__ __forceinline__ uint64_t argmax_key(float x, uint32_t v) {
+    uint32_t b = __float_as_uint(x);
+    uint32_t u;
+    if (x != x) {
+        u = 0xFFFFFFFFu;
+    } else {
+        if (b == 0x80000000u) b = 0u;
+        u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    }
+    return ((uint64_t)u << 32) | (uint64_t)(~v);
+}
+
+__device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(~(uint32_t)key); }
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    lo = __shfl_xor(lo, mask, 64);
+    hi = __shfl_xor(hi, mask, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t load_agent_u64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Raise the device-wide best key at *p to at least k.  A relaxed read first skips the
+// atomic when the stored key is already larger (keys only grow within a launch).
+__device__ __forceinline__ void publish_key(uint64_t* p, uint64_t k) {
+    if (k > load_agent_u64(p)) atomicMax((unsigned long long*)p, (unsigned long long)k);
+}
+
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
+    if (status) atomicOr(status, bits);
+}
+
+}  // namespace dspark

@@ -1,0 +1,72 @@
+// Internal launchers of libdspark (not part of the C ABI).  Each enqueues on the
+// given stream and returns the launch status; argument checks happen in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace dspark {
+
+struct ChainArgs {
+    const void* base;
+    const void* A;
+    const void* Bt;
+    int dtype;  // 0 fp32, 1 bf16
+    const int32_t* prev0;
+    int R, K, V, rank;
+    int32_t* tokens;
+    float* logits;
+    uint32_t* status;
+    uint64_t* keys;  // [K, R] per-position argmax keys, zeroed before the first position
+};
+
+struct BudgetArgs {
+    const float* sorted_surv;
+    int n, n_sampling, T, num_reqs;
+    const float* vc;
+    const float* dc;
+    int bmax;
+    int32_t* b_star;
+    double* best_obj;
+    double* obj;
+    uint32_t* status;
+};
+
+struct FusedSchedArgs {
+    const float* conf;
+    int R, K, n_sampling, T, num_reqs;
+    const float* vc;
+    const float* dc;
+    int bmax;
+    float* surv;
+    int32_t* order;
+    float* sorted_surv;
+    int32_t* b_star;
+    double* best_obj;
+    int32_t* prefix_len;
+    int32_t* offsets;
+    int32_t* ver_idx;
+    uint32_t* status;
+    uint64_t* keys;  // chain keys to zero
+    int nkeys;
+};
+
+int chain_tile_vocab();
+hipError_t launch_zero_keys(uint64_t* keys, size_t n, hipStream_t s);
+hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s);
+hipError_t launch_chain_finalize(const uint64_t* keys, int32_t* tokens, int R, int K, const int32_t* ver_idx,
+                                 const int32_t* b_star, int32_t* ver_tokens, hipStream_t s);
+hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes, void* dst, hipStream_t s);
+
+hipError_t launch_survival(const float* conf, int R, int K, float* surv, uint32_t* status, hipStream_t s);
+hipError_t launch_topb(const float* surv, int R, int K, int32_t* order, float* sorted_surv, int32_t* rank,
+                       hipStream_t s);
+hipError_t launch_budget(const BudgetArgs& a, hipStream_t s);
+hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, int K, const int32_t* tokens,
+                           int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                           hipStream_t s);
+hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s);
+
+}  // namespace dspark

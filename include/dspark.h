@@ -1,0 +1,229 @@
+/*
+ * dspark.h -- C ABI of libdspark.so, the MI355X (gfx950) implementation of the
+ * per-step chain-and-schedule pass of DSpark confidence-scheduled verification.
+ *
+ * The pass, in the order one step runs it:
+ *   1. chain     -- a K-token draft block is chained semi-autoregressively: each
+ *                   position adds a rank-r bias keyed on the previously chosen
+ *                   token to the backbone's logits and takes the argmax
+ *                   (DSpark summary "How DSpark Speeds Up LLM Inference", section
+ *                   "Draft better"; MAX worklog "DSpark on MAX", section "What
+ *                   DSpark is", item 3);
+ *   2. survival  -- running product of per-position confidences along each
+ *                   request (vLLM blog "Adaptive Verification in vLLM", section
+ *                   "Scheduling the budget");
+ *   3. top-B     -- all request x position slots ranked globally by survival;
+ *                   every prefix of that ranking is a contiguous prefix of each
+ *                   request's draft (same section);
+ *   4. budget    -- B chosen to maximise expected tokens per microsecond,
+ *                   (N_sampling + sum of the B best survivals) divided by
+ *                   verify_cost[T + B] + draft_cost[num_reqs] (same section, and
+ *                   section "The cost model" for the two summed tables);
+ *   5. allocate  -- per-request prefix lengths and a compacted list of the
+ *                   verified slots, computed on the GPU with no read-back
+ *                   (same section, last paragraph).
+ *
+ * Conventions shared by every entry point below
+ *   - Pointers are DEVICE pointers unless marked (host).  All arrays are
+ *     row-major and densely packed.  bf16 data is passed as its 16-bit bit
+ *     patterns.
+ *   - `stream` is a hipStream_t.  Calls only enqueue work on it and return; they
+ *     never synchronise, never copy to the host and never allocate device
+ *     memory.  Work enqueued by one call completes in stream order.
+ *   - The caller owns every buffer.  Outputs must not alias inputs.  A
+ *     workspace is used by one call at a time (calls on different streams need
+ *     different workspaces).
+ *   - A negative return value means nothing was enqueued; the reason is in
+ *     dspark_last_error().  DSPARK_EHIP means a HIP launch failed after host
+ *     checks passed; work enqueued before the failure may already be running.
+ *   - `status` (optional, may be NULL) is a device uint32 into which kernels OR
+ *     the DSPARK_STATUS_* bits for conditions only the device can see.  It is
+ *     never cleared by the library.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_EINVAL = -1,       /* null pointer, negative size, unknown dtype      */
+    DSPARK_ERANGE = -2,       /* scalar outside its documented range              */
+    DSPARK_EUNSUPPORTED = -3, /* shape the kernels do not implement (see limits)  */
+    DSPARK_EWORKSPACE = -4,   /* workspace missing or smaller than required       */
+    DSPARK_EHIP = -5          /* HIP runtime error (text in dspark_last_error)    */
+} dspark_status_t;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
+
+/* Device-side conditions, OR-ed into *status. */
+#define DSPARK_STATUS_PREV_CLAMPED 1u   /* a prev0 entry was outside [0,V); it was clamped into range      */
+#define DSPARK_STATUS_CONF_SANITIZED 2u /* a confidence was NaN or outside [0,1]; NaN and <0 became 0, >1 became 1 */
+#define DSPARK_STATUS_COST_INVALID 4u   /* verify_cost[T+B] + draft_cost[num_reqs] was not a positive finite
+                                           number for some B; that B's objective is -inf                    */
+
+/* Limits. */
+#define DSPARK_MAX_SLOTS 16384          /* R*K handled by the single-workgroup scheduler                 */
+#define DSPARK_MAX_RANK_BF16 256        /* bf16 chain: rank must be a multiple of 32 and at most this     */
+#define DSPARK_MAX_RANK_F32 1024        /* fp32 chain: any rank up to this                                */
+
+/* Thread-local text describing the last non-OK return on this thread. */
+const char* dspark_last_error(void);
+
+/* Library version string. */
+const char* dspark_version(void);
+
+/* Bytes of device workspace needed by dspark_chain / dspark_step for this shape
+ * (0 when R*K == 0).  The workspace needs no initialisation. */
+size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
+
+/*
+ * Start-up layout change of the Markov head's second factor.  The head's bias
+ * for previous token u and candidate v is W[u,v] = sum_k A[u,k] * Bmat[k,v]
+ * with A [V,rank] and Bmat [rank,V] (a rank-r factorisation; DSpark summary,
+ * "Draft better").  The chain kernels read Bmat transposed, Bt [V,rank]
+ * (Bt[v,k] = Bmat[k,v]), so that every candidate token's rank-r vector is
+ * contiguous.  This call writes Bt from Bmat; run it once when the weights are
+ * loaded, not per step.  dtype gives the element type of both arrays.
+ */
+int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt, void* stream);
+
+/*
+ * Stage 1, chain.  For every request r, with prev = prev0[r]:
+ *   for i in 0..K-1:
+ *     x[v] = base[r,i,v] + sum_k A[prev,k] * Bt[v,k]      (fp32 accumulation)
+ *     tokens[r,i] = argmax_v x[v];  prev = tokens[r,i]
+ * (DSpark summary, "Draft better": a Markov head adjusts each word's odds using
+ * only the word right before it; MAX worklog, "What DSpark is": a low-rank bias
+ * keyed on the previous chosen token, then an argmax.)
+ *
+ *   base            [R,K,V]   backbone logits (dtype)
+ *   A               [V,rank]  first factor, row u = key vector of previous token u (dtype)
+ *   Bt              [V,rank]  second factor, transposed (see dspark_markov_prepare) (dtype)
+ *   prev0           [R]       int32 token preceding position 0; values outside [0,V)
+ *                             are clamped and flagged with DSPARK_STATUS_PREV_CLAMPED
+ *   tokens          [R,K]     int32 output
+ *   chained_logits  [R,K,V]   fp32 output x, or NULL (debug / parity use only)
+ *   ws, ws_bytes              workspace of at least dspark_workspace_bytes(R,K,V,rank,dtype)
+ *
+ * argmax: the largest value wins; NaN counts as larger than every number; among
+ * equal values the lowest index wins.  The returned index is always in [0,V).
+ * bf16: products are exact and summed in fp32 by the matrix cores; fp32: fused
+ * multiply-add in increasing k.  R == 0 or K == 0 enqueues nothing (data pointers
+ * may then be NULL).
+ * Limits: V >= 1; bf16 needs rank % 32 == 0 and rank <= DSPARK_MAX_RANK_BF16;
+ * fp32 needs 1 <= rank <= DSPARK_MAX_RANK_F32.
+ */
+int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
+                 int R, int K, int V, int rank, int32_t* tokens, float* chained_logits,
+                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 2, survival (vLLM blog, "Scheduling the budget"): for every request r,
+ *   surv[r,0] = c[r,0];  surv[r,i] = fl32(surv[r,i-1] * c[r,i])   for i = 1..K-1,
+ * i.e. the inclusive running product in float32, in increasing i.  A confidence
+ * that is NaN or below 0 is read as 0 and one above 1 as 1
+ * (DSPARK_STATUS_CONF_SANITIZED); -0.0 is read as +0.0.
+ *   conf [R,K] fp32 input; surv [R,K] fp32 output.
+ */
+int dspark_survival(const float* conf, int R, int K, float* surv, uint32_t* status, void* stream);
+
+/*
+ * Stage 3, global top-B (vLLM blog, "Scheduling the budget"): all n = R*K slots
+ * ranked by survival descending, then request ascending, then position
+ * ascending.  The first B entries of `order` are the top-B slots for every B.
+ *   surv        [R,K] fp32 input, entries in [0,1] (as produced by dspark_survival)
+ *   order       [n]   int32 output, flat slot ids r*K+i in rank order
+ *   sorted_surv [n]   fp32 output, surv at those slots
+ *   rank        [R,K] int32 output (position of each slot in `order`), or NULL
+ * Limit: n <= DSPARK_MAX_SLOTS.
+ */
+int dspark_topb_select(const float* surv, int R, int K, int32_t* order, float* sorted_surv, int32_t* rank,
+                       void* stream);
+
+/*
+ * Stage 4, budget (vLLM blog, "Scheduling the budget" and "The cost model"):
+ *   Bmax = min(n_slots, verify_len - 1 - T)
+ *   f(B) = fl64(n_sampling + S_B) / fl64(verify_cost[T+B] + draft_cost[num_reqs]),  B = 0..Bmax
+ * where S_B is the exact sum of sorted_surv[0..B) (rounded to double once, with
+ * n_sampling) and the division is IEEE double.  b_star is the smallest B with the
+ * largest f.  A denominator that is not a positive finite number gives f(B) = -inf
+ * and sets DSPARK_STATUS_COST_INVALID.
+ *   sorted_surv  [n_slots] fp32, non-increasing, entries in [0,1]
+ *   n_sampling   requests that sample a bonus token this step (>= 0)
+ *   T            non-draft tokens already in the step, 0 <= T < verify_len
+ *   num_reqs     index into draft_cost (scheduled requests), 0 <= num_reqs < draft_len
+ *   verify_cost  [verify_len] fp32 microseconds by step token count (forced monotone)
+ *   draft_cost   [draft_len]  fp32 microseconds by request count (forced monotone)
+ *   b_star [1] int32 output; best_obj [1] fp64 output; obj [Bmax+1] fp64 output or NULL
+ * Limit: n_slots <= DSPARK_MAX_SLOTS.
+ */
+int dspark_choose_budget(const float* sorted_surv, int n_slots, int n_sampling, int T, int num_reqs,
+                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                         int32_t* b_star, double* best_obj, double* obj, uint32_t* status, void* stream);
+
+/*
+ * Stage 5, allocation (vLLM blog, "Scheduling the budget": the B slots are
+ * handed to individual requests on the GPU, with no read-back to the host).
+ * The selected slots are order[0 .. *b_star).
+ *   order       [R*K] int32, a permutation of 0..R*K-1 (from dspark_topb_select)
+ *   b_star      [1]   int32 device scalar, 0 <= *b_star <= R*K
+ *   tokens      [R,K] int32 draft tokens, or NULL
+ *   prefix_len  [R]   int32 output: selected slots of each request
+ *   offsets     [R+1] int32 output: exclusive running sum of prefix_len
+ *   ver_idx     [R*K] int32 output: selected flat ids r*K+i ordered by request
+ *                     then position; entries from *b_star on are -1
+ *   ver_tokens  [R*K] int32 output tokens[ver_idx[j]] (-1 past *b_star), or NULL;
+ *                     requires tokens
+ * Limit: R*K <= DSPARK_MAX_SLOTS.
+ */
+int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, const int32_t* tokens,
+                    int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                    void* stream);
+
+/*
+ * The whole pass on one stream: stages 2-5 (survival, top-B, budget, the
+ * allocation) and stage 1 (chain), then the verified tokens are gathered.  The
+ * stages share no host round trip.  Arguments are those of the stage calls;
+ * `surv`, `order`, `sorted_surv`, `prefix_len`, `offsets`, `ver_idx`, `ver_tokens`
+ * and `best_obj` are outputs (surv, order, sorted_surv may be NULL).
+ * conf holds R rows (the drafting requests), R*K <= DSPARK_MAX_SLOTS.
+ */
+int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
+                int R, int K, int V, int rank,
+                const float* conf, int n_sampling, int T, int num_reqs,
+                const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                int32_t* b_star, double* best_obj,
+                int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Measurement hook.  When set (non-NULL hipEvent_t handles), every later
+ * dspark_step call on this thread records `before_chain` on its stream after the
+ * schedule kernels and before the first chain kernel, and `after_chain` after the
+ * last chain kernel, so a caller can time the phases with hipEventElapsedTime.
+ * Pass NULLs to turn it off (the default).  Recording an event enqueues a marker
+ * only; no synchronisation happens.
+ */
+int dspark_set_timing_events(void* before_chain, void* after_chain);
+
+/*
+ * Start-up forcing of a profiled cost table (host memory): each entry becomes
+ * the running maximum of the entries up to it, so the table never decreases
+ * (vLLM blog, "The cost model": profiling noise is smoothed by forcing the
+ * curve monotonic).  Returns DSPARK_EINVAL for a NULL table, a negative length
+ * or a non-finite entry (the table is then left unchanged).
+ */
+int dspark_force_monotone(float* table, int len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,147 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI, and compare with the oracle under the parity rules:
+
+  * draft tokens, slot ranking, B*, prefix lengths, offsets and compacted
+    indices: bit-exact;
+  * chained logits: |gpu - oracle| <= 1e-4 * max(|oracle|, 1);
+  * a token may differ from the oracle's only where the oracle's own logits of
+    the two tokens are within that same tolerance (a near-tie); the oracle is
+    keyed on the GPU's previous token (teacher forcing) so later positions still
+    compare like for like;
+  * the budget objective: bit-exact (both sides round the exact sum once and
+    divide in IEEE double), which is inside the 1e-6 relative bound.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from confidence_scheduled_verification_amd import binding as B
+from confidence_scheduled_verification_amd import inputs
+from oracle import sched
+
+DEV = "cuda"
+LOGIT_RTOL = 1e-4
+OBJ_RTOL = 1e-6
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+class Chain:
+    """Device copies of one chain problem (A, Bt prepared from Bmat on the GPU)."""
+
+    def __init__(self, base, A, Bmat, dtype, prev0):
+        self.R, self.K, self.V = base.shape
+        self.rank = A.shape[1]
+        self.dtype = dtype
+        self.base = to_dev(base)
+        self.A = to_dev(A)
+        Bm = to_dev(Bmat)
+        self.Bt = torch.empty((self.V, self.rank), dtype=Bm.dtype, device=DEV)
+        B.dspark_markov_prepare(Bm, dtype, self.Bt)
+        del Bm
+        self.prev0 = to_dev(np.asarray(prev0, dtype=np.int32))
+        self.ws = B.workspace(self.R, self.K, self.V, self.rank, dtype)
+
+    def run(self, want_logits=False):
+        tokens = torch.full((self.R, self.K), -7, dtype=torch.int32, device=DEV)
+        logits = torch.empty((self.R, self.K, self.V), dtype=torch.float32, device=DEV) if want_logits else None
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        B.dspark_chain(self.base, self.A, self.Bt, self.dtype, self.prev0, tokens, logits, status, self.ws)
+        torch.cuda.synchronize()
+        return tokens, logits, int(status.item())
+
+
+def _close(g, o, rtol):
+    both_nan = np.isnan(g) & np.isnan(o)
+    same_inf = np.isinf(o) & (g == o)
+    ok = np.abs(g - o) <= rtol * np.maximum(np.abs(o), 1.0)
+    return both_nan | same_inf | ok
+
+
+def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows=None):
+    """Compare GPU tokens (and logits for the same rows, if given) with the teacher-forced oracle.
+    gpu_tokens: [R,K] numpy; gpu_logits: [len(rows),K,V] numpy or None.  Returns the near-tie count."""
+    R, K, V = base.shape
+    rows = np.arange(R) if rows is None else np.asarray(rows)
+    assert gpu_tokens.min() >= 0 and gpu_tokens.max() < V, "token index outside [0, V)"
+    otok, olog, _ = oracle.chain(base, A, Bmat, dtype, prev0, rows=rows, forced=gpu_tokens, want_logits=True)
+    near = 0
+    for q, r in enumerate(rows):
+        for i in range(K):
+            g, o = int(gpu_tokens[r, i]), int(otok[q, i])
+            if g != o:
+                xo, xg = olog[q, i, o], olog[q, i, g]
+                gap = xo - xg
+                assert not np.isnan(xo), f"row {r} pos {i}: oracle NaN winner {o}, gpu {g}"
+                assert gap <= LOGIT_RTOL * max(abs(xo), 1.0), f"row {r} pos {i}: gpu {g} oracle {o} gap {gap}"
+                near += 1
+    if gpu_logits is not None:
+        ok = _close(gpu_logits.astype(np.float64), olog, LOGIT_RTOL)
+        if not ok.all():
+            bad = np.argwhere(~ok)[:5]
+            raise AssertionError(f"chained logits outside tolerance at {bad.tolist()}: "
+                                 f"gpu {[gpu_logits[tuple(b)] for b in bad]} oracle {[olog[tuple(b)] for b in bad]}")
+    return near
+
+
+def sched_oracle(conf, n_sampling, T, num_reqs, vc, dc, tokens=None):
+    return sched.schedule(conf, n_sampling, T, num_reqs, vc, dc, tokens=tokens)
+
+
+def assert_sched_parity(got: dict, want: dict, R: int, K: int):
+    n = R * K
+    B_ = int(want["b_star"])
+    if "surv" in got and got["surv"] is not None:
+        np.testing.assert_array_equal(got["surv"].view(np.uint32), want["surv"].view(np.uint32))
+    if "order" in got and got["order"] is not None:
+        np.testing.assert_array_equal(got["order"], want["order"])
+    if "sorted_surv" in got and got["sorted_surv"] is not None:
+        np.testing.assert_array_equal(got["sorted_surv"].view(np.uint32), want["sorted_surv"].view(np.uint32))
+    assert int(got["b_star"]) == B_, (int(got["b_star"]), B_)
+    gb, wb = float(got["best_obj"]), float(want["best_obj"])
+    assert gb == wb or (np.isinf(wb) and gb == wb), (gb, wb)
+    assert abs(gb - wb) <= OBJ_RTOL * abs(wb) or gb == wb
+    np.testing.assert_array_equal(got["prefix_len"], want["prefix_len"])
+    np.testing.assert_array_equal(got["offsets"], want["offsets"])
+    np.testing.assert_array_equal(got["ver_idx"], want["ver_idx"])
+    if got.get("ver_tokens") is not None and want.get("ver_tokens") is not None:
+        np.testing.assert_array_equal(got["ver_tokens"], want["ver_tokens"])
+    assert len(got["ver_idx"]) == n
+
+
+def forced_tables(w: inputs.Workload, ins: inputs.Inputs):
+    return sched.force_monotone(ins.verify_cost_raw), sched.force_monotone(ins.draft_cost_raw)
+
+
+def run_step(ch: Chain, conf, n_sampling, T, num_reqs, vc, dc, out=None):
+    """dspark_step on device buffers; returns (outputs as numpy dict, status, StepBuffers)."""
+    out = out or B.StepBuffers(ch.R, ch.K)
+    conf_d = to_dev(np.asarray(conf, dtype=np.float32))
+    vc_d, dc_d = to_dev(np.asarray(vc, dtype=np.float32)), to_dev(np.asarray(dc, dtype=np.float32))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.dspark_step(ch.base, ch.A, ch.Bt, ch.dtype, ch.prev0, conf_d, n_sampling, T, num_reqs, vc_d, dc_d, out,
+                  ch.ws, status)
+    torch.cuda.synchronize()
+    return step_numpy(out), int(status.item()), out
+
+
+def step_numpy(out: B.StepBuffers) -> dict:
+    return dict(tokens=out.tokens.cpu().numpy(), surv=out.surv.cpu().numpy(), order=out.order.cpu().numpy(),
+                sorted_surv=out.sorted_surv.cpu().numpy(), b_star=int(out.b_star.item()),
+                best_obj=float(out.best_obj.item()), prefix_len=out.prefix_len.cpu().numpy(),
+                offsets=out.offsets.cpu().numpy(), ver_idx=out.ver_idx.cpu().numpy(),
+                ver_tokens=out.ver_tokens.cpu().numpy())

@@ -1,0 +1,137 @@
+"""GPU parity of stage 1 (chain) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from confidence_scheduled_verification_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, R, K, V, rank, dtype, **kw):
+    return inputs.random_case(seed, R=R, K=K, V=V, rank=rank, dtype=dtype, **kw)
+
+
+def test_tiny_workload_fp32_full_parity():
+    w = inputs.WORKLOADS["tiny"]
+    ins = inputs.generate(w)
+    gu.say(f"tiny fp32 R={w.R} K={w.K} V={w.V} rank={w.rank}")
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    tok, lg, st = ch.run(want_logits=True)
+    assert st == 0
+    near = gu.assert_chain_parity(tok.cpu().numpy(), lg.cpu().numpy(), ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    assert near == 0
+
+
+def test_small_workload_bf16_full_parity():
+    w = inputs.WORKLOADS["small"]
+    ins = inputs.generate(w)
+    gu.say(f"small bf16 R={w.R} K={w.K} V={w.V} rank={w.rank}")
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    tok, lg, st = ch.run(want_logits=True)
+    assert st == 0
+    near = gu.assert_chain_parity(tok.cpu().numpy(), lg.cpu().numpy(), ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    assert near <= 1
+
+
+@pytest.mark.parametrize("R,K,V,rank", [
+    (5, 3, 1000, 64),      # V not a multiple of 8 (element-wise loads), partial request block
+    (17, 2, 4104, 32),     # two request blocks, ragged vocabulary tile, rank 32
+    (33, 4, 777, 96),      # rank 96 padded to 128, short vocabulary
+    (300, 2, 2048, 256),   # more requests than one LDS chunk (256)
+    (1, 1, 1, 32),         # one vocabulary entry
+    (16, 7, 1280 * 8, 128),
+])
+def test_ragged_bf16_parity(R, K, V, rank):
+    c = _case(100 + R + V, R, K, V, rank, inputs.BF16)
+    gu.say(f"ragged bf16 R={R} K={K} V={V} rank={rank}")
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    tok, lg, st = ch.run(want_logits=True)
+    assert st == 0
+    gu.assert_chain_parity(tok.cpu().numpy(), lg.cpu().numpy(), c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+
+
+@pytest.mark.parametrize("R,K,V,rank", [(3, 5, 300, 7), (9, 2, 1025, 16), (1, 3, 64, 1)])
+def test_ragged_fp32_parity(R, K, V, rank):
+    c = _case(200 + R + V, R, K, V, rank, inputs.F32, base_std=1.0, factor_std=0.3)
+    gu.say(f"ragged fp32 R={R} K={K} V={V} rank={rank}")
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.F32, c["prev0"])
+    tok, lg, st = ch.run(want_logits=True)
+    gu.assert_chain_parity(tok.cpu().numpy(), lg.cpu().numpy(), c["base"], c["A"], c["Bmat"], inputs.F32, c["prev0"])
+
+
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.F32])
+def test_zero_bias_is_numpy_argmax_with_special_values(dtype):
+    # Bmat = 0: the chain is numpy's argmax of each base row, NaN first, lowest index on ties.
+    R, K, V, rank = 6, 3, 1536, 32
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((R, K, V)).astype(np.float32)
+    x[0, 0, 700] = np.nan
+    x[0, 0, 900] = np.nan
+    x[1, 1, :] = -np.inf
+    x[2, 2, 11] = np.inf
+    x[2, 2, 12] = np.inf
+    x[3, 0, :] = 0.0
+    x[3, 0, 5] = -0.0
+    x[4, 1, 1000] = x[4, 1].max() + 1
+    x[4, 1, 3] = x[4, 1, 1000]          # exact tie: lower index wins
+    x[5, 2, 1535] = 50.0                # last entry of the vocabulary
+    if dtype == inputs.BF16:
+        x = np.where(np.isnan(x), np.float32(np.nan), x)
+        base = inputs.round_to_bf16(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+        base[np.isnan(x)] = 0x7FC0
+        base[np.isposinf(x)] = 0x7F80
+        base[np.isneginf(x)] = 0xFF80
+        ref = inputs.bf16_to_f32(base)
+    else:
+        base, ref = x, x
+    A = np.ones((V, rank), dtype=np.float32)
+    Bmat = np.zeros((rank, V), dtype=np.float32)
+    if dtype == inputs.BF16:
+        A, Bmat = inputs.round_to_bf16(A), inputs.round_to_bf16(Bmat)
+    prev0 = rng.integers(0, V, size=R, dtype=np.int32)
+    ch = gu.Chain(base, A, Bmat, dtype, prev0)
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))
+
+
+def test_closed_form_token_cycle_bf16():
+    # A[v,:] = G e_{v mod r}, Bmat[k,v] = [v == k+1]: tok_i = (tok_{i-1} mod r) + 1 exactly.
+    R, K, V, r, G = 20, 9, 3000, 64, 64.0
+    rng = np.random.default_rng(3)
+    base = inputs.round_to_bf16(rng.uniform(-1, 1, size=(R, K, V)).astype(np.float32))
+    A = np.zeros((V, r), dtype=np.float32)
+    A[np.arange(V), np.arange(V) % r] = G
+    Bmat = np.zeros((r, V), dtype=np.float32)
+    Bmat[np.arange(r), np.arange(r) + 1] = 1.0
+    prev0 = rng.integers(0, V, size=R, dtype=np.int32)
+    ch = gu.Chain(base, inputs.round_to_bf16(A), inputs.round_to_bf16(Bmat), inputs.BF16, prev0)
+    tok, _, _ = ch.run()
+    tok = tok.cpu().numpy()
+    for rr in range(R):
+        p = prev0[rr]
+        for i in range(K):
+            p = (p % r) + 1
+            assert tok[rr, i] == p, (rr, i)
+
+
+def test_prev0_out_of_range_is_clamped_and_flagged():
+    c = _case(5, 4, 2, 512, 32, inputs.BF16)
+    bad = c["prev0"].copy()
+    bad[0], bad[2] = -3, 512
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, bad)
+    tok, _, st = ch.run()
+    assert st == gu.B.STATUS_PREV_CLAMPED
+    clamped = bad.copy()
+    clamped[0], clamped[2] = 0, 511
+    gu.assert_chain_parity(tok.cpu().numpy(), None, c["base"], c["A"], c["Bmat"], inputs.BF16, clamped)
+
+
+def test_chain_is_deterministic():
+    c = _case(6, 64, 5, 20000, 256, inputs.BF16)
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    t1, l1, _ = ch.run(want_logits=True)
+    t2, l2, _ = ch.run(want_logits=True)
+    assert torch.equal(t1, t2)
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))

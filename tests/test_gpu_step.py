@@ -1,0 +1,82 @@
+"""GPU parity of the fused step (dspark_step) on every workload at its full size,
+in the launch configuration the benchmark times.  Chain rows are sampled (the
+fp64 oracle runs them one by one); the schedule is compared in full."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from confidence_scheduled_verification_amd import binding as B
+from confidence_scheduled_verification_amd import inputs
+from oracle import sched
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_ROWS = {"tiny": None, "small": None, "mid": [0, 37, 111], "headline": [0, 101, 255],
+               "large": [0, 63]}
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "mid", "headline", "large"])
+def test_full_size_step_parity(name):
+    w = inputs.WORKLOADS[name]
+    gu.say(f"step {name}: generating R={w.R} K={w.K} V={w.V}")
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    gu.say(f"step {name}: running")
+    got, status, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+    assert status == 0
+    rows = SAMPLE_ROWS[name]
+    gu.say(f"step {name}: oracle on rows {rows}")
+    gu.assert_chain_parity(got["tokens"], None, ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0, rows=rows)
+    want = sched.schedule(ins.conf, w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
+    gu.assert_sched_parity(got, want, w.R, w.K)
+    # the chained logits of the sampled rows, from the stage-1 entry point on the same inputs
+    tok, lg, _ = ch.run(want_logits=True)
+    np.testing.assert_array_equal(tok.cpu().numpy(), got["tokens"])
+    sel = np.arange(w.R) if rows is None else np.array(rows)
+    gu.assert_chain_parity(got["tokens"], lg[torch.as_tensor(sel, device=gu.DEV)].cpu().numpy(), ins.base, ins.A,
+                           ins.Bmat, w.dtype, ins.prev0, rows=sel)
+
+
+def test_step_is_deterministic_and_equals_stagewise():
+    w = inputs.WORKLOADS["headline"]
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    a, _, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+    b, _, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), a["tokens"])
+    R, K = w.R, w.K
+    assert np.array_equal(a["ver_tokens"][:a["b_star"]], a["tokens"].reshape(-1)[a["ver_idx"][:a["b_star"]]])
+    assert np.all(a["ver_tokens"][a["b_star"]:] == -1)
+
+
+def test_multi_step_inputs_change_the_result():
+    w = inputs.WORKLOADS["small"]
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    out = B.StepBuffers(w.R, w.K)
+    for k in range(3):
+        st = inputs.generate_step(w, k)
+        ch.base.copy_(gu.to_dev(st["base"]))
+        ch.prev0.copy_(gu.to_dev(st["prev0"]))
+        got, _, _ = gu.run_step(ch, st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, out=out)
+        gu.assert_chain_parity(got["tokens"], None, st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=[0, 31])
+        want = sched.schedule(st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
+        gu.assert_sched_parity(got, want, w.R, w.K)
+
+
+def test_empty_batch_step():
+    w = inputs.WORKLOADS["tiny"]
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    base = np.zeros((0, w.K, w.V), dtype=np.float32)
+    ch = gu.Chain(base, ins.A, ins.Bmat, w.dtype, np.zeros(0, np.int32))
+    got, status, _ = gu.run_step(ch, np.zeros((0, w.K), np.float32), 0, 0, 0, vc, dc)
+    assert got["b_star"] == 0 and got["offsets"].tolist() == [0]
+    assert got["best_obj"] == 0.0 and status == 0

@@ -1,0 +1,126 @@
+"""CPU checks of libdspark.so: it loads, exports every function include/dspark.h
+declares, and its host-side logic (argument checks that return before any HIP
+call, the start-up cost-table forcing) behaves as documented.  No kernel runs."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from confidence_scheduled_verification_amd import binding, inputs
+from oracle import sched
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_calls():
+    names = _declared()
+    for n in ("dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
+              "dspark_step", "dspark_force_monotone", "dspark_workspace_bytes", "dspark_markov_prepare"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dspark_\w+)", out))
+    assert set(_declared()) <= exported
+    assert set(binding.EXPORTS) == set(_declared())
+
+
+def test_version_and_workspace_size():
+    assert binding.dspark_version().startswith("dspark")
+    assert binding.dspark_workspace_bytes(0, 7, 100, 256, 1) == 0
+    n = binding.dspark_workspace_bytes(256, 7, 129280, 256, 1)
+    assert n >= 256 * 7 * 8 and n % 256 == 0
+
+
+def test_force_monotone_matches_running_max():
+    for name in ("tiny", "small", "mid", "large"):
+        w = inputs.WORKLOADS[name]
+        raw = inputs.raw_verify_cost(w, np.random.default_rng(1))
+        got = binding.dspark_force_monotone(raw)
+        np.testing.assert_array_equal(got, np.maximum.accumulate(raw))
+        np.testing.assert_array_equal(got, sched.force_monotone(raw))
+    np.testing.assert_array_equal(binding.dspark_force_monotone(np.zeros(0, np.float32)), np.zeros(0, np.float32))
+
+
+def test_force_monotone_rejects_non_finite_and_leaves_table():
+    t = np.array([3.0, 1.0, np.nan, 2.0], dtype=np.float32)
+    L = binding.lib()
+    rc = L.dspark_force_monotone(t.ctypes.data_as(ctypes.c_void_p), 4)
+    assert rc == -1
+    assert b"not finite" in L.dspark_last_error()
+    assert t[1] == 1.0
+    assert L.dspark_force_monotone(None, 3) == -1
+
+
+def _fake(n=64):
+    # host buffers standing in for device pointers: every call below fails its checks first
+    return ctypes.c_void_p(ctypes.addressof((ctypes.c_char * n)()))
+
+
+def test_chain_argument_checks_return_before_launch():
+    L = binding.lib()
+    p = _fake()
+    # NULL base
+    assert L.dspark_chain(None, p, p, 1, p, 4, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_chain(None, None, None, 1, None, 0, 7, 1024, 256, None, None, None, None, 0, None) == 0
+    # unknown dtype
+    assert L.dspark_chain(p, p, p, 7, p, 4, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
+    # bf16 rank not a multiple of 32
+    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 48, p, None, None, p, 1 << 20, None) == -3
+    assert b"multiple of 32" in L.dspark_last_error()
+    # bf16 rank too large
+    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 512, p, None, None, p, 1 << 20, None) == -3
+    # workspace too small / missing
+    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, p, 8, None) == -4
+    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, None, 0, None) == -4
+    # negative sizes
+    assert L.dspark_chain(p, p, p, 1, p, -1, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 0, 256, p, None, None, p, 1 << 20, None) == -1
+    # R == 0 is a valid empty call that enqueues nothing
+    assert L.dspark_chain(p, p, p, 1, p, 0, 7, 1024, 256, p, None, None, None, 0, None) == 0
+
+
+def test_schedule_argument_checks_return_before_launch():
+    L = binding.lib()
+    p = _fake()
+    # T outside [0, verify_len)
+    assert L.dspark_choose_budget(p, 10, 4, 65, 4, p, 65, p, 257, p, p, None, None, None) == -2
+    # num_reqs outside the draft table
+    assert L.dspark_choose_budget(p, 10, 4, 0, 257, p, 65, p, 257, p, p, None, None, None) == -2
+    # negative n_sampling
+    assert L.dspark_choose_budget(p, 10, -1, 0, 4, p, 65, p, 257, p, p, None, None, None) == -2
+    # too many slots
+    assert L.dspark_choose_budget(p, 16385, 4, 0, 4, p, 65, p, 257, p, p, None, None, None) == -3
+    assert L.dspark_topb_select(p, 1025, 16, p, p, None, None) == -3
+    assert L.dspark_allocate(p, p, 2000, 9, None, p, p, p, None, None) == -3
+    # ver_tokens without tokens
+    assert L.dspark_allocate(p, p, 4, 7, None, p, p, p, p, None) == -1
+    # NULL tables
+    assert L.dspark_choose_budget(p, 10, 4, 0, 4, None, 65, p, 257, p, p, None, None, None) == -1
+    # the fused step checks both halves
+    assert L.dspark_step(p, p, p, 1, p, 2048, 9, 1024, 256, p, 4, 0, 4, p, 65, p, 257,
+                         p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
+    assert L.dspark_step(p, p, p, 1, p, 4, 7, 1024, 256, p, 4, 70, 4, p, 65, p, 257,
+                         p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -2
+    # empty survival / top-B calls are valid no-ops
+    assert L.dspark_survival(p, 0, 7, p, None, None) == 0
+    assert L.dspark_topb_select(p, 0, 7, p, p, None, None) == 0
+
+
+def test_binding_raises_with_the_library_message():
+    with pytest.raises(binding.DSparkError, match="not finite"):
+        binding.dspark_force_monotone(np.array([np.inf], dtype=np.float32))
