@@ -10,22 +10,26 @@
 //     the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation) in the
 //     transposed form D[v, r] = Bt[v,:] . A[prev_r,:]: vocabulary rows are the
 //     MFMA M dimension, requests the N dimension.
-//   * A workgroup (4 waves) owns vocabulary tiles of 4*16*MB entries; each wave
-//     keeps its tile's Bt fragments in registers and sweeps all requests in
-//     blocks of 16.  The gathered key rows A[prev_r,:] of up to 256 requests are
-//     staged once per launch in LDS and shared by the 4 waves.
+//   * A workgroup of WAVES waves owns one vocabulary tile of WAVES*16*MB
+//     entries; each wave keeps its rows' Bt fragments in registers and sweeps
+//     all requests in blocks of 16.  The gathered key rows A[prev_r,:] of up to
+//     256 requests are staged once per launch in LDS and shared by the waves.
+//   * Everything that does not depend on the previous position -- the Bt
+//     fragments and the first base blocks -- is requested before the previous
+//     position's winners are decoded, so those loads overlap the key-row gather,
+//     and the gather itself keeps all of a thread's loads in flight at once.
 //   * Each lane's accumulator holds 8 consecutive vocabulary entries of one
 //     request per pair of M blocks (the M-row -> vocabulary mapping is permuted
 //     to make that so), so base logits stream in as 16-byte coalesced loads,
 //     prefetched PF request blocks ahead.
-//   * The argmax is fused: 64-bit keys (value, ~index) reduced in registers, by
-//     cross-lane shuffles, across the 4 waves in LDS, and across workgroups by
-//     one 64-bit atomicMax per request per workgroup (skipped when the stored
-//     key is already larger).  The next position's launch decodes the winners.
-//   * Grids are capped at the CU count (the 141 KB of LDS allows one workgroup
-//     per CU); workgroups loop over tiles rather than launching ~10^5 tiny
-//     blocks, which the MAX worklog found dispatch-bound ("Correctness, then
-//     1.3x").
+//   * The argmax is fused: per lane an ordered 32-bit key and the first index of
+//     its maximum, then 64-bit keys (value, ~index) reduced by cross-lane
+//     shuffles, across waves in LDS, and across workgroups by one 64-bit
+//     atomicMax per request per workgroup (skipped when the stored key is
+//     already larger).  The next position's launch decodes the winners.
+//   * About 250 workgroups of 512 threads per launch for a 129280-entry
+//     vocabulary: enough to fill the CUs without ~10^5 tiny blocks, which the MAX
+//     worklog found dispatch-bound ("Correctness, then 1.3x").
 #include "common.h"
 #include "kernels.h"
 
@@ -33,8 +37,12 @@ namespace dspark {
 
 namespace {
 
-constexpr int kChainThreads = 256;
-constexpr int kReqChunk = 256;  // requests whose key rows are staged in LDS at once
+constexpr int kReqChunk = 256;   // requests whose key rows are staged in LDS at once
+constexpr int kWaves = 8;        // waves per workgroup of the bf16 kernel
+constexpr int kMB = 4;           // 16-row M blocks per wave
+constexpr int kPF = 3;           // request blocks of base prefetched ahead
+constexpr int kTileV = kWaves * 16 * kMB;
+constexpr int kF32Threads = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,6 +60,15 @@ __device__ __forceinline__ int decode_prev(const int32_t* prev0, const uint64_t*
     // range; the clamp only guarantees that the gather below can never leave A.
     const int p = key_index(load_agent_u64(&keys[(size_t)(pos - 1) * R + r]));
     return p < 0 ? 0 : (p >= V ? V - 1 : p);
+}
+
+// Order-preserving image of a float in the unsigned integers: NaN above every
+// number, -0 equal to +0.  Never 0, so 0 marks "no candidate".
+__device__ __forceinline__ uint32_t ordered_u32(float x) {
+    uint32_t b = __float_as_uint(x);
+    if (x != x) return 0xFFFFFFFFu;
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 // Base logits of one request block for one wave: MB/2 groups of 8 consecutive
@@ -83,135 +100,187 @@ __device__ __forceinline__ void load_base(BaseFrag<MB>& f, const uint16_t* __res
     }
 }
 
-// One launch per position.  KS = padded rank / 32, MB = 16-row M blocks per wave,
-// PF = request blocks of base prefetched ahead, VEC = V % 8 == 0 (16-byte loads).
-template <int KS, int MB, int PF, bool VEC>
-__global__ __launch_bounds__(kChainThreads, 1) void chain_pos_bf16_kernel(
+// One launch per position, one vocabulary tile per workgroup.  KS = padded rank / 32,
+// VEC = V % 8 == 0 (16-byte base loads).
+template <int KS, bool VEC>
+__global__ __launch_bounds__(kWaves * 64, 1) void chain_pos_bf16_kernel(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, int32_t* __restrict__ tokens,
     float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos) {
+    constexpr int MB = kMB, PF = kPF, NT = kWaves * 64;
     constexpr int RP = 32 * KS;     // padded rank
     constexpr int LROW = RP + 8;    // LDS row stride in bf16 elements (16-byte pad spreads banks)
     constexpr int SEGS = RP / 8;    // 16-byte segments per key row
     constexpr int WV = 16 * MB;     // vocabulary entries per wave
-    constexpr int TV = 4 * WV;      // vocabulary entries per workgroup tile
+    constexpr int GATHER = (kReqChunk * SEGS + NT - 1) / NT;  // key-row segments per thread
+    constexpr int GB = GATHER < 8 ? GATHER : 8;                 // of which in flight at once
     __shared__ __attribute__((aligned(16))) uint16_t s_a[kReqChunk * LROW];
-    __shared__ uint64_t s_best[4][kReqChunk];
+    __shared__ uint64_t s_best[kWaves][kReqChunk];
     __shared__ int32_t s_prev[kReqChunk];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, g = lane >> 4;
-    const int ntiles = (V + TV - 1) / TV;
+    const int vb = blockIdx.x * kTileV + w * WV;
+    const int vlane = vb + 8 * g;  // first vocabulary entry of this lane's first group
+
+    // Bt fragments of this wave's vocabulary rows (independent of the previous
+    // position).  M row m of block mb is vocabulary vb + 32*(mb/2) + 8*(m/4) +
+    // 4*(mb%2) + m%4, which puts 8 consecutive entries in each lane's accumulator pair.
+    bf16x8 bt[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int v = vb + 32 * (mb >> 1) + 8 * (n16 >> 2) + 4 * (mb & 1) + (n16 & 3);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = ks * 32 + g * 8;
+            if (v < V && k0 < rank)
+                bt[mb][ks] = *(const bf16x8*)(Bt + (size_t)v * rank + k0);
+            else
+                bt[mb][ks] = bf16x8{};
+        }
+    }
 
     for (int c0 = 0; c0 < R; c0 += kReqChunk) {
         const int RC = min(kReqChunk, R - c0);
         const int nRB = (RC + 15) >> 4;
-        for (int j = tid; j < RC; j += kChainThreads) {
+
+        // First base blocks of this chunk (independent of the previous position).
+        BaseFrag<MB> pre[PF];
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+            if (q < nRB) load_base<MB, VEC>(pre[q], base, c0 + q * 16 + n16, R, K, V, pos, vlane);
+
+        if (c0 > 0) __syncthreads();  // the previous chunk is done with s_a / s_best / s_prev
+        for (int j = tid; j < RC; j += NT) {
             const int p = decode_prev(prev0, keys, status, R, V, pos, c0 + j, blockIdx.x == 0);
             s_prev[j] = p;
             if (pos > 0 && blockIdx.x == 0) tokens[(size_t)(c0 + j) * K + (pos - 1)] = p;
         }
-        for (int j = tid; j < 4 * kReqChunk; j += kChainThreads) (&s_best[0][0])[j] = 0ull;
+        for (int j = tid; j < kWaves * kReqChunk; j += NT) (&s_best[0][0])[j] = 0ull;
         __syncthreads();
 
-        // Gather the key rows A[prev_r, :] of this chunk into LDS (zero past rank and R).
-        for (int idx = tid; idx < nRB * 16 * SEGS; idx += kChainThreads) {
-            const int j = idx / SEGS, s = idx - j * SEGS;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (j < RC && s * 8 < rank) val = *(const u32x4*)(A + (size_t)s_prev[j] * rank + s * 8);
-            *(u32x4*)(s_a + j * LROW + s * 8) = val;
+        // Gather the key rows A[prev_r, :] of this chunk into LDS (zero past rank and
+        // R), GB independent loads in flight per thread before their stores.
+#pragma unroll
+        for (int q0 = 0; q0 < GATHER; q0 += GB) {
+            u32x4 seg[GB];
+#pragma unroll
+            for (int q = 0; q < GB; ++q) {
+                const int idx = tid + (q0 + q) * NT;
+                const int j = idx / SEGS, s = idx - j * SEGS;
+                seg[q] = u32x4{0u, 0u, 0u, 0u};
+                if (q0 + q < GATHER && j < RC && s * 8 < rank)
+                    seg[q] = *(const u32x4*)(A + (size_t)s_prev[j] * rank + s * 8);
+            }
+#pragma unroll
+            for (int q = 0; q < GB; ++q) {
+                const int idx = tid + (q0 + q) * NT;
+                const int j = idx / SEGS, s = idx - j * SEGS;
+                if (q0 + q < GATHER && j < nRB * 16) *(u32x4*)(s_a + j * LROW + s * 8) = seg[q];
+            }
         }
         __syncthreads();
 
-        for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-            const int vb = t * TV + w * WV;
-            // Bt fragments of this wave's vocabulary rows.  M row m of block mb is
-            // vocabulary vb + 32*(mb/2) + 8*(m/4) + 4*(mb%2) + m%4, which puts 8
-            // consecutive entries in each lane's accumulator pair.
-            bf16x8 bt[MB][KS];
+        for (int rb0 = 0; rb0 < nRB; rb0 += PF) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int v = vb + 32 * (mb >> 1) + 8 * (n16 >> 2) + 4 * (mb & 1) + (n16 & 3);
+            for (int q = 0; q < PF; ++q) {
+                const int rb = rb0 + q;
+                if (rb < nRB) {
+                    // The accumulator starts at the base logits (bf16 -> fp32 is exact), so the
+                    // matrix cores add the bias.  Lane element e (0..15) is vocabulary
+                    // vlane + 32*(e/8) + e%8, held in acc[2*(e/8) + (e%8)/4][e%4].
+                    f32x4 acc[MB];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int k0 = ks * 32 + g * 8;
-                    if (v < V && k0 < rank)
-                        bt[mb][ks] = *(const bf16x8*)(Bt + (size_t)v * rank + k0);
-                    else
-                        bt[mb][ks] = bf16x8{};
-                }
-            }
-            const int vlane = vb + 8 * g;  // first vocabulary entry of this lane's first group
-
-            BaseFrag<MB> pre[PF];
+                    for (int p = 0; p < MB / 2; ++p) {
 #pragma unroll
-            for (int q = 0; q < PF; ++q)
-                if (q < nRB) load_base<MB, VEC>(pre[q], base, c0 + q * 16 + n16, R, K, V, pos, vlane);
-
-            for (int rb0 = 0; rb0 < nRB; rb0 += PF) {
-#pragma unroll
-                for (int q = 0; q < PF; ++q) {
-                    const int rb = rb0 + q;
-                    if (rb < nRB) {
-                        const BaseFrag<MB> cur = pre[q];
-                        if (rb + PF < nRB)
-                            load_base<MB, VEC>(pre[q], base, c0 + (rb + PF) * 16 + n16, R, K, V, pos, vlane);
-
-                        f32x4 acc[MB];
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        const uint16_t* arow = s_a + (rb * 16 + n16) * LROW + g * 8;
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            const bf16x8 bfr = *(const bf16x8*)(arow + ks * 32);
-#pragma unroll
-                            for (int mb = 0; mb < MB; ++mb)
-                                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[mb][ks], bfr, acc[mb], 0, 0, 0);
+                        for (int h = 0; h < 2; ++h) {
+                            const uint32_t w0 = pre[q].q[p][2 * h], w1 = pre[q].q[p][2 * h + 1];
+                            acc[2 * p + h] = f32x4{__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                                                   __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
                         }
+                    }
+                    // refill this slot with the block PF ahead (its base is in acc now)
+                    if (rb + PF < nRB)
+                        load_base<MB, VEC>(pre[q], base, c0 + (rb + PF) * 16 + n16, R, K, V, pos, vlane);
+                    const uint16_t* arow = s_a + (rb * 16 + n16) * LROW + g * 8;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 bfr = *(const bf16x8*)(arow + ks * 32);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt[mb][ks], bfr, acc[mb], 0, 0, 0);
+                    }
 
-                        const int r = c0 + rb * 16 + n16;
-                        uint64_t best = 0ull;
+                    const int r = c0 + rb * 16 + n16;
+                    float x[4 * MB];
 #pragma unroll
-                        for (int p = 0; p < MB / 2; ++p) {
-                            const int v0 = vlane + 32 * p;
+                    for (int e = 0; e < 4 * MB; ++e) x[e] = acc[2 * (e >> 3) + ((e & 7) >> 2)][e & 3];
+                    if (logits != nullptr && r < R) {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const uint32_t h = (cur.q[p][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                                const float x = acc[2 * p + (e >> 2)][e & 3] + bf16_bits_to_f32(h);
-                                const int v = v0 + e;
-                                if (v < V) {
-                                    best = umax64(best, argmax_key(x, (uint32_t)v));
-                                    if (logits != nullptr && r < R) logits[((size_t)r * K + pos) * V + v] = x;
-                                }
+                        for (int e = 0; e < 4 * MB; ++e) {
+                            const int v = vlane + 32 * (e >> 3) + (e & 7);
+                            if (v < V) logits[((size_t)r * K + pos) * V + v] = x[e];
+                        }
+                    }
+                    if (vb + WV > V) {  // ragged last tile: entries past V cannot win
+#pragma unroll
+                        for (int e = 0; e < 4 * MB; ++e)
+                            if (vlane + 32 * (e >> 3) + (e & 7) >= V) x[e] = -__builtin_huge_valf();
+                    }
+                    // Largest x of this lane (NaN-propagating; -0 below +0), then the first
+                    // element equal to it (== treats -0 and +0 as equal).
+                    float m = x[0];
+#pragma unroll
+                    for (int e = 1; e + 1 < 4 * MB; e += 2)
+                        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, x[e]), x[e + 1]);
+                    m = __builtin_elementwise_maximum(m, x[4 * MB - 1]);
+                    uint32_t bu, bv;
+                    if (__ballot(m != m) == 0ull) {
+                        int idx = 4 * MB - 1;
+#pragma unroll
+                        for (int e = 4 * MB - 1; e >= 0; --e) idx = (x[e] == m) ? e : idx;
+                        bv = (uint32_t)(vlane + 32 * (idx >> 3) + (idx & 7));
+                        bu = ordered_u32(m);
+                    } else {  // a NaN in this wave's block: the general ordered-key scan
+                        bu = 0u;
+                        bv = 0u;
+#pragma unroll
+                        for (int e = 0; e < 4 * MB; ++e) {
+                            const uint32_t u = ordered_u32(x[e]);
+                            if (u > bu) {
+                                bu = u;
+                                bv = (uint32_t)(vlane + 32 * (e >> 3) + (e & 7));
                             }
                         }
-                        best = umax64(best, shfl_xor_u64(best, 16));
-                        best = umax64(best, shfl_xor_u64(best, 32));
-                        if (g == 0) {
-                            const int j = rb * 16 + n16;
-                            if (j < RC) s_best[w][j] = umax64(s_best[w][j], best);
-                        }
+                    }
+                    uint64_t best = (bv < (uint32_t)V) ? (((uint64_t)bu << 32) | (uint64_t)(~bv)) : 0ull;
+                    best = umax64(best, shfl_xor_u64(best, 16));
+                    best = umax64(best, shfl_xor_u64(best, 32));
+                    if (g == 0) {
+                        const int j = rb * 16 + n16;
+                        if (j < RC) s_best[w][j] = best;
                     }
                 }
             }
         }
         __syncthreads();
-        for (int j = tid; j < RC; j += kChainThreads) {
-            const uint64_t b = umax64(umax64(s_best[0][j], s_best[1][j]), umax64(s_best[2][j], s_best[3][j]));
+        for (int j = tid; j < RC; j += NT) {
+            uint64_t b = s_best[0][j];
+#pragma unroll
+            for (int q = 1; q < kWaves; ++q) b = umax64(b, s_best[q][j]);
             if (b) publish_key(&keys[(size_t)pos * R + c0 + j], b);
         }
-        __syncthreads();
     }
 }
 
 // fp32 factors: one thread per vocabulary entry, fused multiply-add in increasing k.
-__global__ __launch_bounds__(kChainThreads) void chain_pos_f32_kernel(
+__global__ __launch_bounds__(kF32Threads) void chain_pos_f32_kernel(
     const float* __restrict__ base, const float* __restrict__ A, const float* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, int32_t* __restrict__ tokens,
     float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos) {
-    __shared__ uint64_t s_wbest[kChainThreads / 64];
+    __shared__ uint64_t s_wbest[kF32Threads / 64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int v = blockIdx.x * kChainThreads + tid;
+    const int v = blockIdx.x * kF32Threads + tid;
     for (int r = 0; r < R; ++r) {
         const int p = decode_prev(prev0, keys, status, R, V, pos, r, blockIdx.x == 0 && tid == 0);
         if (pos > 0 && blockIdx.x == 0 && tid == 0) tokens[(size_t)r * K + (pos - 1)] = p;
@@ -231,7 +300,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_pos_f32_kernel(
         __syncthreads();
         if (tid == 0) {
             uint64_t b = s_wbest[0];
-            for (int q = 1; q < kChainThreads / 64; ++q) b = umax64(b, s_wbest[q]);
+            for (int q = 1; q < kF32Threads / 64; ++q) b = umax64(b, s_wbest[q]);
             if (b) publish_key(&keys[(size_t)pos * R + r], b);
         }
         __syncthreads();
@@ -285,9 +354,9 @@ __global__ void transpose_kernel(const T* __restrict__ src, int rows, int cols, 
     }
 }
 
-template <int KS, int MB, int PF, bool VEC>
+template <int KS, bool VEC>
 hipError_t launch_bf16(const ChainArgs& a, int pos, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((chain_pos_bf16_kernel<KS, MB, PF, VEC>), dim3(grid), dim3(kChainThreads), 0, s,
+    hipLaunchKernelGGL((chain_pos_bf16_kernel<KS, VEC>), dim3(grid), dim3(kWaves * 64), 0, s,
                        (const uint16_t*)a.base, (const uint16_t*)a.A, (const uint16_t*)a.Bt, a.prev0, a.keys,
                        a.tokens, a.logits, a.status, a.R, a.K, a.V, a.rank, pos);
     return hipGetLastError();
@@ -295,14 +364,13 @@ hipError_t launch_bf16(const ChainArgs& a, int pos, int grid, hipStream_t s) {
 
 template <int KS>
 hipError_t launch_bf16_ks(const ChainArgs& a, int pos, int grid, hipStream_t s) {
-    constexpr int MB = 4, PF = 4;
-    if (a.V % 8 == 0) return launch_bf16<KS, MB, PF, true>(a, pos, grid, s);
-    return launch_bf16<KS, MB, PF, false>(a, pos, grid, s);
+    if (a.V % 8 == 0) return launch_bf16<KS, true>(a, pos, grid, s);
+    return launch_bf16<KS, false>(a, pos, grid, s);
 }
 
 }  // namespace
 
-int chain_tile_vocab() { return 4 * 16 * 4; }
+int chain_tile_vocab() { return kTileV; }
 
 hipError_t launch_zero_keys(uint64_t* keys, size_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
@@ -312,9 +380,9 @@ hipError_t launch_zero_keys(uint64_t* keys, size_t n, hipStream_t s) {
 }
 
 hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s) {
+    (void)num_cu;
     if (a.dtype == 1) {
-        const int ntiles = (a.V + chain_tile_vocab() - 1) / chain_tile_vocab();
-        const int grid = std::max(1, std::min(ntiles, num_cu));
+        const int grid = (a.V + kTileV - 1) / kTileV;  // one vocabulary tile per workgroup
         const int ks = (a.rank + 31) / 32;
         for (int pos = 0; pos < a.K; ++pos) {
             hipError_t e;
@@ -325,9 +393,9 @@ hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s)
             if (e != hipSuccess) return e;
         }
     } else {
-        const int grid = (a.V + kChainThreads - 1) / kChainThreads;
+        const int grid = (a.V + kF32Threads - 1) / kF32Threads;
         for (int pos = 0; pos < a.K; ++pos) {
-            hipLaunchKernelGGL(chain_pos_f32_kernel, dim3(grid), dim3(kChainThreads), 0, s, (const float*)a.base,
+            hipLaunchKernelGGL(chain_pos_f32_kernel, dim3(grid), dim3(kF32Threads), 0, s, (const float*)a.base,
                                (const float*)a.A, (const float*)a.Bt, a.prev0, a.keys, a.tokens, a.logits,
                                a.status, a.R, a.K, a.V, a.rank, pos);
             const hipError_t e = hipGetLastError();
