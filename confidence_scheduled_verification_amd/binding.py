@@ -22,6 +22,7 @@ DSPARK_BF16 = 1
 STATUS_PREV_CLAMPED = 1
 STATUS_CONF_SANITIZED = 2
 STATUS_COST_INVALID = 4
+STATUS_SYNC_TIMEOUT = 8
 MAX_SLOTS = 16384
 
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",

@@ -42,7 +42,7 @@ int num_cu() {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t keys_bytes(int R, int K) { return round_up((size_t)R * (size_t)K * sizeof(uint64_t), 256); }
+size_t keys_bytes(int R, int K) { return dspark::ws_total_bytes(R, K); }
 
 int check_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
                 int V, int rank, const int32_t* tokens) {
@@ -115,8 +115,10 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
     if (R == 0 || K == 0) return DSPARK_OK;
     if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    dspark::ChainArgs a{base, A, Bt, dtype, prev0, R, K, V, rank, tokens, chained_logits, status, (uint64_t*)ws};
-    hipError_t e = dspark::launch_zero_keys(a.keys, (size_t)R * K, s);
+    dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
+                        V,      rank, tokens, chained_logits, status, (uint64_t*)ws,
+                        (uint32_t*)((char*)ws + dspark::ws_keys_bytes(R, K))};
+    hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_total_bytes(R, K) / 8, s);
     if (e != hipSuccess) return hip_fail(e, "chain (zero keys)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
     if (e != hipSuccess) return hip_fail(e, "chain");
@@ -191,11 +193,12 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
     const int bmax = std::min((int)n, verify_len - 1 - T);
     dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order,
                               sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, status,
-                              (uint64_t*)ws, (int)n};
+                              (uint64_t*)ws, n > 0 ? (int)(dspark::ws_total_bytes(R, K) / 8) : 0};
     hipError_t e = dspark::launch_sched_fused(sa, s);
     if (e != hipSuccess) return hip_fail(e, "step (schedule)");
     if (n == 0) return DSPARK_OK;
-    dspark::ChainArgs a{base, A, Bt, dtype, prev0, R, K, V, rank, tokens, nullptr, status, (uint64_t*)ws};
+    dspark::ChainArgs a{base, A,       Bt,     dtype,         prev0, R, K, V, rank, tokens,
+                        nullptr, status, (uint64_t*)ws, (uint32_t*)((char*)ws + dspark::ws_keys_bytes(R, K))};
     if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
         return hip_fail(e, "step (timing event)");
     e = dspark::launch_chain_positions(a, num_cu(), s);

@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kStatusPrevClamped = 1u;
 constexpr uint32_t kStatusConfSanitized = 2u;
 constexpr uint32_t kStatusCostInvalid = 4u;
+constexpr uint32_t kStatusSyncTimeout = 8u;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -48,9 +49,13 @@ __device__ __forceinline__ uint64_t load_agent_u64(const uint64_t* p) {
 }
 
 // Raise the device-wide best key at *p to at least k.  A relaxed read first skips the
-// atomic when the stored key is already larger (keys only grow within a launch).
+// atomic when the stored key is already larger (keys only grow within a launch).  The
+// atomic returns its old value, so a later s_waitcnt covers its completion.
 __device__ __forceinline__ void publish_key(uint64_t* p, uint64_t k) {
-    if (k > load_agent_u64(p)) atomicMax((unsigned long long*)p, (unsigned long long)k);
+    if (k > load_agent_u64(p)) {
+        const uint64_t old = __hip_atomic_fetch_max(p, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));
+    }
 }
 
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {

@@ -9,6 +9,15 @@
 
 namespace dspark {
 
+// Chain workspace: the per-position argmax keys [K][R] (uint64), then the
+// persistent kernel's grid-barrier counters [K][kMaxGroups] (uint32); each
+// region 256-byte aligned.  Everything is zeroed before the first chain kernel.
+constexpr int kMaxGroups = 2;
+inline size_t ws_round(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)K * 8); }
+inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
+inline size_t ws_total_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
+
 struct ChainArgs {
     const void* base;
     const void* A;
@@ -20,6 +29,7 @@ struct ChainArgs {
     float* logits;
     uint32_t* status;
     uint64_t* keys;  // [K, R] per-position argmax keys, zeroed before the first position
+    uint32_t* bar;   // [K, kMaxGroups] barrier counters, zeroed before the first position
 };
 
 struct BudgetArgs {
@@ -49,8 +59,8 @@ struct FusedSchedArgs {
     int32_t* offsets;
     int32_t* ver_idx;
     uint32_t* status;
-    uint64_t* keys;  // chain keys to zero
-    int nkeys;
+    uint64_t* ws;    // chain workspace to zero (keys and barrier counters)
+    int ws_words;    // its size in uint64 words
 };
 
 int chain_tile_vocab();

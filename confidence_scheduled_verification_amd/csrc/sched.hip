@@ -443,11 +443,12 @@ __global__ __launch_bounds__(kST, 1) void sched_fused_kernel(
     const float* __restrict__ vc, const float* __restrict__ dc, int bmax, float* __restrict__ surv_out,
     int32_t* __restrict__ order, float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
     double* __restrict__ best_obj, int32_t* __restrict__ prefix_len, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ ver_idx, uint32_t* status, uint64_t* __restrict__ keys, int nkeys) {
+    int32_t* __restrict__ ver_idx, uint32_t* status, uint64_t* __restrict__ ws, int ws_words) {
     __shared__ SchedShared sh;
     const int n = R * K, n_pad = pad_slots(n);
-    // The chain's per-position argmax keys start from zero (this launch precedes it).
-    for (int j = threadIdx.x; j < nkeys; j += kST) keys[j] = 0ull;
+    // The chain's workspace (argmax keys, barrier counters) starts from zero; this launch
+    // precedes the chain kernels on the stream.
+    for (int j = threadIdx.x; j < ws_words; j += kST) ws[j] = 0ull;
     survival_to_lds(sh, conf, R, K, n_pad, surv_out, status);
     sort_slots(sh, n_pad);
     write_ranking(sh, n, order, sorted_surv, nullptr);
@@ -554,7 +555,7 @@ hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, i
 hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sched_fused_kernel, dim3(1), dim3(kST), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T,
                        a.num_reqs, a.vc, a.dc, a.bmax, a.surv, a.order, a.sorted_surv, a.b_star, a.best_obj,
-                       a.prefix_len, a.offsets, a.ver_idx, a.status, a.keys, a.nkeys);
+                       a.prefix_len, a.offsets, a.ver_idx, a.status, a.ws, a.ws_words);
     return hipGetLastError();
 }
 

@@ -66,6 +66,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
 #define DSPARK_STATUS_CONF_SANITIZED 2u /* a confidence was NaN or outside [0,1]; NaN and <0 became 0, >1 became 1 */
 #define DSPARK_STATUS_COST_INVALID 4u   /* verify_cost[T+B] + draft_cost[num_reqs] was not a positive finite
                                            number for some B; that B's objective is -inf                    */
+#define DSPARK_STATUS_SYNC_TIMEOUT 8u   /* the single-launch chain waited too long at a grid barrier (its
+                                           workgroups were not all resident); tokens are then unreliable    */
 
 /* Limits. */
 #define DSPARK_MAX_SLOTS 16384          /* R*K handled by the single-workgroup scheduler                 */
