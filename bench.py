@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--pool", type=int, default=4, help="distinct per-step input sets cycled through")
     ap.add_argument("--cpu-rows", type=int, default=24, help="requests in the oracle's timed chain sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times): under rocprofv3 --pmc its "
+                         "FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM traffic counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -97,6 +100,15 @@ def main():
     B.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     log(f"bench: workload {w.name} R={w.R} K={w.K} V={w.V} rank={w.rank}; generating inputs")
     ins = inputs.generate(w)

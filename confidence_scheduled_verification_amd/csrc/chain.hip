@@ -44,10 +44,25 @@ namespace dspark {
 namespace {
 
 constexpr int kReqChunk = 256;   // requests whose key rows fit in LDS at once
-constexpr int kWaves = 8;        // waves per workgroup of the bf16 kernels
+#ifndef DSPARK_CHAIN_WAVES
+#define DSPARK_CHAIN_WAVES 8
+#endif
+#ifndef DSPARK_CHAIN_MB
+#define DSPARK_CHAIN_MB 4
+#endif
+#ifndef DSPARK_CHAIN_LDS_PAD
+#define DSPARK_CHAIN_LDS_PAD 8
+#endif
+constexpr int kWaves = DSPARK_CHAIN_WAVES;  // waves per workgroup of the bf16 kernels
 constexpr int kNT = kWaves * 64;
-constexpr int kMB = 4;           // 16-row M blocks per wave
-constexpr int kPF = 3;           // request blocks of base prefetched ahead
+constexpr int kMB = DSPARK_CHAIN_MB;        // 16-row M blocks per wave (even)
+#ifndef DSPARK_CHAIN_PF
+#define DSPARK_CHAIN_PF 3
+#endif
+#ifndef DSPARK_CHAIN_GATHER_BATCH
+#define DSPARK_CHAIN_GATHER_BATCH 4
+#endif
+constexpr int kPF = DSPARK_CHAIN_PF;        // request blocks of base prefetched ahead
 constexpr int kWV = 16 * kMB;    // vocabulary entries per wave
 constexpr int kTileV = kWaves * kWV;
 constexpr int kF32Threads = 256;
@@ -112,10 +127,10 @@ __device__ __forceinline__ void load_base(BaseFrag& f, const uint16_t* __restric
 template <int KS>
 struct ChainLds {
     static constexpr int RP = 32 * KS;   // padded rank
-    static constexpr int LROW = RP + 8;  // row stride in bf16 elements (16-byte pad spreads banks)
+    static constexpr int LROW = RP + DSPARK_CHAIN_LDS_PAD;  // row stride in bf16 elements (pad spreads banks)
     static constexpr int SEGS = RP / 8;  // 16-byte segments per key row
     uint16_t a[kReqChunk * LROW];        // gathered key rows
-    uint64_t best[kWaves][kReqChunk];    // per-wave argmax keys
+    uint64_t best[kReqChunk];            // workgroup argmax key per request (LDS atomic max)
     int32_t prev[kReqChunk];             // previous tokens
 };
 
@@ -141,7 +156,7 @@ __device__ __forceinline__ void load_bt(bf16x8 (&bt)[kMB][KS], const uint16_t* _
 
 // Requests [c0, c0+RC) use LDS rows l0 .. l0+RC (rounded up to 16 with zero rows).
 
-__device__ __forceinline__ void decode_rows(int32_t* s_prev, uint64_t (*s_best)[kReqChunk], const int32_t* prev0,
+__device__ __forceinline__ void decode_rows(int32_t* s_prev, uint64_t* s_best, const int32_t* prev0,
                                             const uint64_t* keys, int32_t* tokens, uint32_t* status, int R, int K,
                                             int V, int pos, int c0, int RC, int l0) {
     const int tid = threadIdx.x;
@@ -151,7 +166,7 @@ __device__ __forceinline__ void decode_rows(int32_t* s_prev, uint64_t (*s_best)[
         if (pos > 0 && blockIdx.x == 0) tokens[(size_t)(c0 + j) * K + (pos - 1)] = p;
     }
     const int rows = ((RC + 15) >> 4) << 4;
-    for (int j = tid; j < kWaves * rows; j += kNT) s_best[j / rows][l0 + j % rows] = 0ull;
+    for (int j = tid; j < rows; j += kNT) s_best[l0 + j] = 0ull;
 }
 
 // Key rows A[prev_r, :] into LDS (zero past rank and past RC), a batch of independent
@@ -160,7 +175,7 @@ template <int KS>
 __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __restrict__ A, int rank, int RC,
                                             int l0) {
     constexpr int SEGS = ChainLds<KS>::SEGS, LROW = ChainLds<KS>::LROW;
-    constexpr int GB = 8;
+    constexpr int GB = DSPARK_CHAIN_GATHER_BATCH;
     const int tid = threadIdx.x;
     const int total = ((RC + 15) >> 4) * 16 * SEGS;
     for (int q0 = 0; q0 < total; q0 += GB * kNT) {
@@ -270,7 +285,7 @@ __device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[k
                 best = umax64(best, shfl_xor_u64(best, 32));
                 if (g == 0) {
                     const int j = rb * 16 + n16;
-                    if (j < RC) L.best[w][l0 + j] = best;
+                    if (j < RC) atomicMax((unsigned long long*)&L.best[l0 + j], (unsigned long long)best);
                 }
             }
         }
@@ -285,9 +300,7 @@ template <int KS>
 __device__ __forceinline__ void publish_rows(const ChainLds<KS>& L, uint64_t* keys, int R, int pos, int c0, int RC,
                                              int l0) {
     for (int j = threadIdx.x; j < RC; j += kNT) {
-        uint64_t b = L.best[0][l0 + j];
-#pragma unroll
-        for (int q = 1; q < kWaves; ++q) b = umax64(b, L.best[q][l0 + j]);
+        const uint64_t b = L.best[l0 + j];
         if (b) {
             const uint64_t old =
                 __hip_atomic_fetch_max(&keys[(size_t)pos * R + c0 + j], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

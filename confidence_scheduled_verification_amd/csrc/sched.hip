@@ -133,11 +133,17 @@ __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
     return __longlong_as_double((long long)shfl_xor_u64((uint64_t)__double_as_longlong(x), m));
 }
 
+// Digit counters are stored digit-major with a stride of 17 words, so that both
+// the per-wave ranking (one digit per lane) and the block scan (consecutive
+// (digit, wave) entries per thread) touch distinct LDS banks.
+constexpr int kHistStride = kSW + 1;
+__device__ __forceinline__ int hist_at(int d, int w) { return d * kHistStride + w; }
+
 struct SchedShared {
-    uint32_t key[kMaxN];            // sort keys; after sorting: keys in rank order
-    uint16_t id[kMaxN];             // flat slot ids travelling with the keys
-    uint32_t hist[kSW * 256];       // per-wave digit counters / offsets
-    U192 part[kST];                 // per-thread partial sums; reused as the selection map
+    uint32_t key[kMaxN];                 // sort keys; after sorting: keys in rank order
+    uint16_t id[kMaxN];                  // flat slot ids travelling with the keys
+    uint32_t hist[256 * kHistStride];    // per-(digit, wave) counters / offsets
+    U192 part[kST];                      // per-thread partial sums; reused as the selection map
     uint32_t wsum[kSW];
     U192 wsum192[kSW];
     double wbest_f[kSW];
@@ -180,8 +186,19 @@ __device__ __forceinline__ U192 block_excl_scan192(SchedShared& sh, U192 v) {
     if (lane == 0) excl = U192{0ull, 0ull, 0ull};
     if (lane == 63) sh.wsum192[w] = x;
     __syncthreads();
-    U192 off = {0ull, 0ull, 0ull};
-    for (int q = 0; q < w; ++q) off = add192(off, sh.wsum192[q]);
+    if (w == 0) {  // exclusive scan of the 16 wave totals, in lanes 0..15 of wave 0
+        U192 t = lane < kSW ? sh.wsum192[lane] : U192{0ull, 0ull, 0ull};
+#pragma unroll
+        for (int o = 1; o < kSW; o <<= 1) {
+            const U192 y = shfl_up_192(t, o);
+            if (lane >= o) t = add192(t, y);
+        }
+        U192 te = shfl_up_192(t, 1);
+        if (lane == 0) te = U192{0ull, 0ull, 0ull};
+        if (lane < kSW) sh.part[lane] = te;
+    }
+    __syncthreads();
+    const U192 off = sh.part[w];
     __syncthreads();
     return add192(off, excl);
 }
@@ -203,24 +220,27 @@ __device__ __forceinline__ float sanitize_conf(float c, bool& bad) {
     return c == 0.f ? 0.f : c;  // -0 -> +0
 }
 
-// Stage 2 for all requests; keys/ids in flat order, pads after n.
+// Stage 2 for all requests; keys/ids in flat order, pads after n.  The confidences
+// are first read coalesced into LDS (one memory round trip for the whole block),
+// then each thread runs the sequential product of its request from LDS.
 __device__ __forceinline__ void survival_to_lds(SchedShared& sh, const float* __restrict__ conf, int R, int K, int n_pad,
-                                float* __restrict__ surv_out, uint32_t* status) {
+                                                float* __restrict__ surv_out, uint32_t* status) {
+    const int n = R * K;
+    for (int f = threadIdx.x; f < n_pad; f += kST) {
+        sh.key[f] = f < n ? __float_as_uint(conf[f]) : kPadKey;
+        sh.id[f] = (uint16_t)f;
+    }
+    __syncthreads();
     bool bad = false;
     for (int r = threadIdx.x; r < R; r += kST) {
         float s = 0.f;
         for (int i = 0; i < K; ++i) {
-            const float c = sanitize_conf(conf[(size_t)r * K + i], bad);
-            s = (i == 0) ? c : s * c;
             const int f = r * K + i;
+            const float c = sanitize_conf(__uint_as_float(sh.key[f]), bad);
+            s = (i == 0) ? c : s * c;
             sh.key[f] = kOne - __float_as_uint(s);
-            sh.id[f] = (uint16_t)f;
             if (surv_out) surv_out[f] = s;
         }
-    }
-    for (int f = R * K + threadIdx.x; f < n_pad; f += kST) {
-        sh.key[f] = kPadKey;
-        sh.id[f] = (uint16_t)f;
     }
     if (bad) raise_status(status, kStatusConfSanitized);
     __syncthreads();
@@ -241,21 +261,23 @@ __device__ __forceinline__ void surv_global_to_lds(SchedShared& sh, const float*
     __syncthreads();
 }
 
-// One stable counting pass over the 8-bit digit at `shift`.
+// One stable counting pass over the 8-bit digit at `shift`.  Wave w owns items
+// [w*S, (w+1)*S) of the current order, 64 per round; an item's rank among equal
+// digits of its wave comes from a ballot match of the digit bits and a running
+// per-(digit, wave) counter.
 __device__ __forceinline__ void radix_pass(SchedShared& sh, int n_pad, int shift) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int S = n_pad / kSW;  // items per wave, a multiple of 64
     const int J = S / 64;       // rounds, <= 16
     uint32_t k[16];
-    uint32_t id[16];
-    uint32_t loc[16];
-    for (int d = lane; d < 256; d += 64) sh.hist[w * 256 + d] = 0u;
+    uint32_t il[16];  // flat id (low 16 bits) and rank among equal digits of the wave (high 16 bits)
+    for (int d = lane; d < 256; d += 64) sh.hist[hist_at(d, w)] = 0u;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         if (j < J) {
             const int p = w * S + j * 64 + lane;
             k[j] = sh.key[p];
-            id[j] = sh.id[p];
+            il[j] = sh.id[p];
         }
     }
     __syncthreads();
@@ -272,9 +294,9 @@ __device__ __forceinline__ void radix_pass(SchedShared& sh, int n_pad, int shift
                 peers &= on ? m : ~m;
             }
             const uint32_t before = (uint32_t)__popcll(peers & lt);
-            const uint32_t h = sh.hist[w * 256 + d];
-            loc[j] = h + before;
-            if (before == 0u) sh.hist[w * 256 + d] = h + (uint32_t)__popcll(peers);
+            const uint32_t h = sh.hist[hist_at(d, w)];
+            il[j] |= (h + before) << 16;
+            if (before == 0u) sh.hist[hist_at(d, w)] = h + (uint32_t)__popcll(peers);
         }
     }
     __syncthreads();
@@ -283,14 +305,14 @@ __device__ __forceinline__ void radix_pass(SchedShared& sh, int n_pad, int shift
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
-        c[q] = sh.hist[(e & 15) * 256 + (e >> 4)];
+        c[q] = sh.hist[hist_at(e >> 4, e & 15)];
         s += c[q];
     }
     uint32_t ex = block_excl_scan(sh, s, nullptr);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
-        sh.hist[(e & 15) * 256 + (e >> 4)] = ex;
+        sh.hist[hist_at(e >> 4, e & 15)] = ex;
         ex += c[q];
     }
     __syncthreads();
@@ -298,9 +320,9 @@ __device__ __forceinline__ void radix_pass(SchedShared& sh, int n_pad, int shift
     for (int j = 0; j < 16; ++j) {
         if (j < J) {
             const uint32_t d = (k[j] >> shift) & 0xFFu;
-            const uint32_t dest = sh.hist[w * 256 + d] + loc[j];
+            const uint32_t dest = sh.hist[hist_at(d, w)] + (il[j] >> 16);
             sh.key[dest] = k[j];
-            sh.id[dest] = (uint16_t)id[j];
+            sh.id[dest] = (uint16_t)(il[j] & 0xFFFFu);
         }
     }
     __syncthreads();
@@ -321,11 +343,31 @@ __device__ __forceinline__ void write_ranking(const SchedShared& sh, int n, int3
     }
 }
 
+// The cost-table entries one thread evaluates in stage 4 (B = tid*C + q, and B = n_pad
+// for the last thread), read at the start of the kernel so that their memory latency
+// overlaps the earlier stages.
+struct CostPrefetch {
+    float vc[16];
+    float vc_last;
+    float dc;
+};
+
+__device__ __forceinline__ void prefetch_costs(CostPrefetch& cp, const float* __restrict__ vc,
+                                               const float* __restrict__ dc, int T, int num_reqs, int bmax,
+                                               int n_pad) {
+    const int C = n_pad / kST;
+    const int j0 = threadIdx.x * C;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cp.vc[q] = (q < C && j0 + q <= bmax) ? vc[T + j0 + q] : 0.f;
+    cp.vc_last = (threadIdx.x == kST - 1 && bmax == n_pad) ? vc[T + n_pad] : 0.f;
+    cp.dc = dc[num_reqs];
+}
+
 // Stage 4 over the keys in sh.key (rank order).  Leaves B* in sh.b_star.
-__device__ __forceinline__ void choose_budget_lds(SchedShared& sh, int n, int n_pad, int n_sampling, int T, int num_reqs,
-                                  const float* __restrict__ vc, const float* __restrict__ dc, int bmax,
-                                  int32_t* __restrict__ b_star, double* __restrict__ best_obj,
-                                  double* __restrict__ obj, uint32_t* status) {
+__device__ __forceinline__ void choose_budget_lds(SchedShared& sh, const CostPrefetch& cp, int n, int n_pad,
+                                                  int n_sampling, int bmax, int32_t* __restrict__ b_star,
+                                                  double* __restrict__ best_obj, double* __restrict__ obj,
+                                                  uint32_t* status) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int C = n_pad / kST;
     const int j0 = tid * C;
@@ -335,16 +377,16 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared& sh, int n, int n_
         if (j < n) local = add192(local, fixed_from_bits(kOne - sh.key[j]));
     }
     U192 S = block_excl_scan192(sh, local);
-    const double dcost = (double)dc[num_reqs];
+    const double dcost = (double)cp.dc;
     const uint64_t ns_hi = (uint64_t)(uint32_t)n_sampling << 21;  // n_sampling * 2^149: bit 149 is bit 21 of limb 2
     double bf = -INFINITY;
     int bb = 0x7FFFFFFF;
     bool bad = false;
-    auto eval = [&](int B) {
+    auto eval = [&](int B, float vcost) {
         U192 X = S;
         X.c += ns_hi;
         const double num = fixed_to_double(X);
-        const double den = (double)vc[T + B] + dcost;
+        const double den = (double)vcost + dcost;
         double f;
         if (den > 0.0 && den <= 1.7976931348623157e308) {
             f = num / den;
@@ -358,12 +400,15 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared& sh, int n, int n_
             bb = B;
         }
     };
-    for (int q = 0; q < C; ++q) {
-        const int B = j0 + q;
-        if (B <= bmax) eval(B);
-        if (B < n) S = add192(S, fixed_from_bits(kOne - sh.key[B]));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        if (q < C) {
+            const int B = j0 + q;
+            if (B <= bmax) eval(B, cp.vc[q]);
+            if (B < n) S = add192(S, fixed_from_bits(kOne - sh.key[B]));
+        }
     }
-    if (tid == kST - 1 && bmax == n_pad) eval(n_pad);
+    if (tid == kST - 1 && bmax == n_pad) eval(n_pad, cp.vc_last);
     if (bad) raise_status(status, kStatusCostInvalid);
     // Block argmax: larger f, then smaller B.
 #pragma unroll
@@ -451,8 +496,10 @@ __global__ __launch_bounds__(kST, 1) void sched_fused_kernel(
     for (int j = threadIdx.x; j < ws_words; j += kST) ws[j] = 0ull;
     survival_to_lds(sh, conf, R, K, n_pad, surv_out, status);
     sort_slots(sh, n_pad);
+    CostPrefetch cp;  // requested here so the loads overlap the write-out and the exact scan
+    prefetch_costs(cp, vc, dc, T, num_reqs, bmax, n_pad);
     write_ranking(sh, n, order, sorted_surv, nullptr);
-    choose_budget_lds(sh, n, n_pad, n_sampling, T, num_reqs, vc, dc, bmax, b_star, best_obj, nullptr, status);
+    choose_budget_lds(sh, cp, n, n_pad, n_sampling, bmax, b_star, best_obj, nullptr, status);
     const int B = sh.b_star;
     uint8_t* sel = selection_map(sh);
     for (int j = threadIdx.x; j < n; j += kST) sel[sh.id[j]] = (uint8_t)(j < B);
@@ -492,6 +539,8 @@ __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict_
                                                        double* __restrict__ obj, uint32_t* status) {
     __shared__ SchedShared sh;
     const int n_pad = pad_slots(n);
+    CostPrefetch cp;
+    prefetch_costs(cp, vc, dc, T, num_reqs, bmax, n_pad);
     for (int j = threadIdx.x; j < n_pad; j += kST) {
         uint32_t key = kOne;  // value 0 for pads (never summed: j >= n)
         if (j < n) {
@@ -501,7 +550,7 @@ __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict_
         sh.key[j] = key;
     }
     __syncthreads();
-    choose_budget_lds(sh, n, n_pad, n_sampling, T, num_reqs, vc, dc, bmax, b_star, best_obj, obj, status);
+    choose_budget_lds(sh, cp, n, n_pad, n_sampling, bmax, b_star, best_obj, obj, status);
 }
 
 __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restrict__ order,
