@@ -221,4 +221,4 @@ class StepBuffers:
 def workspace(R: int, K: int, V: int, rank: int, dtype: int, device="cuda"):
     import torch
     n = max(dspark_workspace_bytes(R, K, V, rank, dtype), 8)
-    return torch.empty((n + 7) // 8, dtype=torch.int64, device=device)
+    return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)  # zero-filled once, as the library requires

@@ -54,6 +54,10 @@ int check_chain(const void* base, const void* A, const void* Bt, int dtype, cons
     if (dtype == DSPARK_BF16 && (rank % 32 != 0 || rank > DSPARK_MAX_RANK_BF16))
         return fail(DSPARK_EUNSUPPORTED, "chain: bf16 rank %d must be a multiple of 32 and <= %d", rank,
                     DSPARK_MAX_RANK_BF16);
+    if (dtype == DSPARK_BF16 && (long long)K * V > DSPARK_MAX_KV_BF16)
+        return fail(DSPARK_EUNSUPPORTED, "chain: bf16 K*V = %lld exceeds %d", (long long)K * V, DSPARK_MAX_KV_BF16);
+    if (dtype == DSPARK_BF16 && (long long)V * rank > DSPARK_MAX_VR_BF16)
+        return fail(DSPARK_EUNSUPPORTED, "chain: bf16 V*rank = %lld exceeds %d", (long long)V * rank, DSPARK_MAX_VR_BF16);
     if (dtype == DSPARK_F32 && rank > DSPARK_MAX_RANK_F32)
         return fail(DSPARK_EUNSUPPORTED, "chain: fp32 rank %d exceeds %d", rank, DSPARK_MAX_RANK_F32);
     if ((size_t)R * (size_t)K > (size_t)INT32_MAX) return fail(DSPARK_ERANGE, "chain: R*K overflows int32");
@@ -191,10 +195,29 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
     if (n > 0 && (rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
     const int bmax = std::min((int)n, verify_len - 1 - T);
+    hipError_t e;
+    if (n > 0 && dtype == DSPARK_BF16) {
+        // One cooperative launch for the whole step when it fits on the device.
+        char* w = (char*)ws;
+        dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status, (uint64_t*)w,
+                            (uint32_t*)(w + dspark::ws_keys_bytes(R, K) + dspark::ws_bar_bytes(K)), conf,
+                            n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order, sorted_surv,
+                            b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens};
+        if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
+            return hip_fail(e, "step (timing event)");
+        e = dspark::launch_step_single(st, s);
+        if (e == hipSuccess) {
+            if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
+                return hip_fail(e, "step (timing event)");
+            return DSPARK_OK;
+        }
+        if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "step (single launch)");
+        (void)hipGetLastError();  // nothing was enqueued; run the stage-wise launches
+    }
     dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order,
                               sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, status,
                               (uint64_t*)ws, n > 0 ? (int)(dspark::ws_total_bytes(R, K) / 8) : 0};
-    hipError_t e = dspark::launch_sched_fused(sa, s);
+    e = dspark::launch_sched_fused(sa, s);
     if (e != hipSuccess) return hip_fail(e, "step (schedule)");
     if (n == 0) return DSPARK_OK;
     dspark::ChainArgs a{base, A,       Bt,     dtype,         prev0, R, K, V, rank, tokens,

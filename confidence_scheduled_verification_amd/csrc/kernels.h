@@ -9,14 +9,18 @@
 
 namespace dspark {
 
-// Chain workspace: the per-position argmax keys [K][R] (uint64), then the
-// persistent kernel's grid-barrier counters [K][kMaxGroups] (uint32); each
-// region 256-byte aligned.  Everything is zeroed before the first chain kernel.
-constexpr int kMaxGroups = 2;
+// Chain workspace: the per-position argmax keys [K][R] (uint64), the persistent
+// chain kernel's grid-barrier counters [K][kMaxGroups] (uint32), then the
+// single-launch step kernel's counters [K][kMaxGroups] and ready flag (uint32); each region
+// 256-byte aligned.  The stage-wise paths zero the whole workspace first; the step
+// kernel zeroes its keys in-launch and leaves its counters and flag at zero when it
+// ends, so they are zero at every launch once the workspace was zero-filled once.
+constexpr int kMaxGroups = 1;
 inline size_t ws_round(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)K * 8); }
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
-inline size_t ws_total_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
+inline size_t ws_step_bytes(int K) { return ws_round((size_t)(K * kMaxGroups + 1) * 4); }
+inline size_t ws_total_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K) + ws_step_bytes(K); }
 
 struct ChainArgs {
     const void* base;
@@ -63,7 +67,40 @@ struct FusedSchedArgs {
     int ws_words;    // its size in uint64 words
 };
 
+// Everything of one step in a single cooperative launch: the chain on one
+// workgroup per vocabulary tile plus one workgroup that runs stages 2-5 and writes
+// tokens and ver_tokens once the chain is done.
+struct StepArgs {
+    const void* base;
+    const void* A;
+    const void* Bt;
+    const int32_t* prev0;
+    int R, K, V, rank;
+    int32_t* tokens;
+    uint32_t* status;
+    uint64_t* keys;     // [K, R]
+    uint32_t* sync;     // [K][kMaxGroups] step barrier counters, then the ready flag; zero at launch
+    const float* conf;
+    int n_sampling, T, num_reqs;
+    const float* vc;
+    const float* dc;
+    int bmax;
+    float* surv;
+    int32_t* order;
+    float* sorted_surv;
+    int32_t* b_star;
+    double* best_obj;
+    int32_t* prefix_len;
+    int32_t* offsets;
+    int32_t* ver_idx;
+    int32_t* ver_tokens;
+};
+
 int chain_tile_vocab();
+// bf16 with 1 <= R <= 256 when the grid fits on the device at once; otherwise
+// hipErrorCooperativeLaunchTooLarge (nothing enqueued) and the caller runs the
+// stage-wise launches.
+hipError_t launch_step_single(const StepArgs& a, hipStream_t s);
 hipError_t launch_zero_keys(uint64_t* keys, size_t n, hipStream_t s);
 hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s);
 hipError_t launch_chain_finalize(const uint64_t* keys, int32_t* tokens, int R, int K, const int32_t* ver_idx,

@@ -73,6 +73,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
 #define DSPARK_MAX_SLOTS 16384          /* R*K handled by the single-workgroup scheduler                 */
 #define DSPARK_MAX_RANK_BF16 256        /* bf16 chain: rank must be a multiple of 32 and at most this     */
 #define DSPARK_MAX_RANK_F32 1024        /* fp32 chain: any rank up to this                                */
+#define DSPARK_MAX_KV_BF16 (1 << 27)    /* bf16 chain: K*V at most this (32-bit per-lane base offsets)    */
+#define DSPARK_MAX_VR_BF16 0x7FFFFFFF   /* bf16 chain: V*rank at most this (32-bit key-row offsets)       */
 
 /* Thread-local text describing the last non-OK return on this thread. */
 const char* dspark_last_error(void);
@@ -118,7 +120,8 @@ int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt
  * bf16: products are exact and summed in fp32 by the matrix cores; fp32: fused
  * multiply-add in increasing k.  R == 0 or K == 0 enqueues nothing (data pointers
  * may then be NULL).
- * Limits: V >= 1; bf16 needs rank % 32 == 0 and rank <= DSPARK_MAX_RANK_BF16;
+ * Limits: V >= 1; bf16 needs rank % 32 == 0, rank <= DSPARK_MAX_RANK_BF16 and
+ * K*V <= DSPARK_MAX_KV_BF16 and V*rank <= DSPARK_MAX_VR_BF16;
  * fp32 needs 1 <= rank <= DSPARK_MAX_RANK_F32.
  */
 int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,

@@ -135,3 +135,60 @@ def test_chain_is_deterministic():
     t2, l2, _ = ch.run(want_logits=True)
     assert torch.equal(t1, t2)
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+# Without a logits output the chain runs the pipelined scorer (single launch when the
+# requests fit one LDS chunk, one launch per position otherwise); these shapes cover
+# partial ring cycles (R not a multiple of 64), the ragged last vocabulary tile, V not a
+# multiple of 8, and request chunks that hand the base ring from one to the next.
+@pytest.mark.parametrize("R,K,V,rank", [
+    (5, 3, 1000, 64),
+    (17, 2, 4104, 32),
+    (33, 4, 777, 96),
+    (64, 3, 5000, 256),
+    (70, 5, 2600, 128),
+    (250, 2, 3001, 256),
+    (256, 4, 8192, 256),
+    (300, 2, 2048, 256),
+    (600, 2, 1544, 64),
+    (1, 1, 1, 32),
+])
+def test_ragged_bf16_parity_fast_scorer(R, K, V, rank):
+    c = _case(300 + R + V, R, K, V, rank, inputs.BF16)
+    gu.say(f"fast scorer bf16 R={R} K={K} V={V} rank={rank}")
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    tok, _, st = ch.run()
+    assert st == 0
+    gu.assert_chain_parity(tok.cpu().numpy(), None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+
+
+@pytest.mark.parametrize("R,V", [(70, 1000), (70, 1001), (130, 2048)])
+def test_fast_scorer_special_values_match_numpy_argmax(R, V):
+    # Bmat = 0 and bf16 inputs: every position is numpy's argmax of its base row.  NaNs,
+    # infinities, signed zeros and exact ties sit in later request blocks and in the
+    # ragged last tile, so the NaN rescore and the tail masking both run.
+    K, rank = 3, 32
+    rng = np.random.default_rng(R + V)
+    x = rng.standard_normal((R, K, V)).astype(np.float32)
+    x[65, 0, V - 1] = np.nan
+    x[65, 0, 3] = np.nan
+    x[66, 1, :] = -np.inf
+    x[67, 2, V - 2] = np.inf
+    x[67, 2, V - 1] = np.inf
+    x[68, 0, :] = 0.0
+    x[68, 0, 2] = -0.0
+    x[69, 1, V - 1] = 40.0
+    x[69, 1, V // 2] = 40.0
+    x[1, 2, V - 1] = 30.0
+    base = inputs.round_to_bf16(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+    base[np.isnan(x)] = 0x7FC0
+    base[np.isposinf(x)] = 0x7F80
+    base[np.isneginf(x)] = 0xFF80
+    base[68, 0, 2] = 0x8000
+    ref = inputs.bf16_to_f32(base)
+    A = inputs.round_to_bf16(np.ones((V, rank), dtype=np.float32))
+    Bmat = inputs.round_to_bf16(np.zeros((rank, V), dtype=np.float32))
+    prev0 = rng.integers(0, V, size=R, dtype=np.int32)
+    ch = gu.Chain(base, A, Bmat, inputs.BF16, prev0)
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))

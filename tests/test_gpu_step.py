@@ -80,3 +80,46 @@ def test_empty_batch_step():
     got, status, _ = gu.run_step(ch, np.zeros((0, w.K), np.float32), 0, 0, 0, vc, dc)
     assert got["b_star"] == 0 and got["offsets"].tolist() == [0]
     assert got["best_obj"] == 0.0 and status == 0
+
+
+def test_single_launch_step_keeps_the_workspace_consistent():
+    # The single-launch step zeroes its keys in-launch and leaves its barrier counters
+    # and ready flag at zero; the stage-wise chain zeroes the whole workspace first.
+    # Interleaving them on one workspace must not change any result.
+    w = inputs.WORKLOADS["small"]
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    first, st0, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+    assert st0 == 0
+    for rep in range(4):
+        gu.say(f"workspace reuse round {rep}")
+        tok, _, st = ch.run()
+        assert st == 0
+        np.testing.assert_array_equal(tok.cpu().numpy(), first["tokens"])
+        for _ in range(2):
+            got, st, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+            assert st == 0
+            for k in first:
+                assert np.array_equal(np.asarray(first[k]), np.asarray(got[k])), (rep, k)
+
+
+def test_single_launch_step_at_the_slot_limit():
+    # R = 256 requests x K = 64 positions = 16384 slots, the scheduler's maximum, inside
+    # the single launch (its scheduling workgroup has 512 threads).
+    R, K, V, rank = 256, 64, 2048, 32
+    c = inputs.random_case(77, R=R, K=K, V=V, rank=rank, dtype=inputs.BF16)
+    rng = np.random.default_rng(5)
+    conf = rng.beta(4.0, 1.5, size=(R, K)).astype(np.float32)
+    conf[rng.random((R, K)) < 0.02] = 1.0
+    w = inputs.WORKLOADS["headline"]
+    vlen = R * K + 64
+    vc = np.maximum.accumulate(50.0 + 0.01 * np.arange(vlen) + rng.normal(0, 0.5, vlen)).astype(np.float32)
+    dc = np.maximum.accumulate(5.0 + 0.1 * np.arange(R + 1)).astype(np.float32)
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    got, status, _ = gu.run_step(ch, conf, R, 0, R, vc, dc)
+    assert status == 0
+    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"], rows=[0, 128, 255])
+    want = sched.schedule(conf, R, 0, R, vc, dc, tokens=got["tokens"])
+    gu.assert_sched_parity(got, want, R, K)
+    assert 0 < got["b_star"] < R * K

@@ -84,6 +84,8 @@ def test_chain_argument_checks_return_before_launch():
     assert b"multiple of 32" in L.dspark_last_error()
     # bf16 rank too large
     assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 512, p, None, None, p, 1 << 20, None) == -3
+    # bf16 K*V beyond the 32-bit per-lane base offsets
+    assert L.dspark_chain(p, p, p, 1, p, 4, 16, 1 << 24, 256, p, None, None, p, 1 << 40, None) == -3
     # workspace too small / missing
     assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, p, 8, None) == -4
     assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, None, 0, None) == -4
