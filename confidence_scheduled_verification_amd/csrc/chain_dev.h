@@ -185,8 +185,9 @@ __device__ __forceinline__ void decode_rows(int32_t* s_prev, uint64_t* s_best, c
 // wave instruction fills 64 consecutive slots (lane i -> slot base + i), so no data
 // passes through registers and all of a workgroup's loads are in flight at once.
 // Slots past rank, the pad slots and rows RC .. `rows` read out of the buffer's
-// range and land as zeros.  Needs V * rank * 2 < 2^32.
-template <int KS>
+// range and land as zeros.  Needs V * rank * 2 < 2^32.  WAIT: return only once this
+// wave's slots have landed (otherwise a later s_waitcnt covers them).
+template <int KS, bool WAIT = true>
 __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __restrict__ A, int V, int rank, int RC,
                                             int l0, int rows) {
     constexpr int SEGS = ChainLds<KS>::SEGS, SP = ChainLds<KS>::LROW / 8;
@@ -204,7 +205,7 @@ __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __r
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(L.a + (l0 * SP + t0) * 8),
                                                  16, voff, 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's slots have landed (the caller then syncs the workgroup)
+    if (WAIT) __builtin_amdgcn_s_waitcnt(0);  // this wave's slots have landed (the caller then syncs the workgroup)
 }
 
 // Score the wave's 64 vocabulary rows against requests [c0, c0+RC) and raise each
@@ -607,9 +608,26 @@ __device__ __forceinline__ void grid_arrive(uint32_t* ctr) {
 // All K positions in one cooperative launch (R <= kReqChunk, gridDim.x <= resident
 // workgroups).  Position pos waits for every workgroup to have published position
 // pos-1; the base ring already holds position pos's first blocks by then.
-// G = the workgroups taking part (blockIdx.x < G).  `ready` (may be null): a flag
-// that must read nonzero before the first keys are published (the single-launch step
-// kernel zeroes the keys in-launch first).  tokens may be null.
+// Split of the requests for the persistent schedule: half 0 = [0, H), half 1 =
+// [H, R), H a multiple of one ring cycle (64 requests); a single group when R <= 64.
+__device__ __forceinline__ int half_split(int R) {
+    if (R <= 64) return R;
+    const int H = ((R + 1) / 2 + 63) / 64 * 64;
+    return H < R ? H : R;
+}
+
+// All K positions of the chain in one launch.  G = the workgroups taking part
+// (blockIdx.x < G).  `ready` (may be null): a flag that must read nonzero before the
+// first keys are published (the single-launch step kernel zeroes the keys in-launch
+// first).  tokens may be null.
+//
+// With two request halves the halves run out of phase: while a workgroup scores one
+// half, the other half's keys of the previous position finish arriving from every
+// workgroup, so its barrier wait is (nearly) free; its key rows are gathered
+// asynchronously and its publish atomics overlap that gather.  Per position:
+//   score h0 | wait h1(p-1), decode h1(p), gather h1 (async), publish h0(p), arrive h0
+//   score h1 | wait h0(p),   decode h0(p+1), gather h0 (async), publish h1(p), arrive h1
+// Barrier counters: bar[p * kMaxGroups + h].
 template <int KS, bool VEC>
 __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16_t* __restrict__ base,
                                                    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
@@ -617,24 +635,54 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
                                                    uint32_t* __restrict__ bar, int32_t* __restrict__ tokens,
                                                    uint32_t* __restrict__ status, int R, int K, int V, int rank,
                                                    int G, const uint32_t* ready) {
+    static_assert(kMaxGroups >= 2, "two request halves");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int vb = blockIdx.x * kTileV + w * kWV;
-    const int rows = fast_rows(R);
     bf16x8 bt[kMB][KS];
     load_bt<KS>(bt, Bt, V, rank, vb, lane & 15, lane >> 4);
     BaseFrag pre[kPF];
     prefetch_rows<VEC>(pre, base, R, K, V, 0, 0, vb);
-    for (int pos = 0; pos < K; ++pos) {
-        if (pos > 0) grid_wait(&bar[(pos - 1) * kMaxGroups], (uint32_t)G, status);
-        decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, pos, 0, R, 0, rows);
+    // Segments in order: (pos, half) for pos = 0..K-1 and each half.
+    const int H = half_split(R);
+    const bool two = H < R;
+    const int nseg = two ? 2 * K : K;
+    const int RC1 = R - H, rows0 = fast_rows(H), rows1 = two ? fast_rows(RC1) : 0;
+    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, H, 0, rows0);
+    __syncthreads();
+    gather_rows<KS>(L, A, V, rank, H, 0, rows0);
+    __syncthreads();
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int pos = two ? sg >> 1 : sg, h = two ? sg & 1 : 0;
+        const int c0 = h ? H : 0, RC = h ? RC1 : H;
+        const int ns = sg + 1;  // the next segment
+        const bool more = ns < nseg;
+        const int npos = two ? ns >> 1 : ns, nh = two ? ns & 1 : 0;
+        const int nc0 = nh ? H : 0, nRC = nh ? RC1 : H, nrows = nh ? rows1 : rows0;
+        score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos, more ? nc0 : c0);
         __syncthreads();
-        gather_rows<KS>(L, A, V, rank, R, 0, rows);
-        __syncthreads();
-        score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, 0, R, 0, vb, pos + 1 < K ? pos + 1 : pos, 0);
-        __syncthreads();
-        if (pos == 0 && ready != nullptr) grid_wait(ready, 1u, status);
-        publish_rows<KS>(L, keys, R, pos, 0, R, 0);
-        grid_arrive(&bar[pos * kMaxGroups]);
+        if (two) {
+            // the next segment's barrier is the other half's, published a segment ago
+            if (more) {
+                if (npos > 0) grid_wait(&bar[(npos - 1) * kMaxGroups + nh], (uint32_t)G, status);
+                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, nc0, nRC, nc0, nrows);
+                __syncthreads();
+                gather_rows<KS, false>(L, A, V, rank, nRC, nc0, nrows);
+            }
+            if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
+            publish_rows<KS>(L, keys, R, pos, c0, RC, c0);
+            grid_arrive(&bar[pos * kMaxGroups + h]);  // its wait also covers the gather above
+        } else {
+            if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
+            publish_rows<KS>(L, keys, R, pos, 0, H, 0);
+            grid_arrive(&bar[pos * kMaxGroups]);
+            if (more) {
+                grid_wait(&bar[pos * kMaxGroups], (uint32_t)G, status);
+                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, H, 0, rows0);
+                __syncthreads();
+                gather_rows<KS>(L, A, V, rank, H, 0, rows0);
+                __syncthreads();
+            }
+        }
     }
 }
 

@@ -15,7 +15,7 @@ namespace dspark {
 // 256-byte aligned.  The stage-wise paths zero the whole workspace first; the step
 // kernel zeroes its keys in-launch and leaves its counters and flag at zero when it
 // ends, so they are zero at every launch once the workspace was zero-filled once.
-constexpr int kMaxGroups = 1;
+constexpr int kMaxGroups = 2;  // request halves of the persistent chain
 inline size_t ws_round(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)K * 8); }
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
