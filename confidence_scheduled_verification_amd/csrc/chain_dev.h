@@ -661,16 +661,18 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
         score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos, more ? nc0 : c0);
         __syncthreads();
         if (two) {
-            // the next segment's barrier is the other half's, published a segment ago
+            // The key atomics go out first; their round trip overlaps the next
+            // segment's barrier poll, decode and gather (the next segment's barrier is
+            // the other half's, passed by every workgroup a segment ago).
+            if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
+            publish_rows<KS>(L, keys, R, pos, c0, RC, c0);
             if (more) {
                 if (npos > 0) grid_wait(&bar[(npos - 1) * kMaxGroups + nh], (uint32_t)G, status);
                 decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, nc0, nRC, nc0, nrows);
                 __syncthreads();
                 gather_rows<KS, false>(L, A, V, rank, nRC, nc0, nrows);
             }
-            if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
-            publish_rows<KS>(L, keys, R, pos, c0, RC, c0);
-            grid_arrive(&bar[pos * kMaxGroups + h]);  // its wait also covers the gather above
+            grid_arrive(&bar[pos * kMaxGroups + h]);  // its wait covers the key atomics and the gather
         } else {
             if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
             publish_rows<KS>(L, keys, R, pos, 0, H, 0);
