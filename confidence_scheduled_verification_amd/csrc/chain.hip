@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kNT, 1) void chain_pos_bf16_kernel(
             score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, 0, vb, pos, nc0);
         }
         __syncthreads();
-        publish_rows<KS>(L, keys, R, pos, c0, RC, 0);
+        uint64_t token = 0;  // kernel end orders the key atomics before the next launch
+        publish_rows<KS>(L, keys, R, pos, c0, RC, 0, token);
     }
 }
 

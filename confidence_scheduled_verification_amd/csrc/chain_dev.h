@@ -180,6 +180,34 @@ __device__ __forceinline__ void decode_rows(int32_t* s_prev, uint64_t* s_best, c
     for (int j = tid; j < rows; j += kNT) s_best[l0 + j] = 0ull;
 }
 
+// A raw buffer resource (stride 0) over `bytes` bytes at p: loads at offsets past the
+// end return zeros.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// One wave instruction of a direct-to-LDS 16-byte buffer load: lane i's 16 bytes at
+// buffer offset voff land at LDS byte address lds + 16*i.  Issued through inline
+// assembly so that the compiler does not order every later LDS read after it (it
+// cannot tell the target rows from the ones being read); callers wait for it with
+// an explicit s_waitcnt before reading what it wrote.
+__device__ __forceinline__ void dma16_to_lds(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
+    uint32_t saved;  // M0 is the compiler's too: restore it
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 // Key rows A[prev_r, :] into LDS by direct-to-LDS buffer loads: the rows region is
 // a sequence of 16-byte slots, SEGS data slots and one pad slot per row, and each
 // wave instruction fills 64 consecutive slots (lane i -> slot base + i), so no data
@@ -194,16 +222,14 @@ __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __r
     static_assert(ChainLds<KS>::LROW % 8 == 0 && SP > SEGS, "rows are whole 16-byte slots with a pad");
     const int tid = phase_tid();
     const int lane = tid & 63, w = tid >> 6;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)((uint32_t)V * (uint32_t)rank * 2u), 0x00020000);
+    const u32x4 rs = buffer_rsrc(A, (uint32_t)V * (uint32_t)rank * 2u);
     const int total = rows * SP;
     for (int t0 = w * 64; t0 < total; t0 += kNT) {
         const int t = t0 + lane;
         const int j = t / SP, sg = t - j * SP;
         uint32_t voff = 0xFFFFFFF0u;  // out of range: zeros
         if (j < RC && sg < SEGS && sg * 8 < rank) voff = ((uint32_t)L.prev[l0 + j] * (uint32_t)rank + sg * 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(L.a + (l0 * SP + t0) * 8),
-                                                 16, voff, 0, 0, 0);
+        dma16_to_lds(rs, lds_addr(L.a + (l0 * SP + t0) * 8), voff);
     }
     if (WAIT) __builtin_amdgcn_s_waitcnt(0);  // this wave's slots have landed (the caller then syncs the workgroup)
 }
@@ -551,19 +577,20 @@ __device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[k
 }
 
 // Best key over the waves, raised into the device-wide key of each request by an
-// atomic max that returns the old value (so a later s_waitcnt covers its completion).
-// Every workgroup raises every request's key: measured cheaper than reading the key
-// first to skip atomics that cannot win.
+// atomic max that returns the old value.  The returned values are folded into
+// `token` and consumed only by grid_arrive (through its s_waitcnt), so the round
+// trip of the atomics overlaps whatever the caller does in between.  Every
+// workgroup raises every request's key: measured cheaper than reading the key first
+// to skip atomics that cannot win.
+// Threads [t0, kNT) take part (waves whose memory-counter waits should not include
+// the atomics' round trip stay out).
 template <int KS>
 __device__ __forceinline__ void publish_rows(const ChainLds<KS>& L, uint64_t* keys, int R, int pos, int c0, int RC,
-                                             int l0) {
-    for (int j = phase_tid(); j < RC; j += kNT) {
+                                             int l0, uint64_t& token, int t0 = 0) {
+    for (int j = phase_tid() - t0; j >= 0 && j < RC; j += kNT - t0) {
         const uint64_t b = L.best[l0 + j];
-        if (b) {
-            const uint64_t old =
-                __hip_atomic_fetch_max(&keys[(size_t)pos * R + c0 + j], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("" ::"v"(old));
-        }
+        if (b) token ^= __hip_atomic_fetch_max(&keys[(size_t)pos * R + c0 + j], b, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -599,8 +626,9 @@ __device__ __forceinline__ void grid_wait(const uint32_t* ctr, uint32_t target, 
     __syncthreads();
 }
 
-__device__ __forceinline__ void grid_arrive(uint32_t* ctr) {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's key atomics have returned
+__device__ __forceinline__ void grid_arrive(uint32_t* ctr, uint64_t token = 0) {
+    asm volatile("" ::"v"(token));  // the key atomics folded into token have returned
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -661,22 +689,26 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
         score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos, more ? nc0 : c0);
         __syncthreads();
         if (two) {
-            // The key atomics go out first; their round trip overlaps the next
-            // segment's barrier poll, decode and gather (the next segment's barrier is
-            // the other half's, passed by every workgroup a segment ago).
+            // The key atomics go out first, from the upper half of the waves; their
+            // round trip overlaps the next segment's barrier poll, decode and gather
+            // (the next segment's barrier is the other half's, passed by every
+            // workgroup a segment ago), which run in waves 0-1 (at most 128 requests
+            // per half), whose in-order memory-counter waits then exclude the atomics.
             if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
-            publish_rows<KS>(L, keys, R, pos, c0, RC, c0);
+            uint64_t token = 0;
+            publish_rows<KS>(L, keys, R, pos, c0, RC, c0, token, kNT / 2);
             if (more) {
                 if (npos > 0) grid_wait(&bar[(npos - 1) * kMaxGroups + nh], (uint32_t)G, status);
                 decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, nc0, nRC, nc0, nrows);
                 __syncthreads();
                 gather_rows<KS, false>(L, A, V, rank, nRC, nc0, nrows);
             }
-            grid_arrive(&bar[pos * kMaxGroups + h]);  // its wait covers the key atomics and the gather
+            grid_arrive(&bar[pos * kMaxGroups + h], token);  // its wait covers the key atomics and the gather
         } else {
             if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
-            publish_rows<KS>(L, keys, R, pos, 0, H, 0);
-            grid_arrive(&bar[pos * kMaxGroups]);
+            uint64_t token = 0;
+            publish_rows<KS>(L, keys, R, pos, 0, H, 0, token);
+            grid_arrive(&bar[pos * kMaxGroups], token);
             if (more) {
                 grid_wait(&bar[pos * kMaxGroups], (uint32_t)G, status);
                 decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, H, 0, rows0);
