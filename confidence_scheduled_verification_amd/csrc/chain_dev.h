@@ -86,35 +86,43 @@ __device__ __forceinline__ void load_base(BaseFrag& f, const uint16_t* __restric
 }
 
 // Base blocks for the pipelined scorer.  With 8 | V each lane's 16-byte groups are
-// aligned, and a block is read through a buffer resource whose base is the block's
-// first row at the wanted position and whose size ends at the end of the base
-// tensor: rows past R read as zero (hardware range check), entries past V read
-// in-range data that the scorer masks, and the per-lane offset is one loop-invariant
-// 32-bit register.  Without 8 | V the element-wise clamped form is used.
+// aligned, and the blocks of one segment (requests c0.. at one position) are read
+// through a buffer resource whose base is the segment's first row at that position
+// and whose size ends at the end of the base tensor: rows past R read as zero
+// (hardware range check), entries past V read in-range data that the scorer masks.
+// A lane's offset is its loop-invariant (n16*K*V + vlane)*2 plus t blocks of
+// 16*K*V*2 bytes, all in 32 bits (K*V <= DSPARK_MAX_KV_BF16).  The resource is built
+// once per segment, so a block costs one vector add.  Without 8 | V the
+// element-wise clamped form is used.
 struct BaseSrc {
     const uint16_t* base;
-    uint64_t bytes;  // R*K*V*2
-    uint32_t voff;   // (n16*K*V + vlane) * 2
+    uint64_t bytes;    // R*K*V*2
+    uint32_t voff;     // (n16*K*V + vlane) * 2
+    uint32_t bstride;  // 16*K*V*2: one block of 16 rows
 };
 
 __device__ __forceinline__ BaseSrc base_src(const uint16_t* base, int R, int K, int V, int n16, int vlane) {
-    return BaseSrc{base, (uint64_t)R * K * V * 2, (uint32_t)(((uint64_t)n16 * K * V + vlane) * 2)};
+    return BaseSrc{base, (uint64_t)R * K * V * 2, (uint32_t)(((uint64_t)n16 * K * V + vlane) * 2),
+                   (uint32_t)(16u * (uint32_t)K * (uint32_t)V * 2u)};
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const BaseSrc& src, int c0, int pos, int K, int V) {
+    const uint64_t o = ((uint64_t)c0 * K + pos) * (uint64_t)V * 2;
+    const uint64_t rem = o < src.bytes ? src.bytes - o : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)src.base + o), 0,
+                                             (int)(uint32_t)(rem < 0xFFFFFFFFull ? rem : 0xFFFFFFFFull), 0x00020000);
+}
+
+// Block t of the segment whose resource is rs (VEC), or of segment (c0, pos).
 template <bool VEC>
-__device__ __forceinline__ void load_block(BaseFrag& f, const BaseSrc& src, int row0, int pos, int R, int K, int V,
-                                           int n16, int vlane) {
+__device__ __forceinline__ void load_block(BaseFrag& f, const BaseSrc& src, __amdgpu_buffer_rsrc_t rs, int t, int c0,
+                                           int pos, int R, int K, int V, int n16, int vlane) {
     if (VEC) {
-        const uint64_t o = ((uint64_t)row0 * K + pos) * (uint64_t)V * 2;
-        const uint64_t rem = o < src.bytes ? src.bytes - o : 0;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)src.base + o), 0, (int)(uint32_t)(rem < 0xFFFFFFFFull ? rem : 0xFFFFFFFFull),
-            0x00020000);
+        const uint32_t off = src.voff + (uint32_t)t * src.bstride;
 #pragma unroll
-        for (int p = 0; p < kMB / 2; ++p)
-            f.q[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(src.voff + 64 * p), 0, 0);
+        for (int p = 0; p < kMB / 2; ++p) f.q[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 64 * p), 0, 0);
     } else {
-        load_base<false>(f, src.base, row0 + n16, R, K, V, pos, vlane);
+        load_base<false>(f, src.base, c0 + t * 16 + n16, R, K, V, pos, vlane);
     }
 }
 
@@ -497,10 +505,12 @@ __device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&b
     uint64_t* best = L.best + l0 + n16;
     uint64_t nan_mask = 0ull;
     const BaseSrc src = base_src(base, R, K, V, n16, vlane);
+    const __amdgpu_buffer_rsrc_t rs_cur = seg_rsrc(src, c0, pos, K, V), rs_nxt = seg_rsrc(src, nc0, npos, K, V);
     // refill of the slot just emptied with ring block t (t >= PF)
     auto refill = [&](BaseFrag& f, int t) {
         const bool next = t >= nB;
-        load_block<VEC>(f, src, next ? nc0 + (t - nB) * 16 : c0 + t * 16, next ? npos : pos, R, K, V, n16, vlane);
+        load_block<VEC>(f, src, next ? rs_nxt : rs_cur, next ? t - nB : t, next ? nc0 : c0, next ? npos : pos, R, K,
+                        V, n16, vlane);
     };
     f32x4 acc[2][kMB];
     init_acc<TAIL, VEC>(acc[0], pre[0], vlane, V);
@@ -601,8 +611,9 @@ __device__ __forceinline__ void prefetch_rows(BaseFrag (&pre)[kPF], const uint16
     const int lane = threadIdx.x & 63;
     const int n16 = lane & 15, vlane = vb + 8 * (lane >> 4);
     const BaseSrc src = base_src(base, R, K, V, n16, vlane);
+    const __amdgpu_buffer_rsrc_t rs = seg_rsrc(src, c0, pos, K, V);
 #pragma unroll
-    for (int q = 0; q < kPF; ++q) load_block<VEC>(pre[q], src, c0 + q * 16, pos, R, K, V, n16, vlane);
+    for (int q = 0; q < kPF; ++q) load_block<VEC>(pre[q], src, rs, q, c0, pos, R, K, V, n16, vlane);
 }
 
 // Grid barrier.  Everything workgroups exchange inside the launch -- the argmax keys

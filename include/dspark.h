@@ -73,7 +73,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
 #define DSPARK_MAX_SLOTS 16384          /* R*K handled by the single-workgroup scheduler                 */
 #define DSPARK_MAX_RANK_BF16 256        /* bf16 chain: rank must be a multiple of 32 and at most this     */
 #define DSPARK_MAX_RANK_F32 1024        /* fp32 chain: any rank up to this                                */
-#define DSPARK_MAX_KV_BF16 (1 << 27)    /* bf16 chain: K*V at most this (32-bit per-lane base offsets)    */
+#define DSPARK_MAX_KV_BF16 (1 << 23)    /* bf16 chain: K*V at most this (32-bit offsets in 256 rows)      */
 #define DSPARK_MAX_VR_BF16 0x7FFFFFFF   /* bf16 chain: V*rank at most this (32-bit key-row offsets)       */
 
 /* Thread-local text describing the last non-OK return on this thread. */
