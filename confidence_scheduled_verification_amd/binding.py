@@ -24,10 +24,12 @@ STATUS_CONF_SANITIZED = 2
 STATUS_COST_INVALID = 4
 STATUS_SYNC_TIMEOUT = 8
 MAX_SLOTS = 16384
+RULE_ARGMAX = 0
+RULE_FIRST_DROP = 1
 
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
            "dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
-           "dspark_step", "dspark_set_timing_events", "dspark_force_monotone"]
+           "dspark_step", "dspark_step_sized", "dspark_set_timing_events", "dspark_force_monotone"]
 
 
 class DSparkError(RuntimeError):
@@ -58,10 +60,12 @@ def lib():
         L.dspark_chain.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, p, sz, p]
         L.dspark_survival.argtypes = [p, i, i, p, p, p]
         L.dspark_topb_select.argtypes = [p, i, i, p, p, p, p]
-        L.dspark_choose_budget.argtypes = [p, i, i, i, i, p, i, p, i, p, p, p, p, p]
+        L.dspark_choose_budget.argtypes = [p, i, i, i, i, p, i, p, i, i, p, p, p, p, p]
         L.dspark_allocate.argtypes = [p, p, i, i, p, p, p, p, p, p]
         L.dspark_step.argtypes = [p, p, p, i, p, i, i, i, i, p, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p, p,
                                   p, p, p, sz, p]
+        L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, i, i, p, i, p, i, p, p, p, p,
+                                        p, p, p, p, p, p, p, p, sz, p]
         L.dspark_set_timing_events.argtypes = [p, p]
         L.dspark_force_monotone.argtypes = [p, i]
         for name in EXPORTS:
@@ -151,11 +155,11 @@ def dspark_topb_select(surv, order, sorted_surv, rank=None, stream=None):
 
 
 def dspark_choose_budget(sorted_surv, n_sampling: int, T: int, num_reqs: int, verify_cost, draft_cost, b_star,
-                         best_obj, obj=None, status=None, stream=None):
+                         best_obj, obj=None, status=None, stream=None, rule: int = RULE_ARGMAX):
     n = sorted_surv.numel()
     _contig(sorted_surv, verify_cost, draft_cost, obj)
     _check(lib().dspark_choose_budget(_p(sorted_surv), n, n_sampling, T, num_reqs, _p(verify_cost),
-                                      verify_cost.numel(), _p(draft_cost), draft_cost.numel(), _p(b_star),
+                                      verify_cost.numel(), _p(draft_cost), draft_cost.numel(), rule, _p(b_star),
                                       _p(best_obj), _p(obj), _p(status), _stream(stream)))
 
 
@@ -184,6 +188,31 @@ def dspark_step(base, A, Bt, dtype: int, prev0, conf, n_sampling: int, T: int, n
                              _p(out.tokens), _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
                              _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
                              _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_step_sized(base, A, Bt, dtype: int, prev0, conf, size_conf, rule: int, n_sampling: int, T: int,
+                      num_reqs: int, verify_cost, draft_cost, out: "StepBuffers", ws, status=None, stream=None):
+    """dspark_step with B sized from `size_conf` ([R', K], e.g. an older step's confidences, or
+    None for the current ones) under admission rule `rule`."""
+    R, K, V = base.shape
+    rank = A.shape[1]
+    if tuple(conf.shape) != (R, K):
+        raise ValueError("dspark_step_sized: conf must be [R, K]")
+    size_R = -1                      # -1: size from conf itself
+    if size_conf is not None:
+        if size_conf.dim() != 2 or size_conf.shape[1] != K:
+            raise ValueError("dspark_step_sized: size_conf must be [R', K]")
+        size_R = size_conf.shape[0]
+    _contig(base, A, Bt, prev0, conf, size_conf, verify_cost, draft_cost)
+    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
+        _elem_ok(t, dtype, n)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dspark_step_sized(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(conf),
+                                   _p(size_conf), size_R, rule, n_sampling, T, num_reqs, _p(verify_cost),
+                                   verify_cost.numel(), _p(draft_cost), draft_cost.numel(), _p(out.tokens),
+                                   _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
+                                   _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
+                                   _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
 
 
 def dspark_set_timing_events(before_chain=None, after_chain=None):
@@ -221,4 +250,5 @@ class StepBuffers:
 def workspace(R: int, K: int, V: int, rank: int, dtype: int, device="cuda"):
     import torch
     n = max(dspark_workspace_bytes(R, K, V, rank, dtype), 8)
-    return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)  # zero-filled once, as the library requires
+    # zero-filled once, as the library requires; it then serves calls of any shape up to (R, K)
+    return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)

@@ -18,7 +18,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     # packed fp32 vector ops stay off on this target (the host pass ignores the feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -27,13 +26,26 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libdspark.so next to this file; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every HIP source into libdspark.so next to this file; returns its path.
+
+    The sources compile in parallel to objects under _build/ and are then linked."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, obj, subprocess.Popen(cmd)))
+    failed = [src for src, _, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc {' '.join(failed)}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o, _ in procs], "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+        print(" ".join(link), flush=True)
+    subprocess.check_call(link)
     os.replace(tmp, LIB)
     return LIB
 

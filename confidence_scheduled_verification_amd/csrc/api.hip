@@ -9,6 +9,8 @@
 #include "dspark.h"
 #include "kernels.h"
 
+static_assert(dspark::kMaxSlotsWs == DSPARK_MAX_SLOTS, "the step counters are sized for the slot limit");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -119,10 +121,11 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
     if (R == 0 || K == 0) return DSPARK_OK;
     if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
+    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
-                        V,      rank, tokens, chained_logits, status, (uint64_t*)ws,
-                        (uint32_t*)((char*)ws + dspark::ws_keys_bytes(R, K))};
-    hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_total_bytes(R, K) / 8, s);
+                        V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
+                        (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K))};
+    hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_chain_bytes(R, K) / 8, s);
     if (e != hipSuccess) return hip_fail(e, "chain (zero keys)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
     if (e != hipSuccess) return hip_fail(e, "chain");
@@ -150,15 +153,17 @@ int dspark_topb_select(const float* surv, int R, int K, int32_t* order, float* s
 }
 
 int dspark_choose_budget(const float* sorted_surv, int n_slots, int n_sampling, int T, int num_reqs,
-                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len, int rule,
                          int32_t* b_star, double* best_obj, double* obj, uint32_t* status, void* stream) {
     if (!b_star || !best_obj) return fail(DSPARK_EINVAL, "choose_budget: NULL output");
+    if (rule != DSPARK_RULE_ARGMAX && rule != DSPARK_RULE_FIRST_DROP)
+        return fail(DSPARK_EINVAL, "choose_budget: unknown admission rule %d", rule);
     if (n_slots < 0) return fail(DSPARK_EINVAL, "choose_budget: negative n_slots %d", n_slots);
     if (n_slots > 0 && !sorted_surv) return fail(DSPARK_EINVAL, "choose_budget: NULL sorted_surv");
     int rc = check_sched_scalars(n_slots, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
     if (rc != DSPARK_OK) return rc;
     const int bmax = std::min(n_slots, verify_len - 1 - T);
-    dspark::BudgetArgs a{sorted_surv, n_slots, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax,
+    dspark::BudgetArgs a{sorted_surv, n_slots, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, rule,
                          b_star, best_obj, obj, status};
     const hipError_t e = dspark::launch_budget(a, (hipStream_t)stream);
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "choose_budget");
@@ -178,31 +183,42 @@ int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, c
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "allocate");
 }
 
-int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
-                int V, int rank, const float* conf, int n_sampling, int T, int num_reqs, const float* verify_cost,
-                int verify_len, const float* draft_cost, int draft_len, int32_t* tokens, float* surv,
-                int32_t* order, float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len,
-                int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws,
-                size_t ws_bytes, void* stream) {
+int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R,
+                      int K, int V, int rank, const float* conf, const float* size_conf, int size_R, int rule,
+                      int n_sampling, int T, int num_reqs, const float* verify_cost, int verify_len,
+                      const float* draft_cost, int draft_len, int32_t* tokens, float* surv, int32_t* order,
+                      float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len, int32_t* offsets,
+                      int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws, size_t ws_bytes,
+                      void* stream) {
     int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
     if (rc != DSPARK_OK) return rc;
     const long long n = (long long)R * K;
     if (n > DSPARK_MAX_SLOTS) return fail(DSPARK_EUNSUPPORTED, "step: %lld slots exceed %d", n, DSPARK_MAX_SLOTS);
     if (!b_star || !best_obj || !offsets || (R > 0 && !prefix_len) || (n > 0 && (!ver_idx || !conf)))
         return fail(DSPARK_EINVAL, "step: a required schedule pointer is NULL");
+    if (rule != DSPARK_RULE_ARGMAX && rule != DSPARK_RULE_FIRST_DROP)
+        return fail(DSPARK_EINVAL, "step: unknown admission rule %d", rule);
+    if (size_R < -1) return fail(DSPARK_EINVAL, "step: size_R %d < -1", size_R);
+    const bool stale = size_R >= 0;  // -1: size from conf itself
+    const long long ns = stale ? (long long)size_R * K : n;
+    if (ns > DSPARK_MAX_SLOTS)
+        return fail(DSPARK_EUNSUPPORTED, "step: %lld sizing slots exceed %d", ns, DSPARK_MAX_SLOTS);
+    if (stale && ns > 0 && !size_conf) return fail(DSPARK_EINVAL, "step: NULL size_conf with %d rows", size_R);
     rc = check_sched_scalars((int)n, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
     if (rc != DSPARK_OK) return rc;
     if (n > 0 && (rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
     const int bmax = std::min((int)n, verify_len - 1 - T);
+    const dspark::SizingArgs sizing{stale ? 1 : 0, size_conf, stale ? size_R : R,
+                                    std::min((int)ns, verify_len - 1 - T), rule};
     hipError_t e;
     if (n > 0 && dtype == DSPARK_BF16) {
         // One cooperative launch for the whole step when it fits on the device.
         char* w = (char*)ws;
-        dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status, (uint64_t*)w,
-                            (uint32_t*)(w + dspark::ws_keys_bytes(R, K) + dspark::ws_bar_bytes(K)), conf,
-                            n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order, sorted_surv,
-                            b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens};
+        dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status,
+                            (uint64_t*)(w + dspark::ws_sync_bytes()), (uint32_t*)w, conf,
+                            n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, sizing, surv, order,
+                            sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens};
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
         e = dspark::launch_step_single(st, s);
@@ -214,14 +230,16 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
         if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "step (single launch)");
         (void)hipGetLastError();  // nothing was enqueued; run the stage-wise launches
     }
-    dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, surv, order,
+    dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, sizing, surv, order,
                               sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, status,
-                              (uint64_t*)ws, n > 0 ? (int)(dspark::ws_total_bytes(R, K) / 8) : 0};
+                              (uint64_t*)((char*)ws + dspark::ws_sync_bytes()),
+                              n > 0 ? (int)(dspark::ws_chain_bytes(R, K) / 8) : 0};
     e = dspark::launch_sched_fused(sa, s);
     if (e != hipSuccess) return hip_fail(e, "step (schedule)");
     if (n == 0) return DSPARK_OK;
-    dspark::ChainArgs a{base, A,       Bt,     dtype,         prev0, R, K, V, rank, tokens,
-                        nullptr, status, (uint64_t*)ws, (uint32_t*)((char*)ws + dspark::ws_keys_bytes(R, K))};
+    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
+    dspark::ChainArgs a{base,    A,      Bt,     dtype, prev0, R, K, V, rank, tokens, nullptr, status,
+                        (uint64_t*)chain_ws, (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K))};
     if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
         return hip_fail(e, "step (timing event)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
@@ -230,6 +248,18 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
         return hip_fail(e, "step (timing event)");
     e = dspark::launch_chain_finalize(a.keys, tokens, R, K, ver_idx, b_star, ver_tokens, s);
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (finalize)");
+}
+
+int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
+                int V, int rank, const float* conf, int n_sampling, int T, int num_reqs, const float* verify_cost,
+                int verify_len, const float* draft_cost, int draft_len, int32_t* tokens, float* surv,
+                int32_t* order, float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len,
+                int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws,
+                size_t ws_bytes, void* stream) {
+    return dspark_step_sized(base, A, Bt, dtype, prev0, R, K, V, rank, conf, nullptr, -1, DSPARK_RULE_ARGMAX,
+                             n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len, tokens, surv,
+                             order, sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens, status,
+                             ws, ws_bytes, stream);
 }
 
 int dspark_set_timing_events(void* before_chain, void* after_chain) {

@@ -9,18 +9,25 @@
 
 namespace dspark {
 
-// Chain workspace: the per-position argmax keys [K][R] (uint64), the persistent
-// chain kernel's grid-barrier counters [K][kMaxGroups] (uint32), then the
-// single-launch step kernel's counters [K][kMaxGroups] and ready flag (uint32); each region
-// 256-byte aligned.  The stage-wise paths zero the whole workspace first; the step
-// kernel zeroes its keys in-launch and leaves its counters and flag at zero when it
-// ends, so they are zero at every launch once the workspace was zero-filled once.
+// Workspace layout, each region 256-byte aligned:
+//   [0, ws_sync_bytes)   the single-launch step kernel's counters [K][kMaxGroups] and
+//                        ready flag (uint32), sized for the largest K so that the region
+//                        does not move with the shape;
+//   then                 the per-position argmax keys [K][R] (uint64) and the
+//                        persistent chain kernel's barrier counters [K][kMaxGroups].
+// The stage-wise paths zero the keys and counters they use first.  The step kernel
+// zeroes its keys in-launch and puts its counters and flag back to zero when it ends,
+// so once the workspace was zero-filled one time they are zero at every launch,
+// whatever R and K the earlier calls had.
 constexpr int kMaxGroups = 2;  // request halves of the persistent chain
+constexpr int kMaxSlotsWs = 16384;
 inline size_t ws_round(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t ws_sync_bytes() { return ws_round((size_t)(kMaxSlotsWs * kMaxGroups + 1) * 4); }
 inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)K * 8); }
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
-inline size_t ws_step_bytes(int K) { return ws_round((size_t)(K * kMaxGroups + 1) * 4); }
-inline size_t ws_total_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K) + ws_step_bytes(K); }
+// Keys and chain counters: what the stage-wise paths clear.
+inline size_t ws_chain_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
+inline size_t ws_total_bytes(int R, int K) { return ws_sync_bytes() + ws_chain_bytes(R, K); }
 
 struct ChainArgs {
     const void* base;
@@ -36,12 +43,24 @@ struct ChainArgs {
     uint32_t* bar;   // [K, kMaxGroups] barrier counters, zeroed before the first position
 };
 
+// Budget sizing: from a separate confidence array [R][K] (separate != 0; conf may be
+// null when R == 0) or from the current confidences, its largest B and the admission
+// rule (0 argmax, 1 first drop).
+struct SizingArgs {
+    int separate;
+    const float* conf;
+    int R;
+    int bmax;
+    int rule;
+};
+
 struct BudgetArgs {
     const float* sorted_surv;
     int n, n_sampling, T, num_reqs;
     const float* vc;
     const float* dc;
     int bmax;
+    int rule;
     int32_t* b_star;
     double* best_obj;
     double* obj;
@@ -54,6 +73,7 @@ struct FusedSchedArgs {
     const float* vc;
     const float* dc;
     int bmax;
+    SizingArgs sizing;
     float* surv;
     int32_t* order;
     float* sorted_surv;
@@ -85,6 +105,7 @@ struct StepArgs {
     const float* vc;
     const float* dc;
     int bmax;
+    SizingArgs sizing;
     float* surv;
     int32_t* order;
     float* sorted_surv;

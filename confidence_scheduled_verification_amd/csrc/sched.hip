@@ -15,7 +15,7 @@ constexpr int kST = 1024;  // scheduler threads
 
 __global__ __launch_bounds__(kST, 1) void sched_fused_kernel(
     const float* __restrict__ conf, int R, int K, int n_sampling, int T, int num_reqs,
-    const float* __restrict__ vc, const float* __restrict__ dc, int bmax, float* __restrict__ surv_out,
+    const float* __restrict__ vc, const float* __restrict__ dc, int bmax, SizingArgs sizing, float* __restrict__ surv_out,
     int32_t* __restrict__ order, float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
     double* __restrict__ best_obj, int32_t* __restrict__ prefix_len, int32_t* __restrict__ offsets,
     int32_t* __restrict__ ver_idx, uint32_t* status, uint64_t* __restrict__ ws, int ws_words) {
@@ -23,7 +23,8 @@ __global__ __launch_bounds__(kST, 1) void sched_fused_kernel(
     // The chain's workspace (argmax keys, barrier counters) starts from zero; this launch
     // precedes the chain kernels on the stream.
     for (int j = threadIdx.x; j < ws_words; j += kST) ws[j] = 0ull;
-    sched_pass<kST>(sh, conf, R, K, n_sampling, T, num_reqs, vc, dc, bmax, surv_out, order, sorted_surv, b_star,
+    const Sizing sz{sizing.separate, sizing.conf, sizing.R, sizing.bmax, sizing.rule};
+    sched_pass<kST>(sh, conf, R, K, n_sampling, T, num_reqs, vc, dc, bmax, sz, surv_out, order, sorted_surv, b_star,
                     best_obj, prefix_len, offsets, ver_idx, status);
 }
 
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kST, 1) void topb_kernel(const float* __restrict__ 
 
 __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict__ sorted_surv, int n, int n_sampling,
                                                        int T, int num_reqs, const float* __restrict__ vc,
-                                                       const float* __restrict__ dc, int bmax,
+                                                       const float* __restrict__ dc, int bmax, int rule,
                                                        int32_t* __restrict__ b_star, double* __restrict__ best_obj,
                                                        double* __restrict__ obj, uint32_t* status) {
     __shared__ SchedShared<kST> sh;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict_
         sh.key[j] = key;
     }
     __syncthreads();
-    choose_budget_lds<kST>(sh, cp, n, n_pad, n_sampling, bmax, b_star, best_obj, obj, status);
+    choose_budget_lds<kST>(sh, cp, n, n_pad, n_sampling, bmax, rule, b_star, best_obj, obj, status);
 }
 
 __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restrict__ order,
@@ -109,7 +110,7 @@ hipError_t launch_topb(const float* surv, int R, int K, int32_t* order, float* s
 
 hipError_t launch_budget(const BudgetArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kST), 0, s, a.sorted_surv, a.n, a.n_sampling, a.T, a.num_reqs,
-                       a.vc, a.dc, a.bmax, a.b_star, a.best_obj, a.obj, a.status);
+                       a.vc, a.dc, a.bmax, a.rule, a.b_star, a.best_obj, a.obj, a.status);
     return hipGetLastError();
 }
 
@@ -123,7 +124,7 @@ hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, i
 
 hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sched_fused_kernel, dim3(1), dim3(kST), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T,
-                       a.num_reqs, a.vc, a.dc, a.bmax, a.surv, a.order, a.sorted_surv, a.b_star, a.best_obj,
+                       a.num_reqs, a.vc, a.dc, a.bmax, a.sizing, a.surv, a.order, a.sorted_surv, a.b_star, a.best_obj,
                        a.prefix_len, a.offsets, a.ver_idx, a.status, a.ws, a.ws_words);
     return hipGetLastError();
 }

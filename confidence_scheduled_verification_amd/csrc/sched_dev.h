@@ -3,7 +3,10 @@
 // for one workgroup of NT threads working out of LDS:
 //   survival      s[r,i] = c[r,0] * ... * c[r,i]        (float32, increasing i)
 //   global top-B  slots ranked by (s desc, request asc, position asc)
-//   budget        B* = smallest argmax_B fl64(N + S_B) / fl64(vc[T+B] + dc[num_reqs])
+//   budget        B* = smallest argmax_B fl64(N + S_B) / fl64(vc[T+B] + dc[num_reqs]), or
+//                 the first-drop rule: admit slots in rank order while that ratio
+//                 strictly rises (DSpark summary "How DSpark Speeds Up LLM
+//                 Inference", section "Verify smarter")
 //   allocation    per-request prefix lengths, offsets and the compacted slot list
 //
 //   * Ranking is a stable LSD radix sort of 32-bit keys (0x3F800000 - bits(s):
@@ -30,6 +33,8 @@ namespace {
 constexpr int kMaxN = 16384;           // slots
 constexpr uint32_t kOne = 0x3F800000u; // bits of 1.0f
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;
+constexpr int kRuleArgmax = 0;
+constexpr int kRuleFirstDrop = 1;
 
 struct U192 {
     uint64_t a, b, c;  // little-endian limbs
@@ -148,6 +153,7 @@ struct SchedShared {
     uint32_t wsum[SW];
     U192 wsum192[SW];
     double wbest_f[SW];
+    double wbest_v[SW];
     int32_t wbest_b[SW];
     int32_t b_star;
 };
@@ -355,13 +361,14 @@ __device__ __forceinline__ void write_ranking(const SchedShared<NT>& sh, int n, 
     }
 }
 
-// The cost-table entries one thread evaluates in stage 4 (B = tid*C + q, and B = n_pad
-// for the last thread), read at the start of the kernel so that their memory latency
-// overlaps the earlier stages.
+// The cost-table entries one thread evaluates in stage 4 (B = tid*C + q, and
+// B = tid*C + C, the next thread's first candidate, which the first-drop rule compares
+// against and which is n_pad for the last thread), read at the start of the kernel so
+// that their memory latency overlaps the earlier stages.
 template <int NT>
 struct CostPrefetch {
     float vc[kMaxN / NT];
-    float vc_last;
+    float vc_next;
     float dc;
 };
 
@@ -373,14 +380,17 @@ __device__ __forceinline__ void prefetch_costs(CostPrefetch<NT>& cp, const float
     const int j0 = threadIdx.x * C;
 #pragma unroll
     for (int q = 0; q < kMaxN / NT; ++q) cp.vc[q] = (q < C && j0 + q <= bmax) ? vc[T + j0 + q] : 0.f;
-    cp.vc_last = (threadIdx.x == NT - 1 && bmax == n_pad) ? vc[T + n_pad] : 0.f;
+    cp.vc_next = (j0 + C <= bmax) ? vc[T + j0 + C] : 0.f;
     cp.dc = dc[num_reqs];
 }
 
-// Stage 4 over the keys in sh.key (rank order).  Leaves B* in sh.b_star.
+// Stage 4 over the keys in sh.key (rank order).  Leaves the budget in sh.b_star.
+// rule kRuleArgmax: the smallest B with the largest f.  rule kRuleFirstDrop: the first
+// B whose successor does not raise f (f(B+1) <= f(B)), else bmax.  Every f(B) is the
+// same double in both rules, so where f rises to a single peak they agree.
 template <int NT>
 __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const CostPrefetch<NT>& cp, int n, int n_pad,
-                                                  int n_sampling, int bmax, int32_t* __restrict__ b_star,
+                                                  int n_sampling, int bmax, int rule, int32_t* __restrict__ b_star,
                                                   double* __restrict__ best_obj, double* __restrict__ obj,
                                                   uint32_t* status) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -395,64 +405,90 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const Cos
     U192 S = block_excl_scan192<NT>(sh, local);
     const double dcost = (double)cp.dc;
     const uint64_t ns_hi = (uint64_t)(uint32_t)n_sampling << 21;  // n_sampling * 2^149: bit 149 is bit 21 of limb 2
-    double bf = -INFINITY;
-    int bb = 0x7FFFFFFF;
     bool bad = false;
-    auto eval = [&](int B, float vcost) {
+    auto eval = [&](float vcost) -> double {
         U192 X = S;
         X.c += ns_hi;
         const double num = fixed_to_double(X);
         const double den = (double)vcost + dcost;
-        double f;
-        if (den > 0.0 && den <= 1.7976931348623157e308) {
-            f = num / den;
-        } else {
-            f = -INFINITY;
-            bad = true;
+        if (den > 0.0 && den <= 1.7976931348623157e308) return num / den;
+        bad = true;
+        return -INFINITY;
+    };
+    double bf = -INFINITY;   // argmax candidate of this thread: f and B
+    int bb = 0x7FFFFFFF;
+    double fprev = 0.0;      // f(B-1) of the previous candidate of this thread
+    int drop = 0x7FFFFFFF;   // first-drop candidate: B with f(B+1) <= f(B), and f(B)
+    double fdrop = 0.0;
+    auto take = [&](int B, double f, bool own) {
+        if (own) {
+            if (obj) obj[B] = f;
+            if (f > bf || (f == bf && B < bb)) {
+                bf = f;
+                bb = B;
+            }
+            if (B == bmax && drop == 0x7FFFFFFF) {  // no drop before bmax: admission ends there
+                drop = B;
+                fdrop = f;
+            }
         }
-        if (obj) obj[B] = f;
-        if (f > bf || (f == bf && B < bb)) {
-            bf = f;
-            bb = B;
+        if (B > j0 && !(f > fprev) && drop > B - 1) {
+            drop = B - 1;
+            fdrop = fprev;
         }
+        fprev = f;
     };
 #pragma unroll
     for (int q = 0; q < kMaxN / NT; ++q) {
         if (q < C) {
             const int B = j0 + q;
-            if (B <= bmax) eval(B, cp.vc[q]);
+            if (B <= bmax) take(B, eval(cp.vc[q]), true);
             if (B < n) S = add192(S, fixed_from_bits(kOne - sh.key[B]));
         }
     }
-    if (tid == NT - 1 && bmax == n_pad) eval(n_pad, cp.vc_last);
+    // B = j0 + C: the next thread's first candidate (compared against f(j0 + C - 1)), or
+    // B = n_pad for the last thread.
+    if (j0 + C <= bmax) take(j0 + C, eval(cp.vc_next), tid == NT - 1);
     if (bad) raise_status(status, kStatusCostInvalid);
-    // Block argmax: larger f, then smaller B.
+    // Block reduction: argmax takes the larger f, then the smaller B; first drop takes
+    // the smaller B.  (kf, kb) is the key, vf the objective carried along.
+    double kf = bf, vf = bf;
+    int kb = bb;
+    if (rule == kRuleFirstDrop) {
+        kf = drop == 0x7FFFFFFF ? -INFINITY : 0.0;
+        kb = drop;
+        vf = fdrop;
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
-        const double of = shfl_xor_f64(bf, m);
-        const int ob = __shfl_xor(bb, m, 64);
-        if (of > bf || (of == bf && ob < bb)) {
-            bf = of;
-            bb = ob;
+        const double of = shfl_xor_f64(kf, m);
+        const double ov = shfl_xor_f64(vf, m);
+        const int ob = __shfl_xor(kb, m, 64);
+        if (of > kf || (of == kf && ob < kb)) {
+            kf = of;
+            kb = ob;
+            vf = ov;
         }
     }
     if (lane == 0) {
-        sh.wbest_f[w] = bf;
-        sh.wbest_b[w] = bb;
+        sh.wbest_f[w] = kf;
+        sh.wbest_v[w] = vf;
+        sh.wbest_b[w] = kb;
     }
     __syncthreads();
     if (tid == 0) {
-        double f = sh.wbest_f[0];
+        double f = sh.wbest_f[0], v = sh.wbest_v[0];
         int b = sh.wbest_b[0];
         for (int q = 1; q < kSW; ++q) {
             if (sh.wbest_f[q] > f || (sh.wbest_f[q] == f && sh.wbest_b[q] < b)) {
                 f = sh.wbest_f[q];
+                v = sh.wbest_v[q];
                 b = sh.wbest_b[q];
             }
         }
         sh.b_star = b;
         if (b_star) *b_star = b;
-        if (best_obj) *best_obj = f;
+        if (best_obj) *best_obj = v;
     }
     __syncthreads();
 }
@@ -507,27 +543,68 @@ __device__ __forceinline__ uint8_t* selection_map(SchedShared<NT>& sh) {
 }
 
 
+// Where the budget is sized from: the current confidences (separate == 0), or another
+// array [R][K] such as the one of one or two steps earlier (vLLM blog, "Scheduling the
+// budget": B is sized from a one-step-old confidence buffer while the slots are handed
+// out with current values).  bmax is the largest B of that sizing, rule the admission
+// rule.
+struct Sizing {
+    int separate;
+    const float* conf;
+    int R;
+    int bmax;
+    int rule;
+};
+
 // Stages 2-5 in sequence: survival (optionally written out), ranking (written out),
 // budget, selection and allocation.  Leaves B* in sh.b_star and the selection map in
 // LDS; every output pointer except the required ones may be null.  lds_ver (may be
 // null, may alias sh.key, which is free by then): an LDS copy of ver_idx[0, B*).
+// With a separate sizing array, B is chosen from its survivals first (same survival,
+// ranking and budget code over its slots), capped at R*K, and best_obj is the sizing
+// objective.
 template <int NT>
 __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __restrict__ conf, int R, int K,
                                            int n_sampling, int T, int num_reqs, const float* __restrict__ vc,
-                                           const float* __restrict__ dc, int bmax, float* __restrict__ surv_out,
-                                           int32_t* __restrict__ order, float* __restrict__ sorted_surv,
-                                           int32_t* __restrict__ b_star, double* __restrict__ best_obj,
-                                           int32_t* __restrict__ prefix_len, int32_t* __restrict__ offsets,
-                                           int32_t* __restrict__ ver_idx, uint32_t* status,
-                                           int32_t* lds_ver = nullptr) {
-    const int n = R * K, n_pad = pad_slots<NT>(n);
-    survival_to_lds<NT>(sh, conf, R, K, n_pad, surv_out, status);
-    sort_slots<NT>(sh, n_pad);
-    CostPrefetch<NT> cp;  // requested here so the loads overlap the write-out and the exact scan
-    prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bmax, n_pad);
-    write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
-    choose_budget_lds<NT>(sh, cp, n, n_pad, n_sampling, bmax, b_star, best_obj, nullptr, status);
-    const int B = sh.b_star;
+                                           const float* __restrict__ dc, int bmax, const Sizing& sz,
+                                           float* __restrict__ surv_out, int32_t* __restrict__ order,
+                                           float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
+                                           double* __restrict__ best_obj, int32_t* __restrict__ prefix_len,
+                                           int32_t* __restrict__ offsets, int32_t* __restrict__ ver_idx,
+                                           uint32_t* status, int32_t* lds_ver = nullptr) {
+    const int n = R * K;
+    // One or two passes of the same code (a loop, so that the stage code exists once in
+    // the kernel): with a separate sizing array, pass 0 sizes B from it and pass 1 ranks
+    // the current slots; otherwise one pass does both.
+    const int passes = sz.separate ? 2 : 1;
+    int B = 0;
+#pragma unroll 1
+    for (int ps = 0; ps < passes; ++ps) {
+        const bool sizing = ps == 0, last = ps == passes - 1;
+        const float* src = sz.separate && sizing ? sz.conf : conf;
+        const int rows = sz.separate && sizing ? sz.R : R;
+        const int m = rows * K, m_pad = pad_slots<NT>(m);
+        survival_to_lds<NT>(sh, src, rows, K, m_pad, last ? surv_out : nullptr, status);
+        sort_slots<NT>(sh, m_pad);
+        if (sizing) {
+            const int bm = sz.separate ? sz.bmax : bmax;
+            CostPrefetch<NT> cp;  // requested here so the loads overlap the write-out and the exact scan
+            prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
+            if (last) write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
+            choose_budget_lds<NT>(sh, cp, m, m_pad, n_sampling, bm, sz.rule, last ? b_star : nullptr, best_obj,
+                                  nullptr, status);
+            B = sh.b_star;  // every thread reads it before the next barrier
+        } else {
+            write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
+        }
+    }
+    if (sz.separate) {
+        B = B < n ? B : n;
+        if (threadIdx.x == 0) {
+            sh.b_star = B;
+            if (b_star) *b_star = B;
+        }
+    }
     uint8_t* sel = selection_map<NT>(sh);
     for (int j = threadIdx.x; j < n; j += NT) sel[sh.id[j]] = (uint8_t)(j < B);
     __syncthreads();

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kNT, 1) void step_single_bf16_kernel(StepArgs a) {
     __syncthreads();
     if (threadIdx.x == 0) set_agent_u32(ready, 1u);
     int32_t* lds_ver = reinterpret_cast<int32_t*>(sh.key);
-    sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, a.surv, a.order,
+    const Sizing sz{a.sizing.separate, a.sizing.conf, a.sizing.R, a.sizing.bmax, a.sizing.rule};
+    sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, sz, a.surv, a.order,
                     a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_ver);
     __syncthreads();
     // each chain workgroup arrives for half 0 before half 1 of a position

@@ -69,6 +69,12 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
 #define DSPARK_STATUS_SYNC_TIMEOUT 8u   /* the single-launch chain waited too long at a grid barrier (its
                                            workgroups were not all resident); tokens are then unreliable    */
 
+/* Admission rules of stage 4. */
+#define DSPARK_RULE_ARGMAX 0      /* the smallest B with the largest f(B) (vLLM blog, "Scheduling the budget")  */
+#define DSPARK_RULE_FIRST_DROP 1  /* admit slots in rank order while f strictly rises; stop at the first B
+                                     with f(B+1) <= f(B), else Bmax (DSpark summary "How DSpark Speeds Up
+                                     LLM Inference", section "Verify smarter")                              */
+
 /* Limits. */
 #define DSPARK_MAX_SLOTS 16384          /* R*K handled by the single-workgroup scheduler                 */
 #define DSPARK_MAX_RANK_BF16 256        /* bf16 chain: rank must be a multiple of 32 and at most this     */
@@ -82,8 +88,11 @@ const char* dspark_last_error(void);
 /* Library version string. */
 const char* dspark_version(void);
 
-/* Bytes of device workspace needed by dspark_chain / dspark_step for this shape
- * (0 when R*K == 0).  The workspace needs no initialisation. */
+/* Bytes of device workspace needed by dspark_chain / dspark_step / dspark_step_sized
+ * for this shape (0 when R*K == 0).  Zero-fill a workspace once, before its first
+ * use: the single-launch step keeps grid-barrier counters and a ready flag in it and
+ * leaves them at zero when it ends, so later calls need no further clearing.  A
+ * workspace sized for one shape serves any smaller R and K. */
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
 
 /*
@@ -156,9 +165,16 @@ int dspark_topb_select(const float* surv, int R, int K, int32_t* order, float* s
  *   Bmax = min(n_slots, verify_len - 1 - T)
  *   f(B) = fl64(n_sampling + S_B) / fl64(verify_cost[T+B] + draft_cost[num_reqs]),  B = 0..Bmax
  * where S_B is the exact sum of sorted_surv[0..B) (rounded to double once, with
- * n_sampling) and the division is IEEE double.  b_star is the smallest B with the
- * largest f.  A denominator that is not a positive finite number gives f(B) = -inf
- * and sets DSPARK_STATUS_COST_INVALID.
+ * n_sampling) and the division is IEEE double.  A denominator that is not a positive
+ * finite number gives f(B) = -inf and sets DSPARK_STATUS_COST_INVALID.
+ *   rule DSPARK_RULE_ARGMAX:     b_star is the smallest B with the largest f;
+ *   rule DSPARK_RULE_FIRST_DROP: slots are admitted one at a time in rank order while
+ *        f strictly rises: b_star is the smallest B < Bmax with f(B+1) <= f(B), else
+ *        Bmax (DSpark summary "How DSpark Speeds Up LLM Inference", section "Verify
+ *        smarter": admission stops as soon as throughput would fall).
+ * Both rules see the same f values; the first-drop b_star never exceeds the argmax
+ * one, and they agree whenever f rises to a single peak (e.g. for a linear cost).
+ * best_obj is f(b_star).  An unknown rule returns DSPARK_EINVAL.
  *   sorted_surv  [n_slots] fp32, non-increasing, entries in [0,1]
  *   n_sampling   requests that sample a bonus token this step (>= 0)
  *   T            non-draft tokens already in the step, 0 <= T < verify_len
@@ -169,7 +185,7 @@ int dspark_topb_select(const float* surv, int R, int K, int32_t* order, float* s
  * Limit: n_slots <= DSPARK_MAX_SLOTS.
  */
 int dspark_choose_budget(const float* sorted_surv, int n_slots, int n_sampling, int T, int num_reqs,
-                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                         const float* verify_cost, int verify_len, const float* draft_cost, int draft_len, int rule,
                          int32_t* b_star, double* best_obj, double* obj, uint32_t* status, void* stream);
 
 /*
@@ -207,6 +223,35 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
                 int32_t* b_star, double* best_obj,
                 int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_step with the budget sized from a separate confidence array and a chosen
+ * admission rule (vLLM blog, "Scheduling the budget": B is sized from a
+ * double-buffered confidence array one step old, while the slots are handed to the
+ * requests with current values; the DSpark summary's production notes size it from
+ * confidences two steps earlier).
+ *   size_conf  [size_R, K] fp32 confidences B is sized from (e.g. the previous step's
+ *              conf buffer); may be NULL when size_R is 0 or -1
+ *   size_R     rows of size_conf (may differ from R), size_R*K <= DSPARK_MAX_SLOTS;
+ *              0 sizes from no slots at all (B = 0); -1 sizes from `conf` itself
+ *   rule       DSPARK_RULE_ARGMAX or DSPARK_RULE_FIRST_DROP (see dspark_choose_budget)
+ * Sizing: survival, ranking and budget (stages 2-4) over size_conf's slots with this
+ * step's n_sampling, T, num_reqs and cost tables, Bmax = min(size_R*K, verify_len-1-T).
+ * Allocation: the first min(B, R*K) slots of the ranking of the CURRENT conf; *b_star
+ * receives that capped value and *best_obj the sizing objective f(B).  surv, order and
+ * sorted_surv describe the current conf.  Everything else is as in dspark_step, and
+ * dspark_step is this call with size_R = -1 and DSPARK_RULE_ARGMAX.  size_conf is
+ * read before the chain finishes; it must not alias an output.
+ */
+int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
+                      int R, int K, int V, int rank,
+                      const float* conf, const float* size_conf, int size_R, int rule,
+                      int n_sampling, int T, int num_reqs,
+                      const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                      int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                      int32_t* b_star, double* best_obj,
+                      int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                      uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Measurement hook.  When set (non-NULL hipEvent_t handles), every later

@@ -24,7 +24,19 @@ Readings of what the pages leave open (each one is also listed in the design doc):
   * a cost sum that is not a positive finite number makes that B's objective
     -inf and sets status bit 4;
   * the compacted verification list holds flat slot ids r*K+i, ordered by
-    request then position, padded with -1 to R*K entries.
+    request then position, padded with -1 to R*K entries;
+  * the first-drop admission rule (AlphaSignal's DSpark summary "How DSpark
+    Speeds Up LLM Inference", section "Verify smarter": slots are admitted in
+    rank order while throughput keeps rising, and admission stops as soon as it
+    would fall) admits slot B+1 only when f(B+1) > f(B) strictly, so it stops at
+    the smallest B of a plateau, as the argmax rule does;
+  * stale sizing (vLLM blog, "Scheduling the budget": B is sized from a
+    confidence array one step old while the slots are handed out with current
+    values; the DSpark summary's production notes speak of two steps): B is
+    chosen from the older array's survivals with the current step's scalars and
+    cost tables, then capped at the current slot count, and the current ranking's
+    first B slots are allocated.  best_obj is the sizing objective f(B) before
+    the cap.
 """
 from __future__ import annotations
 
@@ -36,6 +48,9 @@ import numpy as np
 STATUS_PREV_CLAMPED = 1
 STATUS_CONF_SANITIZED = 2
 STATUS_COST_INVALID = 4
+
+RULE_ARGMAX = 0       # B* = smallest B maximising f (vLLM blog, "Scheduling the budget")
+RULE_FIRST_DROP = 1   # admit while f rises (DSpark summary, "Verify smarter")
 
 
 def force_monotone(table):
@@ -108,10 +123,18 @@ def objective(sorted_surv, B, n_sampling, T, num_reqs, verify_cost, draft_cost):
     return num / den, False
 
 
-def choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost):
-    """Stage 4: B* = the smallest B in [0, Bmax] maximising f(B).
+def choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost, rule=RULE_ARGMAX):
+    """Stage 4: the budget B in [0, Bmax].
 
-    Returns (b_star, best_obj, obj [Bmax+1] float64, status)."""
+    RULE_ARGMAX: the smallest B maximising f(B) (vLLM blog, "Scheduling the budget").
+    RULE_FIRST_DROP: starting from B = 0, slots are admitted one at a time in rank
+    order while the objective strictly rises; B is where the next admission would
+    not raise it, or Bmax (DSpark summary "How DSpark Speeds Up LLM Inference",
+    section "Verify smarter").
+
+    Returns (b, f(b), obj [Bmax+1] float64, status)."""
+    if rule not in (RULE_ARGMAX, RULE_FIRST_DROP):
+        raise ValueError("unknown admission rule")
     n = len(sorted_surv)
     verify_len = len(verify_cost)
     if not (0 <= T < verify_len) or not (0 <= num_reqs < len(draft_cost)) or n_sampling < 0:
@@ -121,7 +144,6 @@ def choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost)
     obj = np.zeros(bmax + 1, dtype=np.float64)
     status = 0
     S = Fraction(0)
-    best_b, best_f = 0, None
     for B in range(bmax + 1):
         if B > 0:
             S += Fraction(float(sorted_surv[B - 1]))      # S is now the sum of the B best
@@ -133,9 +155,16 @@ def choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost)
             f = -math.inf
             status |= STATUS_COST_INVALID
         obj[B] = f
-        if best_f is None or f > best_f:
-            best_b, best_f = B, f
-    return best_b, best_f, obj, status
+    if rule == RULE_ARGMAX:
+        best_b = 0
+        for B in range(1, bmax + 1):
+            if obj[B] > obj[best_b]:
+                best_b = B
+    else:
+        best_b = 0
+        while best_b < bmax and obj[best_b + 1] > obj[best_b]:
+            best_b += 1
+    return best_b, float(obj[best_b]), obj, status
 
 
 def allocate(order, b_star, R, K, tokens=None):
@@ -170,14 +199,29 @@ def allocate(order, b_star, R, K, tokens=None):
     return prefix_len, offsets, ver_idx, ver_tokens
 
 
-def schedule(conf, n_sampling, T, num_reqs, verify_cost, draft_cost, tokens=None):
-    """Stages 2-5 in order.  Returns a dict of every intermediate and output."""
+def schedule(conf, n_sampling, T, num_reqs, verify_cost, draft_cost, tokens=None, size_conf=None,
+             rule=RULE_ARGMAX):
+    """Stages 2-5 in order.  Returns a dict of every intermediate and output.
+
+    size_conf (optional, [R', K]): the confidences B is sized from, e.g. those of one
+    or two steps earlier; the current conf is then used for the ranking and the
+    allocation only, and B is capped at R*K (vLLM blog, "Scheduling the budget")."""
     conf = np.asarray(conf, dtype=np.float32)
     R, K = conf.shape
     surv, st2 = survival(conf)
     order, sorted_surv, rank = topb_order(surv)
-    b_star, best_obj, obj, st4 = choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost)
+    st_size = 0
+    if size_conf is None:
+        b_star, best_obj, obj, st4 = choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost,
+                                                   rule)
+    else:
+        size_conf = np.asarray(size_conf, dtype=np.float32).reshape(-1, K)
+        size_surv, st_size = survival(size_conf)
+        _, size_sorted, _ = topb_order(size_surv)
+        b_size, best_obj, obj, st4 = choose_budget(size_sorted, n_sampling, T, num_reqs, verify_cost, draft_cost,
+                                                   rule)
+        b_star = min(b_size, R * K)
     prefix_len, offsets, ver_idx, ver_tokens = allocate(order, b_star, R, K, tokens)
     return dict(surv=surv, order=order, sorted_surv=sorted_surv, rank=rank, b_star=b_star,
                 best_obj=best_obj, obj=obj, prefix_len=prefix_len, offsets=offsets, ver_idx=ver_idx,
-                ver_tokens=ver_tokens, status=st2 | st4)
+                ver_tokens=ver_tokens, status=st2 | st4 | st_size)

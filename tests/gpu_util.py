@@ -145,3 +145,16 @@ def step_numpy(out: B.StepBuffers) -> dict:
                 best_obj=float(out.best_obj.item()), prefix_len=out.prefix_len.cpu().numpy(),
                 offsets=out.offsets.cpu().numpy(), ver_idx=out.ver_idx.cpu().numpy(),
                 ver_tokens=out.ver_tokens.cpu().numpy())
+
+
+def run_step_sized(ch: Chain, conf, size_conf, rule, n_sampling, T, num_reqs, vc, dc, out=None):
+    """dspark_step_sized on device buffers; size_conf None sizes from conf itself."""
+    out = out or B.StepBuffers(ch.R, ch.K)
+    conf_d = to_dev(np.asarray(conf, dtype=np.float32))
+    size_d = None if size_conf is None else to_dev(np.asarray(size_conf, dtype=np.float32).reshape(-1, ch.K))
+    vc_d, dc_d = to_dev(np.asarray(vc, dtype=np.float32)), to_dev(np.asarray(dc, dtype=np.float32))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.dspark_step_sized(ch.base, ch.A, ch.Bt, ch.dtype, ch.prev0, conf_d, size_d, rule, n_sampling, T, num_reqs,
+                        vc_d, dc_d, out, ch.ws, status)
+    torch.cuda.synchronize()
+    return step_numpy(out), int(status.item()), out

@@ -138,3 +138,61 @@ def test_topb_matches_python_sorted_on_fresh_draws():
         flat = surv.reshape(-1)
         want = sorted(range(R * K), key=lambda f: (-float(flat[f]), f))
         np.testing.assert_array_equal(order.cpu().numpy(), np.array(want, dtype=np.int32))
+
+
+def _budget_gpu(ss, n_sampling, T, num_reqs, vc, dc, rule):
+    n = len(ss)
+    bmax = min(n, len(vc) - 1 - T)
+    b_star = torch.empty(1, dtype=torch.int32, device=gu.DEV)
+    best = torch.empty(1, dtype=torch.float64, device=gu.DEV)
+    obj = torch.empty(bmax + 1, dtype=torch.float64, device=gu.DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=gu.DEV)
+    ss_d = gu.to_dev(np.asarray(ss, np.float32)) if n else torch.empty(0, dtype=torch.float32, device=gu.DEV)
+    B.dspark_choose_budget(ss_d, n_sampling, T, num_reqs, gu.to_dev(np.asarray(vc, np.float32)),
+                           gu.to_dev(np.asarray(dc, np.float32)), b_star, best, obj, status, rule=rule)
+    torch.cuda.synchronize()
+    return int(b_star.item()), float(best.item()), obj.cpu().numpy(), int(status.item())
+
+
+def _budget_cases():
+    """(label, sorted survivals, n_sampling, T, num_reqs, vc, dc) over the shapes the rules differ on."""
+    cases = []
+    for name in ("tiny", "small", "mid", "headline", "large", "sweep"):
+        w = inputs.WORKLOADS[name]
+        for seed in range(2):
+            rng = np.random.default_rng(300 + seed)
+            conf = inputs._confidences(w, rng)
+            ss = sched.topb_order(sched.survival(conf)[0])[1]
+            vc = sched.force_monotone(inputs.raw_verify_cost(w, rng))
+            dc = sched.force_monotone(inputs.raw_draft_cost(w))
+            cases.append((f"{name}/{seed}", ss, w.n_sampling, w.T, w.R_all, vc, dc))
+    rng = np.random.default_rng(8)
+    for n, slope in ((16384, 0.02), (5000, 1.0), (1023, 3.0), (1, 0.5), (0, 1.0)):
+        s = np.sort(rng.beta(3.0, 1.5, n).astype(np.float32))[::-1].copy()
+        vc = (1000.0 + slope * np.arange(n + 40)).astype(np.float32)
+        dc = np.full(8, 100.0, np.float32)
+        cases.append((f"linear/{n}", s, 64, 3, 5, vc, dc))
+    # plateaus: zero survivals under a flat cost; a staircase from the pages' cost model
+    s = np.concatenate([np.full(700, 0.5, np.float32), np.zeros(600, np.float32)])
+    cases.append(("plateau", s, 4, 0, 1, np.full(2000, 300.0, np.float32), np.full(4, 10.0, np.float32)))
+    stair = np.array([2000.0 + 1.0 * inputs.pad_to_graph(t, 4096) for t in range(1500)], np.float32)
+    cases.append(("stair", s, 4, 0, 1, stair, np.full(4, 10.0, np.float32)))
+    # every B's cost is the same, so f only rises until the zeros: also no room at all
+    cases.append(("no-room", s, 4, 1999, 1, np.full(2000, 300.0, np.float32), np.full(4, 10.0, np.float32)))
+    return cases
+
+
+@pytest.mark.parametrize("rule", [B.RULE_ARGMAX, B.RULE_FIRST_DROP])
+def test_budget_rules_match_the_oracle(rule):
+    differ = 0
+    for label, ss, ns, T, nr, vc, dc in _budget_cases():
+        gu.say(f"budget rule {rule}: {label} n={len(ss)}")
+        b, best, obj, st = _budget_gpu(ss, ns, T, nr, vc, dc, rule)
+        wb, wbest, wobj, wst = sched.choose_budget(ss, ns, T, nr, vc, dc, rule=rule)
+        assert b == wb, (label, b, wb)
+        assert best == wbest, (label, best, wbest)
+        np.testing.assert_array_equal(obj, wobj)
+        assert st == wst
+        differ += wb != sched.choose_budget(ss, ns, T, nr, vc, dc)[0]
+    if rule == B.RULE_FIRST_DROP:
+        assert differ >= 3

@@ -25,7 +25,8 @@ def _declared():
 def test_header_declares_the_documented_calls():
     names = _declared()
     for n in ("dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
-              "dspark_step", "dspark_force_monotone", "dspark_workspace_bytes", "dspark_markov_prepare"):
+              "dspark_step", "dspark_step_sized", "dspark_force_monotone", "dspark_workspace_bytes",
+              "dspark_markov_prepare"):
         assert n in names
 
 
@@ -100,24 +101,35 @@ def test_schedule_argument_checks_return_before_launch():
     L = binding.lib()
     p = _fake()
     # T outside [0, verify_len)
-    assert L.dspark_choose_budget(p, 10, 4, 65, 4, p, 65, p, 257, p, p, None, None, None) == -2
+    assert L.dspark_choose_budget(p, 10, 4, 65, 4, p, 65, p, 257, 0, p, p, None, None, None) == -2
     # num_reqs outside the draft table
-    assert L.dspark_choose_budget(p, 10, 4, 0, 257, p, 65, p, 257, p, p, None, None, None) == -2
+    assert L.dspark_choose_budget(p, 10, 4, 0, 257, p, 65, p, 257, 0, p, p, None, None, None) == -2
     # negative n_sampling
-    assert L.dspark_choose_budget(p, 10, -1, 0, 4, p, 65, p, 257, p, p, None, None, None) == -2
+    assert L.dspark_choose_budget(p, 10, -1, 0, 4, p, 65, p, 257, 0, p, p, None, None, None) == -2
     # too many slots
-    assert L.dspark_choose_budget(p, 16385, 4, 0, 4, p, 65, p, 257, p, p, None, None, None) == -3
+    assert L.dspark_choose_budget(p, 16385, 4, 0, 4, p, 65, p, 257, 0, p, p, None, None, None) == -3
     assert L.dspark_topb_select(p, 1025, 16, p, p, None, None) == -3
     assert L.dspark_allocate(p, p, 2000, 9, None, p, p, p, None, None) == -3
     # ver_tokens without tokens
     assert L.dspark_allocate(p, p, 4, 7, None, p, p, p, p, None) == -1
     # NULL tables
-    assert L.dspark_choose_budget(p, 10, 4, 0, 4, None, 65, p, 257, p, p, None, None, None) == -1
+    assert L.dspark_choose_budget(p, 10, 4, 0, 4, None, 65, p, 257, 0, p, p, None, None, None) == -1
     # the fused step checks both halves
     assert L.dspark_step(p, p, p, 1, p, 2048, 9, 1024, 256, p, 4, 0, 4, p, 65, p, 257,
                          p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
     assert L.dspark_step(p, p, p, 1, p, 4, 7, 1024, 256, p, 4, 70, 4, p, 65, p, 257,
                          p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -2
+    # unknown admission rule
+    assert L.dspark_choose_budget(p, 10, 4, 0, 4, p, 65, p, 257, 2, p, p, None, None, None) == -1
+    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, None, -1, 7, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
+    # sizing array: rows below -1, NULL with rows, too many slots
+    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, -2, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, None, 3, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, 2341, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
     # empty survival / top-B calls are valid no-ops
     assert L.dspark_survival(p, 0, 7, p, None, None) == 0
     assert L.dspark_topb_select(p, 0, 7, p, p, None, None) == 0

@@ -215,22 +215,144 @@ def test_cost_jump_right_after_T_gives_zero_budget():
 
 
 def test_linear_cost_argmax_equals_greedy_first_drop():
-    # For cost a + b t the ratio is quasi-concave in B, so the global argmax and the
-    # "admit one at a time while throughput rises" rule agree.
+    # For cost a + b t the ratio is quasi-concave in B (a concave numerator over a positive
+    # affine denominator), so the global argmax and the "admit one at a time while
+    # throughput rises" rule agree.
     for seed in range(5):
         rng = np.random.default_rng(100 + seed)
         w = inputs.WORKLOADS["headline"]
         conf = inputs._confidences(w, rng)
         surv, _ = sched.survival(conf)
         _, sorted_surv, _ = sched.topb_order(surv)
-        slope = [0.5, 2.0, 5.0, 20.0, 60.0][seed]
+        slope = [0.1, 0.5, 2.0, 5.0, 9.0][seed]
         vc = np.array([3000.0 + slope * t for t in range(2000)], dtype=np.float32)
         dc = (300.0 + 2.0 * np.arange(300)).astype(np.float32)
-        b_star, _, obj, _ = sched.choose_budget(sorted_surv, 256, 0, 256, vc, dc)
-        B = 0
-        while B + 1 < len(obj) and obj[B + 1] > obj[B]:
-            B += 1
-        assert B == b_star, seed
+        b_star, best, _, _ = sched.choose_budget(sorted_surv, 256, 0, 256, vc, dc)
+        b_fd, best_fd, _, _ = sched.choose_budget(sorted_surv, 256, 0, 256, vc, dc, rule=sched.RULE_FIRST_DROP)
+        assert b_fd == b_star and best_fd == best, seed
+        assert 0 < b_star < 1792
+
+
+def test_first_drop_worked_staircase():
+    g = _golden("first_drop_staircase.json")
+    surv, _ = sched.survival(np.array(g["conf"], dtype=np.float32))
+    _, ss, _ = sched.topb_order(surv)
+    args = (g["n_sampling"], g["T"], g["num_reqs"], np.array(g["verify_cost"], dtype=np.float32),
+            np.array(g["draft_cost"], dtype=np.float32))
+    b_am, f_am, obj, _ = sched.choose_budget(ss, *args)
+    b_fd, f_fd, obj_fd, _ = sched.choose_budget(ss, *args, rule=sched.RULE_FIRST_DROP)
+    assert [float(Fraction(a, b)) for a, b in g["objective_exact"]] == obj.tolist() == obj_fd.tolist()
+    assert (b_am, b_fd) == (g["b_argmax"], g["b_first_drop"])
+    assert f_am == obj[b_am] and f_fd == obj[b_fd]
+
+
+def test_first_drop_against_exact_objective():
+    # The first-drop B from exact rationals: the first B whose successor is not larger.
+    # Staircase cost tables of the workloads (the case where the rules differ).
+    checked = 0
+    for name in ("tiny", "small", "mid"):
+        w = inputs.WORKLOADS[name]
+        for seed in range(3):
+            rng = np.random.default_rng(1000 * seed + 17)
+            conf = inputs._confidences(w, rng)
+            surv, _ = sched.survival(conf)
+            _, ss, _ = sched.topb_order(surv)
+            vc = sched.force_monotone(inputs.raw_verify_cost(w, rng))
+            dc = sched.force_monotone(inputs.raw_draft_cost(w))
+            b_fd, f_fd, _, _ = sched.choose_budget(ss, w.n_sampling, w.T, w.R_all, vc, dc,
+                                                   rule=sched.RULE_FIRST_DROP)
+            b_am, f_am, _, _ = sched.choose_budget(ss, w.n_sampling, w.T, w.R_all, vc, dc)
+            bmax = min(len(ss), len(vc) - 1 - w.T)
+            den_d = Fraction(float(dc[w.R_all]))
+            S, fx = Fraction(w.n_sampling), []
+            for B in range(bmax + 1):
+                if B:
+                    S += Fraction(float(ss[B - 1]))
+                fx.append(S / (Fraction(float(vc[w.T + B])) + den_d))
+            B = 0
+            while B < bmax and fx[B + 1] > fx[B]:
+                B += 1
+            assert b_fd == B, (name, seed)
+            assert f_fd == float(fx[B]) or abs(f_fd - float(fx[B])) <= 1e-15 * abs(float(fx[B]))
+            # the rule stops at the first local maximum, never past the global one
+            assert b_fd <= b_am and f_fd <= f_am
+            checked += b_fd != b_am
+    assert checked >= 3   # the staircase makes the two rules differ
+
+
+def test_first_drop_stops_at_a_plateau():
+    # Flat cost: f rises with every positive survival, then stays flat over zero-survival
+    # slots.  "While throughput keeps rising" stops at the first flat step, where the
+    # argmax's smallest maximiser is as well.
+    rng = np.random.default_rng(5)
+    conf = rng.uniform(0.5, 1.0, size=(6, 5)).astype(np.float32)
+    conf[1, 2] = 0.0
+    conf[4, 0] = 0.0
+    surv, _ = sched.survival(conf)
+    _, ss, _ = sched.topb_order(surv)
+    vc, dc = _tables([1000.0] * 64)
+    b_fd, _, _, _ = sched.choose_budget(ss, 6, 0, 6, vc, dc, rule=sched.RULE_FIRST_DROP)
+    assert b_fd == int(np.count_nonzero(surv)) == 22
+    # and runs to Bmax when f never stops rising
+    b_fd, _, obj, _ = sched.choose_budget(ss[:20], 6, 0, 6, vc, dc, rule=sched.RULE_FIRST_DROP)
+    assert b_fd == 20 == len(obj) - 1
+    with pytest.raises(ValueError):
+        sched.choose_budget(ss, 6, 0, 6, vc, dc, rule=7)
+
+
+# ---------------------------------------------------------------- stale sizing
+
+def _mid_tables(w, seed=7):
+    vc = sched.force_monotone(inputs.raw_verify_cost(w, np.random.default_rng(seed)))
+    dc = sched.force_monotone(inputs.raw_draft_cost(w))
+    return vc, dc
+
+
+def test_sizing_from_the_current_array_is_the_fused_schedule():
+    w = inputs.WORKLOADS["small"]
+    conf = inputs._confidences(w, np.random.default_rng(3))
+    vc, dc = _mid_tables(w)
+    for rule in (sched.RULE_ARGMAX, sched.RULE_FIRST_DROP):
+        a = sched.schedule(conf, w.n_sampling, w.T, w.R_all, vc, dc, rule=rule)
+        b = sched.schedule(conf, w.n_sampling, w.T, w.R_all, vc, dc, size_conf=conf.copy(), rule=rule)
+        for k in ("b_star", "best_obj", "prefix_len", "offsets", "ver_idx", "order"):
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), (rule, k)
+
+
+def test_stale_sizing_takes_B_from_the_old_array_and_slots_from_the_current_one():
+    # vLLM blog, "Scheduling the budget": the size comes from the one-step-old buffer, the
+    # allocation from current values.  B must not move when only the current array changes,
+    # and the allocated slots must be the current ranking's best B.
+    w = inputs.WORKLOADS["small"]
+    rng = np.random.default_rng(9)
+    old = inputs._confidences(w, rng)
+    vc = np.array([1500.0 + 4.0 * t for t in range(w.verify_len)], dtype=np.float32)  # B moves with conf
+    dc = (300.0 + 2.0 * np.arange(w.R_all + 1)).astype(np.float32)
+    b_old, f_old, _, _ = sched.choose_budget(sched.topb_order(sched.survival(old)[0])[1], w.n_sampling, w.T,
+                                             w.R_all, vc, dc)
+    bs = set()
+    for k in range(4):
+        cur = inputs._confidences(w, np.random.default_rng(50 + k))
+        out = sched.schedule(cur, w.n_sampling, w.T, w.R_all, vc, dc, size_conf=old)
+        assert out["b_star"] == b_old and out["best_obj"] == f_old
+        sel = out["ver_idx"][:b_old]
+        assert set(sel.tolist()) == set(out["order"][:b_old].tolist())
+        same = sched.schedule(cur, w.n_sampling, w.T, w.R_all, vc, dc)
+        bs.add(same["b_star"])
+    assert len(bs | {b_old}) > 1     # the same-step size differs on these draws
+
+
+def test_stale_size_is_capped_at_the_current_slots():
+    old = np.full((8, 4), 0.99, dtype=np.float32)     # 32 confident slots
+    cur = np.full((3, 4), 0.5, dtype=np.float32)      # the batch shrank to 12 slots
+    vc, dc = _tables([100.0] * 64)
+    out = sched.schedule(cur, 3, 0, 3, vc, dc, size_conf=old)
+    assert out["b_star"] == 12 and out["prefix_len"].tolist() == [4, 4, 4]
+    b_old, f_old, _, _ = sched.choose_budget(sched.topb_order(sched.survival(old)[0])[1], 3, 0, 3, vc, dc)
+    assert b_old == 32 and out["best_obj"] == f_old
+    # an empty sizing array sizes B = 0
+    out = sched.schedule(cur, 3, 0, 3, vc, dc, size_conf=np.zeros((0, 4), dtype=np.float32))
+    assert out["b_star"] == 0 and out["ver_idx"].tolist() == [-1] * 12
 
 
 def test_objective_is_exact_rational_rounded_once():
