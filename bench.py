@@ -98,6 +98,74 @@ def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
                       f"timed {t_sched:.2f} s; single-threaded"}
 
 
+def _event_loop_us(fn, n: int) -> float:
+    """Mean microseconds per call of fn(k), k < n, from one event pair around the loop."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(n):
+        fn(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def accept_lane(w, B, inputs, out, st, dev, calls: int = 200) -> dict:
+    """The greedy acceptance lane on the last step's allocation, with a synthetic target
+    whose acceptance is drawn from that step's confidences; timed and checked."""
+    import torch
+    from oracle import verify
+    ver = out.ver_tokens.cpu().numpy()
+    offsets = out.offsets.cpu().numpy()
+    target = inputs.synthetic_target(ver, offsets, st["conf"], w.V, seed=12345)
+    tgt = torch.from_numpy(target).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    a, p, o = torch.empty(w.R, **i32), torch.empty(w.R, **i32), torch.empty((w.R, w.K + 1), **i32)
+    stat = torch.zeros(1, **i32)
+
+    def run(_k):
+        B.dspark_accept_greedy(out.ver_tokens, out.offsets, tgt, w.R, w.K, a, p, o, stat)
+
+    for k in range(5):
+        run(k)
+    us = _event_loop_us(run, calls)
+    wa, wp, wo, _ = verify.accept_greedy(ver, offsets, target, w.R, w.K)
+    ok = (np.array_equal(a.cpu().numpy(), wa) and np.array_equal(p.cpu().numpy(), wp)
+          and np.array_equal(o.cpu().numpy(), wo) and int(stat.item()) == 0)
+    log(f"bench: acceptance lane {us:.2f} us/call, parity {'ok' if ok else 'MISMATCH'}")
+    return {"us_per_call": round(us, 2), "calls": calls, "accepted_per_step": int(wa.sum()),
+            "emitted_per_step": int(wa.sum()) + w.R, "verified_per_step": int(offsets[-1]),
+            "parity": "ok" if ok else "MISMATCH"}
+
+
+def stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule, steps) -> dict:
+    """dspark_step_sized with B sized from the previous pool entry's confidences (a
+    one-step-old buffer) under `rule`; timed over `steps` steps and checked on the last."""
+    P = len(pool)
+
+    def run(k):
+        base, prev0, conf = pool[k % P]
+        old = pool[(k - 1) % P][2]
+        B.dspark_step_sized(base, A, Bt, w.dtype, prev0, conf, old, rule, w.n_sampling, w.T, w.R_all, vc_d, dc_d,
+                            out, ws, status)
+
+    for k in range(10):
+        run(k)
+    us = _event_loop_us(run, steps)
+    k = steps - 1
+    want = osched.schedule(host_steps[k % P]["conf"], w.n_sampling, w.T, w.R_all, vc, dc,
+                           size_conf=host_steps[(k - 1) % P]["conf"], rule=rule)
+    same = osched.schedule(host_steps[k % P]["conf"], w.n_sampling, w.T, w.R_all, vc, dc, rule=rule)
+    ok = (int(out.b_star.item()) == want["b_star"] and float(out.best_obj.item()) == want["best_obj"]
+          and np.array_equal(out.ver_idx.cpu().numpy(), want["ver_idx"]))
+    log(f"bench: stale sizing rule {rule}: {us:.1f} us/step, B {want['b_star']} (same-step {same['b_star']}), "
+        f"parity {'ok' if ok else 'MISMATCH'}")
+    return {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1), "steps": steps,
+            "b_last": int(want["b_star"]), "b_same_step": int(same["b_star"]), "parity": "ok" if ok else "MISMATCH"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +306,11 @@ def main():
     parity = "ok" if ok else "MISMATCH"
     log(f"bench: parity of the last step: {parity}")
 
+    extra = {"accept_greedy": accept_lane(w, B, inputs, out, st, dev)}
+    for label, rule in (("stale_sizing_argmax", B.RULE_ARGMAX), ("stale_sizing_first_drop", B.RULE_FIRST_DROP)):
+        extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule,
+                                   min(args.event_steps, K))
+
     sb = step_bytes(w)
     ck = chain_kernel(w)
     launch_s = chain_ms.mean() * 1e-3 / ck["launches_per_step"]   # event-timed chain phase per launch
@@ -270,6 +343,7 @@ def main():
                        "chain_us": round(float(chain_ms.mean()) * 1e3, 2)},
         "parity_last_step": parity,
         "status": int(status.item()),
+        "variants": extra,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")

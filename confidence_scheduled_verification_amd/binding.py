@@ -23,13 +23,15 @@ STATUS_PREV_CLAMPED = 1
 STATUS_CONF_SANITIZED = 2
 STATUS_COST_INVALID = 4
 STATUS_SYNC_TIMEOUT = 8
+STATUS_BAD_ALLOCATION = 16
 MAX_SLOTS = 16384
 RULE_ARGMAX = 0
 RULE_FIRST_DROP = 1
 
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
            "dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
-           "dspark_step", "dspark_step_sized", "dspark_set_timing_events", "dspark_force_monotone"]
+           "dspark_step", "dspark_step_sized", "dspark_accept_greedy", "dspark_set_timing_events",
+           "dspark_force_monotone"]
 
 
 class DSparkError(RuntimeError):
@@ -66,6 +68,7 @@ def lib():
                                   p, p, p, sz, p]
         L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, i, i, p, i, p, i, p, p, p, p,
                                         p, p, p, p, p, p, p, p, sz, p]
+        L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
         L.dspark_set_timing_events.argtypes = [p, p]
         L.dspark_force_monotone.argtypes = [p, i]
         for name in EXPORTS:
@@ -213,6 +216,18 @@ def dspark_step_sized(base, A, Bt, dtype: int, prev0, conf, size_conf, rule: int
                                    _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
                                    _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
                                    _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_accept_greedy(ver_tokens, offsets, target, R: int, K: int, accept_len, next_prev0, out_tokens=None,
+                         status=None, stream=None):
+    """Greedy verification: accepted run, bonus token and next prev0 per request."""
+    _contig(ver_tokens, offsets, target, accept_len, next_prev0, out_tokens)
+    if offsets.numel() != R + 1 or accept_len.numel() != R or next_prev0.numel() != R \
+            or target.numel() < R * K + R or (ver_tokens is not None and ver_tokens.numel() < R * K) \
+            or (out_tokens is not None and out_tokens.numel() != R * (K + 1)):
+        raise ValueError("dspark_accept_greedy: inconsistent sizes")
+    _check(lib().dspark_accept_greedy(_p(ver_tokens), _p(offsets), _p(target), R, K, _p(accept_len),
+                                      _p(next_prev0), _p(out_tokens), _p(status), _stream(stream)))
 
 
 def dspark_set_timing_events(before_chain=None, after_chain=None):

@@ -262,6 +262,19 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
                              ws, ws_bytes, stream);
 }
 
+int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R, int K,
+                         int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens, uint32_t* status,
+                         void* stream) {
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "accept_greedy: negative R (%d) or K (%d)", R, K);
+    if (R == 0) return DSPARK_OK;
+    if (!offsets || !target || !accept_len || !next_prev0 || (K > 0 && !ver_tokens))
+        return fail(DSPARK_EINVAL, "accept_greedy: a required pointer is NULL");
+    if ((long long)R * K + R > (long long)INT32_MAX) return fail(DSPARK_ERANGE, "accept_greedy: R*K + R overflows int32");
+    const hipError_t e = dspark::launch_accept_greedy(ver_tokens, offsets, target, R, K, accept_len, next_prev0,
+                                                      out_tokens, status, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "accept_greedy");
+}
+
 int dspark_set_timing_events(void* before_chain, void* after_chain) {
     g_ev_before_chain = (hipEvent_t)before_chain;
     g_ev_after_chain = (hipEvent_t)after_chain;

@@ -13,6 +13,7 @@ constexpr uint32_t kStatusPrevClamped = 1u;
 constexpr uint32_t kStatusConfSanitized = 2u;
 constexpr uint32_t kStatusCostInvalid = 4u;
 constexpr uint32_t kStatusSyncTimeout = 8u;
+constexpr uint32_t kStatusBadAllocation = 16u;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

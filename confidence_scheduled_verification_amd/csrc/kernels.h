@@ -136,5 +136,8 @@ hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, i
                            int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
                            hipStream_t s);
 hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s);
+hipError_t launch_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R,
+                                int K, int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens,
+                                uint32_t* status, hipStream_t s);
 
 }  // namespace dspark

@@ -217,3 +217,31 @@ def random_case(seed: int, R: int, K: int, V: int, rank: int, dtype: int, base_s
     prev0 = rng.integers(0, V, size=R, dtype=np.int32)
     conf = _confidences(w, rng)
     return dict(base=base, A=A, Bmat=Bmat, prev0=prev0, conf=conf)
+
+
+def synthetic_target(ver_tokens, offsets, conf, V: int, seed: int) -> np.ndarray:
+    """Stand-in for the target model's greedy tokens over one step's verified drafts.
+
+    For request r with verified drafts d_0..d_{L-1} (ver_tokens[offsets[r]:offsets[r+1]])
+    the target's token at entry j < L equals d_j with probability conf[r, j] and is some
+    other token otherwise; entry L is a uniform token.  Entries sit at offsets[r] + r + j
+    (1 + L per request) in a buffer of R*K + R tokens (unused entries 0).  Acceptance is
+    thereby drawn from the confidences: the chance that drafts 0..i all match is the
+    product of conf[r, 0..i].  All draws are made up front, so the stream does not depend
+    on the allocation."""
+    ver_tokens = np.asarray(ver_tokens).reshape(-1)
+    offsets = np.asarray(offsets).reshape(-1)
+    conf = np.asarray(conf, dtype=np.float64)
+    R, K = conf.shape
+    rng = np.random.default_rng(seed)
+    u = rng.random((R, K))
+    other = rng.integers(1, max(V, 2), size=(R, K))
+    bonus = rng.integers(0, V, size=R)
+    target = np.zeros(R * K + R, dtype=np.int32)
+    for r in range(R):
+        o, L = int(offsets[r]), int(offsets[r + 1] - offsets[r])
+        for j in range(L):
+            d = int(ver_tokens[o + j])
+            target[o + r + j] = d if u[r, j] < conf[r, j] else (d + int(other[r, j])) % V
+        target[o + r + L] = bonus[r]
+    return target

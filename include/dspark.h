@@ -68,6 +68,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
                                            number for some B; that B's objective is -inf                    */
 #define DSPARK_STATUS_SYNC_TIMEOUT 8u   /* the single-launch chain waited too long at a grid barrier (its
                                            workgroups were not all resident); tokens are then unreliable    */
+#define DSPARK_STATUS_BAD_ALLOCATION 16u /* dspark_accept_greedy met an inconsistent offsets row; that request
+                                           accepted nothing and its next prev0 is -1                        */
 
 /* Admission rules of stage 4. */
 #define DSPARK_RULE_ARGMAX 0      /* the smallest B with the largest f(B) (vLLM blog, "Scheduling the budget")  */
@@ -252,6 +254,37 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
                       int32_t* b_star, double* best_obj,
                       int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
                       uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Greedy verification of one step's allocated drafts (MAX worklog "DSpark on MAX",
+ * section "The kernel pass", item 2: under greedy decoding a draft is accepted
+ * exactly when it equals the target's best token; DSpark summary "How DSpark Speeds
+ * Up LLM Inference", section "Context": the verifier keeps the longest matching
+ * run; vLLM blog "Adaptive Verification in vLLM", section "Scheduling the budget":
+ * each request also gains one bonus token).  For every request r, with
+ * o = offsets[r] and L = offsets[r+1] - o:
+ *   accept_len[r] = the number of leading j < L with ver_tokens[o+j] == target[o+r+j]
+ *   next_prev0[r] = target[o + r + accept_len[r]]      (the bonus token)
+ *   out_tokens[r] = ver_tokens[o .. o+accept_len[r]), then the bonus token, then -1
+ *
+ *   ver_tokens  [R*K]     int32 verified draft tokens by request then position (the
+ *                         ver_tokens output of dspark_step); may be NULL when K == 0
+ *   offsets     [R+1]     int32 exclusive running sum of the prefix lengths (dspark_step)
+ *   target      [R*K + R] int32 the target model's greedy tokens: request r's 1 + L
+ *                         entries start at o + r (the last accepted token and the L
+ *                         drafts run through the target together; vLLM blog, section
+ *                         "Varlen decode CUDA graphs"), entry j being its choice after
+ *                         the request's first j drafts
+ *   accept_len  [R]       int32 output
+ *   next_prev0  [R]       int32 output: the token the next step's chain is keyed on
+ *   out_tokens  [R, K+1]  int32 output: the tokens this step emits per request, or NULL
+ * A row with o < 0, L < 0, L > K or o + L > R*K accepts nothing, gets next_prev0 = -1
+ * and an all -1 out_tokens row, and sets DSPARK_STATUS_BAD_ALLOCATION.  R == 0
+ * enqueues nothing.  Limit: R*K + R <= INT32_MAX.
+ */
+int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R, int K,
+                         int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens, uint32_t* status,
+                         void* stream);
 
 /*
  * Measurement hook.  When set (non-NULL hipEvent_t handles), every later

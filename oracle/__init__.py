@@ -7,7 +7,9 @@ does, and shares no code with it.
 
   * ``chain``          -- stage 1 in plain C, double precision (``chain.c``);
   * ``oracle.sched``   -- stages 2-5 and the cost-table forcing in Python with
-                          exact rational arithmetic where the method sums.
+                          exact rational arithmetic where the method sums;
+  * ``oracle.verify``  -- greedy verification of the allocated drafts (accepted
+                          run, bonus token, the next step's prev0).
 """
 from __future__ import annotations
 

@@ -130,6 +130,10 @@ def test_schedule_argument_checks_return_before_launch():
                                p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
     assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, 2341, 0, 4, 0, 4, p, 65, p, 257,
                                p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
+    # acceptance lane: negative sizes, missing target, empty batch
+    assert L.dspark_accept_greedy(p, p, p, -1, 7, p, p, None, None, None) == -1
+    assert L.dspark_accept_greedy(p, p, None, 4, 7, p, p, None, None, None) == -1
+    assert L.dspark_accept_greedy(None, None, None, 0, 7, None, None, None, None, None) == 0
     # empty survival / top-B calls are valid no-ops
     assert L.dspark_survival(p, 0, 7, p, None, None) == 0
     assert L.dspark_topb_select(p, 0, 7, p, p, None, None) == 0
