@@ -166,6 +166,38 @@ def stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, 
             "b_last": int(want["b_star"]), "b_same_step": int(same["b_star"]), "parity": "ok" if ok else "MISMATCH"}
 
 
+def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev) -> dict:
+    """Cost tables measured on this GPU at start-up: a proxy verification step (4 bf16
+    GEMMs [t, 7168] x [7168, 7168]) over the captured sizes up to the workload's capture
+    limit plus 1.5x and 2x above it, and a proxy drafting step (one GEMM over the K
+    draft tokens of each request) by request count; median of 5 runs each; then one step
+    sized with them, checked against the oracle on the same tables."""
+    import torch
+    from confidence_scheduled_verification_amd import costmodel
+    t0 = time.perf_counter()
+    vproxy = costmodel.GemmProxy(max_tokens=2 * w.graph_max, hidden=7168, layers=4, device=dev)
+    vc, vshapes, vs = costmodel.measure_table(vproxy, w.graph_max, w.verify_len)
+    del vproxy
+    dproxy = costmodel.GemmProxy(max_tokens=2 * (w.draft_len - 1) * w.K, hidden=7168, layers=1, device=dev, seed=1)
+    dc, dshapes, ds = costmodel.measure_table(lambda n: dproxy(n * w.K), w.draft_len - 1, w.draft_len)
+    del dproxy
+    torch.cuda.empty_cache()
+    build_s = time.perf_counter() - t0
+    base, prev0, conf = pool[0]
+    vc_d, dc_d = torch.from_numpy(vc).to(dev), torch.from_numpy(dc).to(dev)
+    B.dspark_step(base, A, Bt, w.dtype, prev0, conf, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
+    torch.cuda.synchronize()
+    want = osched.schedule(host_steps[0]["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
+    ok = (int(out.b_star.item()) == want["b_star"] and float(out.best_obj.item()) == want["best_obj"]
+          and np.array_equal(out.ver_idx.cpu().numpy(), want["ver_idx"]))
+    log(f"bench: measured tables in {build_s:.1f} s; B = {want['b_star']} with them, parity {'ok' if ok else 'MISMATCH'}")
+    med = lambda x: [round(float(np.median(r)), 1) for r in x]
+    return {"verify_shapes": vshapes, "verify_median_us": med(vs), "draft_shapes": dshapes,
+            "draft_median_us": med(ds), "proxy": "4 x bf16 GEMM [t,7168]x[7168,7168] (verify); 1 x GEMM over "
+            f"{w.K} tokens per request (draft)", "build_s": round(build_s, 2), "b_star": int(want["b_star"]),
+            "best_obj": want["best_obj"], "parity": "ok" if ok else "MISMATCH"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +342,8 @@ def main():
     for label, rule in (("stale_sizing_argmax", B.RULE_ARGMAX), ("stale_sizing_first_drop", B.RULE_FIRST_DROP)):
         extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule,
                                    min(args.event_steps, K))
+
+    extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
 
     sb = step_bytes(w)
     ck = chain_kernel(w)

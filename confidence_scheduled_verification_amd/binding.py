@@ -31,7 +31,10 @@ RULE_FIRST_DROP = 1
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
            "dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
            "dspark_step", "dspark_step_sized", "dspark_accept_greedy", "dspark_set_timing_events",
-           "dspark_force_monotone"]
+           "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table"]
+
+# int fn(int shape, void* user, void* stream)
+SHAPE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p)
 
 
 class DSparkError(RuntimeError):
@@ -71,6 +74,8 @@ def lib():
         L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
         L.dspark_set_timing_events.argtypes = [p, p]
         L.dspark_force_monotone.argtypes = [p, i]
+        L.dspark_profile_shapes.argtypes = [SHAPE_FN, p, p, i, i, i, p, p]
+        L.dspark_build_cost_table.argtypes = [p, i, p, i, i, p, i]
         for name in EXPORTS:
             if name not in ("dspark_last_error", "dspark_version", "dspark_workspace_bytes"):
                 getattr(L, name).restype = ctypes.c_int
@@ -242,6 +247,43 @@ def dspark_force_monotone(table: np.ndarray) -> np.ndarray:
     t = np.ascontiguousarray(table, dtype=np.float32).copy()
     _check(lib().dspark_force_monotone(t.ctypes.data_as(ctypes.c_void_p), int(t.size)))
     return t
+
+
+def dspark_profile_shapes(step, shapes, runs: int = 5, warmup: int = 2, stream=None) -> np.ndarray:
+    """Times `step(shape)` (which enqueues one step of that size on the current stream)
+    over `shapes`; returns microseconds [len(shapes), runs].  Synchronises."""
+    sh = np.ascontiguousarray(shapes, dtype=np.int32)
+    out = np.zeros((len(sh), runs), dtype=np.float32)
+    failure = []
+
+    def cb(shape, _user, _stream):
+        try:
+            step(int(shape))
+            return 0
+        except Exception as exc:        # reported through the library's error path
+            failure.append(exc)
+            return 1
+
+    fn = SHAPE_FN(cb)
+    rc = lib().dspark_profile_shapes(fn, None, sh.ctypes.data_as(ctypes.c_void_p), len(sh), runs, warmup,
+                                     out.ctypes.data_as(ctypes.c_void_p), _stream(stream))
+    if failure:
+        raise failure[0]
+    _check(rc)
+    return out
+
+
+def dspark_build_cost_table(shapes, samples_us, graph_max: int, table_len: int) -> np.ndarray:
+    """Host-side cost table from profiled runs (median, staircase, continuous tail, forced)."""
+    sh = np.ascontiguousarray(shapes, dtype=np.int32)
+    smp = np.ascontiguousarray(samples_us, dtype=np.float32)
+    if smp.ndim != 2 or smp.shape[0] != len(sh):
+        raise ValueError("dspark_build_cost_table: samples must be [len(shapes), runs]")
+    table = np.zeros(table_len, dtype=np.float32)
+    _check(lib().dspark_build_cost_table(sh.ctypes.data_as(ctypes.c_void_p), len(sh),
+                                         smp.ctypes.data_as(ctypes.c_void_p), smp.shape[1], graph_max,
+                                         table.ctypes.data_as(ctypes.c_void_p), table_len))
+    return table
 
 
 class StepBuffers:

@@ -6,6 +6,9 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "dspark.h"
 #include "kernels.h"
 
@@ -278,6 +281,86 @@ int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, cons
 int dspark_set_timing_events(void* before_chain, void* after_chain) {
     g_ev_before_chain = (hipEvent_t)before_chain;
     g_ev_after_chain = (hipEvent_t)after_chain;
+    return DSPARK_OK;
+}
+
+int dspark_profile_shapes(dspark_shape_fn fn, void* user, const int32_t* shapes, int n_shapes, int runs, int warmup,
+                          float* samples_us, void* stream) {
+    if (!fn || !shapes || !samples_us) return fail(DSPARK_EINVAL, "profile_shapes: NULL argument");
+    if (n_shapes < 1 || runs < 1 || warmup < 0)
+        return fail(DSPARK_EINVAL, "profile_shapes: n_shapes %d and runs %d must be >= 1, warmup %d >= 0", n_shapes,
+                    runs, warmup);
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    int rc = DSPARK_OK;
+    for (int i = 0; i < n_shapes && rc == DSPARK_OK && e == hipSuccess; ++i) {
+        for (int k = 0; k < warmup + runs && rc == DSPARK_OK; ++k) {
+            const bool timed = k >= warmup;
+            if (timed && (e = hipEventRecord(e0, s)) != hipSuccess) break;
+            const int cb = fn(shapes[i], user, stream);
+            if (cb != 0) {
+                rc = fail(DSPARK_EINVAL, "profile_shapes: the step callback returned %d for shape %d", cb, shapes[i]);
+                break;
+            }
+            if (!timed) continue;
+            float ms = 0.f;
+            if ((e = hipEventRecord(e1, s)) != hipSuccess || (e = hipEventSynchronize(e1)) != hipSuccess ||
+                (e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess)
+                break;
+            samples_us[(size_t)i * runs + (k - warmup)] = ms * 1000.f;
+        }
+    }
+    if (e != hipSuccess && rc == DSPARK_OK) rc = hip_fail(e, "profile_shapes");
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    return rc;
+}
+
+int dspark_build_cost_table(const int32_t* shapes, int n_shapes, const float* samples_us, int runs, int graph_max,
+                            float* table, int table_len) {
+    if (!shapes || !samples_us || (table_len > 0 && !table)) return fail(DSPARK_EINVAL, "build_cost_table: NULL argument");
+    if (n_shapes < 1 || runs < 1 || table_len < 0 || graph_max < 1)
+        return fail(DSPARK_EINVAL, "build_cost_table: need n_shapes >= 1, runs >= 1, table_len >= 0, graph_max >= 1");
+    for (int i = 0; i < n_shapes; ++i)
+        if (shapes[i] < 1 || (i > 0 && shapes[i] <= shapes[i - 1]))
+            return fail(DSPARK_EINVAL, "build_cost_table: shapes must be positive and strictly increasing");
+    // Median of each shape's runs.
+    std::vector<double> med(n_shapes), runs_of(runs);
+    for (int i = 0; i < n_shapes; ++i) {
+        for (int k = 0; k < runs; ++k) {
+            runs_of[k] = (double)samples_us[(size_t)i * runs + k];
+            if (!isfinite(runs_of[k]))
+                return fail(DSPARK_EINVAL, "build_cost_table: shape %d has a non-finite run", shapes[i]);
+        }
+        std::sort(runs_of.begin(), runs_of.end());
+        med[i] = (runs % 2) ? runs_of[runs / 2] : (runs_of[runs / 2 - 1] + runs_of[runs / 2]) / 2.0;
+    }
+    int n_cap = 0;  // shapes[0, n_cap) are captured graph sizes
+    while (n_cap < n_shapes && shapes[n_cap] <= graph_max) ++n_cap;
+    if (n_cap == 0 || shapes[n_cap - 1] != graph_max)
+        return fail(DSPARK_EINVAL, "build_cost_table: the captured shapes must include graph_max %d", graph_max);
+    const int n_eager = n_shapes - n_cap;
+    if (table_len - 1 > graph_max && n_eager == 0)
+        return fail(DSPARK_EINVAL, "build_cost_table: entries above graph_max need a measured shape above it");
+    std::vector<float> out(table_len);
+    int g = 0;  // smallest captured shape >= max(t, 1)
+    for (int t = 0; t < table_len && t <= graph_max; ++t) {
+        while (shapes[g] < std::max(t, 1)) ++g;
+        out[t] = (float)med[g];
+    }
+    int a = n_cap;  // segment [a, a+1] of the measured shapes above graph_max
+    for (int t = graph_max + 1; t < table_len; ++t) {
+        if (n_eager == 1) {
+            out[t] = (float)med[n_cap];
+            continue;
+        }
+        while (a + 2 < n_shapes && shapes[a + 1] <= t) ++a;
+        const double sa = shapes[a], sb = shapes[a + 1], ca = med[a], cb = med[a + 1];
+        out[t] = (float)(ca + ((cb - ca) * ((double)t - sa)) / (sb - sa));
+    }
+    for (int t = 0; t < table_len; ++t) table[t] = (t > 0 && out[t] < table[t - 1]) ? table[t - 1] : out[t];
     return DSPARK_OK;
 }
 

@@ -305,6 +305,48 @@ int dspark_set_timing_events(void* before_chain, void* after_chain);
  */
 int dspark_force_monotone(float* table, int len);
 
+/*
+ * Start-up profiling of a step's cost over a set of shapes (vLLM blog "Adaptive
+ * Verification in vLLM", section "The cost model": the engine times dummy steps over
+ * the captured graph sizes plus a couple of sizes above the largest, five runs per
+ * shape).  For every shape, `warmup` untimed calls and then `runs` timed calls of
+ *   fn(shape, user, stream)
+ * which must enqueue one step of that size on `stream` and return 0 (anything else
+ * aborts with DSPARK_EINVAL).  Each timed call is bracketed by HIP events on `stream`
+ * and waited for, so unlike the per-step calls above THIS CALL SYNCHRONISES (it is a
+ * start-up routine).
+ *   shapes      [n_shapes] (host) token or request counts
+ *   samples_us  [n_shapes, runs] (host) output: microseconds of each timed call
+ */
+typedef int (*dspark_shape_fn)(int shape, void* user, void* stream);
+int dspark_profile_shapes(dspark_shape_fn fn, void* user, const int32_t* shapes, int n_shapes, int runs, int warmup,
+                          float* samples_us, void* stream);
+
+/*
+ * Start-up construction of a cost table from profiled runs (host memory; vLLM blog,
+ * section "The cost model"):
+ *   1. each shape's cost is the median of its runs (the mean of the two middle runs
+ *      for an even count, in double);
+ *   2. shapes <= graph_max are the captured graph sizes and must include graph_max;
+ *      entry t <= graph_max is the cost of the smallest captured shape >= t (t = 0
+ *      counts as 1): a step runs, and pays for, the padded graph, so the table is a
+ *      staircase (a batch of 121 tokens runs the 128-token graph);
+ *   3. past the capture limit the cost is continuous: entry t > graph_max lies on
+ *      the line through the two nearest measured shapes above graph_max (the first
+ *      or last segment extended beyond them; a single such shape gives a constant),
+ *      evaluated in double as c_a + ((c_b - c_a) * (t - s_a)) / (s_b - s_a);
+ *   4. entries are rounded to float32 and the table is forced monotone, each entry
+ *      the running maximum of the entries up to it.
+ *   shapes      [n_shapes] (host) strictly increasing positive counts
+ *   samples_us  [n_shapes, runs] (host) e.g. from dspark_profile_shapes; finite
+ *   table       [table_len] (host) output, ready for dspark_choose_budget
+ * Returns DSPARK_EINVAL for a NULL pointer, a bad count, unsorted shapes, a
+ * non-finite run, graph_max missing from the shapes, or entries above graph_max
+ * with no measured shape above it.
+ */
+int dspark_build_cost_table(const int32_t* shapes, int n_shapes, const float* samples_us, int runs, int graph_max,
+                            float* table, int table_len);
+
 #ifdef __cplusplus
 }
 #endif
