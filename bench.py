@@ -166,6 +166,40 @@ def stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, 
             "b_last": int(want["b_star"]), "b_same_step": int(same["b_star"]), "parity": "ok" if ok else "MISMATCH"}
 
 
+def sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, steps) -> dict:
+    """Stage 1 with probabilistic drafting (dspark_chain_sample, temperature 1.0, a new
+    seed every step): one launch per position of the general scorer with a Gumbel
+    variate (Philox4x32-10 + two logarithms) per vocabulary entry; timed, and one row of
+    the last step checked against the oracle's sampled chain."""
+    import torch
+    import oracle
+    P = len(pool)
+    tokens = torch.empty((w.R, w.K), dtype=torch.int32, device=dev)
+
+    def run(k):
+        base, prev0, _ = pool[k % P]
+        B.dspark_chain_sample(base, A, Bt, w.dtype, prev0, 1.0, 1000 + k, tokens, None, None, ws)
+
+    for k in range(3):
+        run(k)
+    us = _event_loop_us(run, steps)
+    k = steps - 1
+    st = host_steps[k % P]
+    tok = tokens.cpu().numpy()
+    otok, pert, _ = oracle.chain_sample(st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], 1.0, 1000 + k, rows=[0],
+                                        forced=tok, want_perturbed=True)
+    ok = True
+    for i in range(w.K):
+        if otok[0, i] != tok[0, i]:
+            yo, yg = pert[0, i, otok[0, i]], pert[0, i, tok[0, i]]
+            ok &= bool(yo - yg <= 1e-4 * max(abs(yo), 1.0))
+    elems = w.R * w.K * w.V
+    log(f"bench: sampled chain {us:.1f} us/step ({elems / us / 1e3:.1f} G entries/s), parity {'ok' if ok else 'MISMATCH'}")
+    return {"step_us": round(us, 2), "steps": steps, "temperature": 1.0,
+            "entries_per_s": round(elems / (us * 1e-6), 1), "philox_calls_per_step": elems // 4,
+            "parity_row0": "ok" if ok else "MISMATCH"}
+
+
 def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev) -> dict:
     """Cost tables measured on this GPU at start-up: a proxy verification step (4 bf16
     GEMMs [t, 7168] x [7168, 7168]) over the captured sizes up to the workload's capture
@@ -343,6 +377,7 @@ def main():
         extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule,
                                    min(args.event_steps, K))
 
+    extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, min(args.event_steps, 100))
     extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
 
     sb = step_bytes(w)

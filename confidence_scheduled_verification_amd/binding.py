@@ -29,7 +29,7 @@ RULE_ARGMAX = 0
 RULE_FIRST_DROP = 1
 
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
-           "dspark_chain", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
+           "dspark_chain", "dspark_chain_sample", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
            "dspark_step", "dspark_step_sized", "dspark_accept_greedy", "dspark_set_timing_events",
            "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table"]
 
@@ -63,6 +63,8 @@ def lib():
         L.dspark_workspace_bytes.argtypes = [i, i, i, i, i]
         L.dspark_markov_prepare.argtypes = [p, i, i, i, p, p]
         L.dspark_chain.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, p, sz, p]
+        L.dspark_chain_sample.argtypes = [p, p, p, i, p, i, i, i, i, ctypes.c_float, ctypes.c_uint64, p, p, p, p,
+                                          sz, p]
         L.dspark_survival.argtypes = [p, i, i, p, p, p]
         L.dspark_topb_select.argtypes = [p, i, i, p, p, p, p]
         L.dspark_choose_budget.argtypes = [p, i, i, i, i, p, i, p, i, i, p, p, p, p, p]
@@ -144,6 +146,25 @@ def dspark_chain(base, A, Bt, dtype: int, prev0, tokens, chained_logits=None, st
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().dspark_chain(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(tokens),
                               _p(chained_logits), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_chain_sample(base, A, Bt, dtype: int, prev0, temperature: float, seed: int, tokens, chained_logits=None,
+                        status=None, ws=None, stream=None):
+    """Stage 1 with Gumbel-max sampling of softmax(x / temperature) (Philox4x32-10 keyed on seed)."""
+    R, K, V = base.shape
+    rank = A.shape[1]
+    if tuple(A.shape) != (V, rank) or tuple(Bt.shape) != (V, rank) or tuple(prev0.shape) != (R,) \
+            or tuple(tokens.shape) != (R, K):
+        raise ValueError("dspark_chain_sample: inconsistent shapes")
+    if chained_logits is not None and tuple(chained_logits.shape) != (R, K, V):
+        raise ValueError("dspark_chain_sample: chained_logits must be [R, K, V]")
+    _contig(base, A, Bt, prev0, tokens, chained_logits)
+    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
+        _elem_ok(t, dtype, n)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dspark_chain_sample(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, float(temperature),
+                                     int(seed) & 0xFFFFFFFFFFFFFFFF, _p(tokens), _p(chained_logits), _p(status),
+                                     _p(ws), wsb, _stream(stream)))
 
 
 def dspark_survival(conf, surv, status=None, stream=None):

@@ -136,6 +136,30 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain (finalize)");
 }
 
+int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R,
+                        int K, int V, int rank, float temperature, uint64_t seed, int32_t* tokens,
+                        float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+    if (rc != DSPARK_OK) return rc;
+    if (!(temperature > 0.f) || !isfinite(temperature) || !isfinite(1.0f / temperature))
+        return fail(DSPARK_ERANGE, "chain_sample: temperature %g must be positive, finite and invertible",
+                    (double)temperature);
+    if (R == 0 || K == 0) return DSPARK_OK;
+    if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
+    dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
+                        V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
+                        (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
+                        dspark::SampleArgs{1, (uint32_t)seed, (uint32_t)(seed >> 32), 1.0f / temperature}};
+    hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_chain_bytes(R, K) / 8, s);
+    if (e != hipSuccess) return hip_fail(e, "chain_sample (zero keys)");
+    e = dspark::launch_chain_positions(a, num_cu(), s);
+    if (e != hipSuccess) return hip_fail(e, "chain_sample");
+    e = dspark::launch_chain_finalize(a.keys, tokens, R, K, nullptr, nullptr, nullptr, s);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain_sample (finalize)");
+}
+
 int dspark_survival(const float* conf, int R, int K, float* surv, uint32_t* status, void* stream) {
     if (!conf || !surv) return fail(DSPARK_EINVAL, "survival: NULL pointer");
     if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "survival: negative R (%d) or K (%d)", R, K);

@@ -44,12 +44,15 @@ namespace {
 
 // One launch per position, one vocabulary tile per workgroup, requests in chunks of
 // kReqChunk.  KS = padded rank / 32, VEC = V % 8 == 0 (16-byte base loads), LOGITS =
-// also write the chained logits (general scorer).
-template <int KS, bool VEC, bool LOGITS>
+// the general scorer (chained logits written when `logits` is given, tokens sampled
+// when SAMPLE).
+template <int KS, bool VEC, bool LOGITS, bool SAMPLE = false>
 __global__ __launch_bounds__(kNT, 1) void chain_pos_bf16_kernel(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, int32_t* __restrict__ tokens,
-    float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos) {
+    float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos,
+    SampleArgs smp) {
+    static_assert(LOGITS || !SAMPLE, "sampling runs in the general scorer");
     __shared__ __attribute__((aligned(16))) ChainLds<KS> L;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int vb = blockIdx.x * kTileV + w * kWV;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kNT, 1) void chain_pos_bf16_kernel(
         gather_rows<KS>(L, A, V, rank, RC, 0, rows);
         __syncthreads();
         if (LOGITS) {
-            score_generic<KS, VEC>(L, bt, pre, base, logits, R, K, V, pos, c0, RC, 0, vb);
+            score_generic<KS, VEC, SAMPLE>(L, bt, pre, base, logits, R, K, V, pos, c0, RC, 0, vb, smp);
         } else {
             const int nc0 = c0 + kReqChunk < R ? c0 + kReqChunk : c0;
             score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, 0, vb, pos, nc0);
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
 __global__ __launch_bounds__(kF32Threads) void chain_pos_f32_kernel(
     const float* __restrict__ base, const float* __restrict__ A, const float* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, int32_t* __restrict__ tokens,
-    float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos) {
+    float* __restrict__ logits, uint32_t* __restrict__ status, int R, int K, int V, int rank, int pos,
+    SampleArgs smp) {
     __shared__ uint64_t s_wbest[kF32Threads / 64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int v = blockIdx.x * kF32Threads + tid;
@@ -107,8 +111,13 @@ __global__ __launch_bounds__(kF32Threads) void chain_pos_f32_kernel(
             const float* b = Bt + (size_t)v * rank;
             float acc = 0.f;
             for (int k = 0; k < rank; ++k) acc = fmaf(a[k], b[k], acc);
-            const float x = base[((size_t)r * K + pos) * V + v] + acc;
+            float x = base[((size_t)r * K + pos) * V + v] + acc;
             if (logits != nullptr) logits[((size_t)r * K + pos) * V + v] = x;
+            if (smp.on) {  // Gumbel-max sample of softmax(x / temperature)
+                uint32_t wd[4];
+                philox4x32_10((uint32_t)v >> 2, (uint32_t)pos, (uint32_t)r, 0u, smp.k0, smp.k1, wd);
+                x = x * smp.inv_tau + gumbel_from_bits(wd[v & 3]);
+            }
             key = argmax_key(x, (uint32_t)v);
         }
 #pragma unroll
@@ -205,20 +214,24 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
 
 template <int KS, bool VEC>
 hipError_t launch_bf16(const ChainArgs& a, int grid, hipStream_t s) {
-    if (a.R <= kReqChunk && a.logits == nullptr) {
+    if (a.R <= kReqChunk && a.logits == nullptr && !a.smp.on) {
         const hipError_t e = launch_persist<KS, VEC>(a, grid, s);
         if (e != hipErrorCooperativeLaunchTooLarge) return e;
         (void)hipGetLastError();  // clear the sticky launch error before falling back
     }
     for (int pos = 0; pos < a.K; ++pos) {
-        if (a.logits != nullptr)
+        if (a.smp.on)
+            hipLaunchKernelGGL((chain_pos_bf16_kernel<KS, VEC, true, true>), dim3(grid), dim3(kNT), 0, s,
+                               (const uint16_t*)a.base, (const uint16_t*)a.A, (const uint16_t*)a.Bt, a.prev0, a.keys,
+                               a.tokens, a.logits, a.status, a.R, a.K, a.V, a.rank, pos, a.smp);
+        else if (a.logits != nullptr)
             hipLaunchKernelGGL((chain_pos_bf16_kernel<KS, VEC, true>), dim3(grid), dim3(kNT), 0, s,
                                (const uint16_t*)a.base, (const uint16_t*)a.A, (const uint16_t*)a.Bt, a.prev0, a.keys,
-                               a.tokens, a.logits, a.status, a.R, a.K, a.V, a.rank, pos);
+                               a.tokens, a.logits, a.status, a.R, a.K, a.V, a.rank, pos, a.smp);
         else
             hipLaunchKernelGGL((chain_pos_bf16_kernel<KS, VEC, false>), dim3(grid), dim3(kNT), 0, s,
                                (const uint16_t*)a.base, (const uint16_t*)a.A, (const uint16_t*)a.Bt, a.prev0, a.keys,
-                               a.tokens, nullptr, a.status, a.R, a.K, a.V, a.rank, pos);
+                               a.tokens, nullptr, a.status, a.R, a.K, a.V, a.rank, pos, a.smp);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -256,7 +269,7 @@ hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s)
     for (int pos = 0; pos < a.K; ++pos) {
         hipLaunchKernelGGL(chain_pos_f32_kernel, dim3(grid), dim3(kF32Threads), 0, s, (const float*)a.base,
                            (const float*)a.A, (const float*)a.Bt, a.prev0, a.keys, a.tokens, a.logits, a.status,
-                           a.R, a.K, a.V, a.rank, pos);
+                           a.R, a.K, a.V, a.rank, pos, a.smp);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

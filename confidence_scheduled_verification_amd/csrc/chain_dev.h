@@ -246,10 +246,15 @@ __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __r
 // request's key in L.best[l0 + j] to this wave's best.  pre[] holds the first kPF
 // base blocks of the range, already requested.  General form: optional logits
 // output, ragged tiles, and an exact ordered-key scan for blocks holding a NaN.
-template <int KS, bool VEC>
+// SAMPLE: the key ranks x / temperature + g instead of x, g a standard Gumbel variate
+// of Philox4x32-10 word v % 4 at counter (v / 4, pos, r, 0) under the seed, so the
+// winner is a sample of softmax(x / temperature) (Gumbel-max); the logits output
+// stays x.
+template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void score_generic(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
                                               const uint16_t* __restrict__ base, float* __restrict__ logits, int R,
-                                              int K, int V, int pos, int c0, int RC, int l0, int vb) {
+                                              int K, int V, int pos, int c0, int RC, int l0, int vb,
+                                              const SampleArgs& smp = SampleArgs{}) {
     constexpr int LROW = ChainLds<KS>::LROW, MB = kMB, PF = kPF;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n16 = lane & 15, g = lane >> 4;
@@ -293,6 +298,23 @@ __device__ __forceinline__ void score_generic(ChainLds<KS>& L, const bf16x8 (&bt
                     for (int e = 0; e < 4 * MB; ++e) {
                         const int v = vlane + 32 * (e >> 3) + (e & 7);
                         if (v < V) logits[((size_t)r * K + pos) * V + v] = x[e];
+                    }
+                }
+                if (SAMPLE) {
+                    static_assert(4 * kMB == 16, "the sampled form covers 2 x 8 consecutive entries per lane");
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            uint32_t wd[4];
+                            philox4x32_10((uint32_t)(vlane + 32 * h + 4 * q) >> 2, (uint32_t)pos, (uint32_t)r, 0u,
+                                          smp.k0, smp.k1, wd);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int e = 8 * h + 4 * q + j;
+                                x[e] = x[e] * smp.inv_tau + gumbel_from_bits(wd[j]);
+                            }
+                        }
                     }
                 }
                 if (vb + kWV > V) {  // ragged last tile: entries past V cannot win

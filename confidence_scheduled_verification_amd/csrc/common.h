@@ -59,6 +59,41 @@ __device__ __forceinline__ void publish_key(uint64_t* p, uint64_t k) {
     }
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC 2011): ten rounds of the Philox S-box over the counter (c0, c1, c2, c3)
+// under the key (k0, k1), the key advanced by the two Weyl constants between rounds.
+// Each round's two 32x32 -> 64-bit products are one multiply-add each.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+// Standard Gumbel variate -log(-log u) from 32 random bits: u = (2b + 1) / 2^24 for the
+// top 23 bits b (exact in float32, strictly inside (0, 1)); both logarithms through the
+// hardware base-2 logarithm, scaled by ln 2.
+__device__ __forceinline__ float gumbel_from_bits(uint32_t w) {
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float u = (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
+    const float e = -__builtin_amdgcn_logf(u) * kLn2;  // -ln u, in (0, 16.7)
+    return -__builtin_amdgcn_logf(e) * kLn2;
+}
+
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
     if (status) atomicOr(status, bits);
 }

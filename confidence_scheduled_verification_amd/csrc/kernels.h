@@ -29,6 +29,14 @@ inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4);
 inline size_t ws_chain_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
 inline size_t ws_total_bytes(int R, int K) { return ws_sync_bytes() + ws_chain_bytes(R, K); }
 
+// Probabilistic drafting: Gumbel-max sampling of softmax(x / temperature) with
+// Philox4x32-10 random numbers keyed on the 64-bit seed (k0 low word, k1 high word).
+struct SampleArgs {
+    int on;
+    uint32_t k0, k1;
+    float inv_tau;  // 1 / temperature
+};
+
 struct ChainArgs {
     const void* base;
     const void* A;
@@ -41,6 +49,7 @@ struct ChainArgs {
     uint32_t* status;
     uint64_t* keys;  // [K, R] per-position argmax keys, zeroed before the first position
     uint32_t* bar;   // [K, kMaxGroups] barrier counters, zeroed before the first position
+    SampleArgs smp;  // off unless the tokens are sampled
 };
 
 // Budget sizing: from a separate confidence array [R][K] (separate != 0; conf may be

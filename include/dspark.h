@@ -140,6 +140,28 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
                  uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage 1 with probabilistic drafting: as dspark_chain, but each position's token is
+ * a SAMPLE of softmax(x / temperature) over the chained logits x instead of their
+ * argmax (the vLLM blog's benchmark drafts at temperature 1.0, "Results"), drawn by
+ * the Gumbel-max rule:
+ *   tokens[r,i] = argmax_v  x[v] * (1 / temperature) + g(seed, r, i, v)
+ *   g = -log(-log u),  u = (2 b + 1) / 2^24,  b = top 23 bits of word v % 4 of
+ *       Philox4x32-10 (Salmon et al., SC 2011) at counter (v / 4, i, r, 0) under the
+ *       key (seed & 0xFFFFFFFF, seed >> 32)
+ * and the sampled token keys the next position, as in the greedy chain.  The same
+ * (seed, inputs) always give the same tokens; use a new seed every step.  Both
+ * logarithms use the hardware base-2 logarithm (about 1 ulp), so tokens match an
+ * exact evaluation except where two perturbed values are within rounding of each
+ * other.  chained_logits (optional) receives x, unperturbed.  temperature must be
+ * positive and finite with a finite reciprocal (DSPARK_ERANGE otherwise).  Other
+ * arguments, limits and the workspace are those of dspark_chain.  The tokens can be
+ * scheduled with the stage calls (survival, top-B, budget, allocate with tokens).
+ */
+int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
+                        int R, int K, int V, int rank, float temperature, uint64_t seed, int32_t* tokens,
+                        float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Stage 2, survival (vLLM blog, "Scheduling the budget"): for every request r,
  *   surv[r,0] = c[r,0];  surv[r,i] = fl32(surv[r,i-1] * c[r,i])   for i = 1..K-1,
  * i.e. the inclusive running product in float32, in increasing i.  A confidence

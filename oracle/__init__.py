@@ -44,6 +44,12 @@ def _load():
         lib.oracle_chain.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, p, ctypes.c_int, p, p, p, p]
         lib.oracle_chain.restype = ctypes.c_int
+        lib.oracle_chain_sample.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, p, ctypes.c_int, p, ctypes.c_double, ctypes.c_uint64,
+                                            p, p, p]
+        lib.oracle_chain_sample.restype = ctypes.c_int
+        lib.oracle_philox4x32.argtypes = [p, p, p]
+        lib.oracle_philox4x32.restype = None
         _lib = lib
     return _lib
 
@@ -78,3 +84,41 @@ def chain(base, A, Bmat, dtype, prev0, rows=None, forced=None, want_logits=False
     if rc != 0:
         raise ValueError("oracle_chain rejected its arguments")
     return tokens, logits, int(status[0])
+
+
+def chain_sample(base, A, Bmat, dtype, prev0, temperature, seed, rows=None, forced=None, want_perturbed=False):
+    """Stage 1 with probabilistic drafting (see chain.c): token = argmax_v x[v]/temperature + g(seed, r, i, v).
+
+    Returns (tokens [n_rows,K] int32, perturbed values [n_rows,K,V] float64 or None, status)."""
+    lib = _load()
+    R, K, V = base.shape
+    rank = A.shape[1]
+    assert A.shape == (V, rank) and Bmat.shape == (rank, V)
+    want = np.uint16 if dtype == 1 else np.float32
+    base = np.ascontiguousarray(base, dtype=want)
+    A = np.ascontiguousarray(A, dtype=want)
+    Bmat = np.ascontiguousarray(Bmat, dtype=want)
+    prev0 = np.ascontiguousarray(prev0, dtype=np.int32)
+    rows = np.arange(R, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    if forced is not None:
+        forced = np.ascontiguousarray(forced, dtype=np.int32)
+        assert forced.shape == (R, K)
+    tokens = np.zeros((len(rows), K), dtype=np.int32)
+    pert = np.zeros((len(rows), K, V), dtype=np.float64) if want_perturbed else None
+    status = np.zeros(1, dtype=np.uint32)
+    rc = lib.oracle_chain_sample(_ptr(base), _ptr(A), _ptr(Bmat), int(dtype), _ptr(prev0), R, K, V, rank,
+                                 _ptr(rows), len(rows), _ptr(forced), float(temperature), int(seed),
+                                 _ptr(tokens), _ptr(pert), _ptr(status))
+    if rc != 0:
+        raise ValueError("oracle_chain_sample rejected its arguments")
+    return tokens, pert, int(status[0])
+
+
+def philox4x32(counter, key):
+    """The C oracle's Philox4x32-10 (for pinning it against oracle.rng)."""
+    lib = _load()
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.oracle_philox4x32(_ptr(c), _ptr(k), _ptr(out))
+    return [int(x) for x in out]

@@ -72,13 +72,24 @@ def _close(g, o, rtol):
     return both_nan | same_inf | ok
 
 
-def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows=None):
+def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows=None, sample=None):
     """Compare GPU tokens (and logits for the same rows, if given) with the teacher-forced oracle.
-    gpu_tokens: [R,K] numpy; gpu_logits: [len(rows),K,V] numpy or None.  Returns the near-tie count."""
+    gpu_tokens: [R,K] numpy; gpu_logits: [len(rows),K,V] numpy or None.  sample=(temperature, seed):
+    the tokens are Gumbel-max samples and the near-tie rule applies to the perturbed values
+    x / temperature + g (the oracle's, in double).  Returns the near-tie count."""
     R, K, V = base.shape
     rows = np.arange(R) if rows is None else np.asarray(rows)
     assert gpu_tokens.min() >= 0 and gpu_tokens.max() < V, "token index outside [0, V)"
-    otok, olog, _ = oracle.chain(base, A, Bmat, dtype, prev0, rows=rows, forced=gpu_tokens, want_logits=True)
+    if sample is not None:
+        otok, olog, _ = oracle.chain_sample(base, A, Bmat, dtype, prev0, sample[0], sample[1], rows=rows,
+                                            forced=gpu_tokens, want_perturbed=True)
+        if gpu_logits is not None:
+            _, xlog, _ = oracle.chain(base, A, Bmat, dtype, prev0, rows=rows, forced=gpu_tokens, want_logits=True)
+            ok = _close(gpu_logits.astype(np.float64), xlog, LOGIT_RTOL)
+            assert ok.all(), f"chained logits outside tolerance at {np.argwhere(~ok)[:5].tolist()}"
+            gpu_logits = None
+    else:
+        otok, olog, _ = oracle.chain(base, A, Bmat, dtype, prev0, rows=rows, forced=gpu_tokens, want_logits=True)
     near = 0
     for q, r in enumerate(rows):
         for i in range(K):

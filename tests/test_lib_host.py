@@ -130,6 +130,10 @@ def test_schedule_argument_checks_return_before_launch():
                                p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
     assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, 2341, 0, 4, 0, 4, p, 65, p, 257,
                                p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
+    # sampling: temperature must be positive, finite and invertible
+    for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert L.dspark_chain_sample(p, p, p, 1, p, 4, 7, 1024, 256, t, 1, p, None, None, p, 1 << 20, None) == -2
+    assert L.dspark_chain_sample(p, p, p, 1, p, 0, 7, 1024, 256, 1.0, 1, p, None, None, None, 0, None) == 0
     # acceptance lane: negative sizes, missing target, empty batch
     assert L.dspark_accept_greedy(p, p, p, -1, 7, p, p, None, None, None) == -1
     assert L.dspark_accept_greedy(p, p, None, 4, 7, p, p, None, None, None) == -1
