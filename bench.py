@@ -243,6 +243,8 @@ def main():
     ap.add_argument("--event-steps", type=int, default=200,
                     help="steps of the second pass that times the kernels with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the timed variants (stale sizing, sampling, acceptance, measured tables)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times): under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM traffic counters")
@@ -372,13 +374,15 @@ def main():
     parity = "ok" if ok else "MISMATCH"
     log(f"bench: parity of the last step: {parity}")
 
-    extra = {"accept_greedy": accept_lane(w, B, inputs, out, st, dev)}
-    for label, rule in (("stale_sizing_argmax", B.RULE_ARGMAX), ("stale_sizing_first_drop", B.RULE_FIRST_DROP)):
-        extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule,
-                                   min(args.event_steps, K))
-
-    extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, min(args.event_steps, 100))
-    extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
+    extra = None
+    if not args.no_variants:
+        extra = {"accept_greedy": accept_lane(w, B, inputs, out, st, dev)}
+        for label, rule in (("stale_sizing_argmax", B.RULE_ARGMAX), ("stale_sizing_first_drop", B.RULE_FIRST_DROP)):
+            extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status,
+                                       rule, min(args.event_steps, K))
+        extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev,
+                                               min(args.event_steps, 100))
+        extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
 
     sb = step_bytes(w)
     ck = chain_kernel(w)
