@@ -200,6 +200,20 @@ def sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, steps) -> dict:
             "parity_row0": "ok" if ok else "MISMATCH"}
 
 
+def cooperative_rate(B, run, steps) -> dict:
+    """The same step with its kernel launched cooperatively (the runtime-guaranteed
+    residency mode) instead of the default plain launch of a resident grid."""
+    B.dspark_set_launch_mode(B.LAUNCH_COOPERATIVE)
+    try:
+        for k in range(10):
+            run(k)
+        us = _event_loop_us(run, steps)
+    finally:
+        B.dspark_set_launch_mode(B.LAUNCH_RESIDENT)
+    log(f"bench: cooperative launch {us:.1f} us/step")
+    return {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1), "steps": steps}
+
+
 def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev) -> dict:
     """Cost tables measured on this GPU at start-up: a proxy verification step (4 bf16
     GEMMs [t, 7168] x [7168, 7168]) over the captured sizes up to the workload's capture
@@ -383,6 +397,7 @@ def main():
         extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev,
                                                min(args.event_steps, 100))
         extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
+        extra["cooperative_launch"] = cooperative_rate(B, run, min(args.event_steps, K))
 
     sb = step_bytes(w)
     ck = chain_kernel(w)
@@ -406,7 +421,8 @@ def main():
         "dtype": "bf16" if w.dtype == 1 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: R={w.R} (of {w.R_all}), K={w.K}, V={w.V}, r={w.rank}, T={w.T}, "
-                               f"N_sampling={w.n_sampling}", "input_pool": len(pool)},
+                               f"N_sampling={w.n_sampling}", "input_pool": len(pool),
+                   "launch": "resident (plain launch of a grid that fits the device; one stream)"},
         "roofline": roofline,
         "step_bytes": sb["total"],
         "step_hbm_frac": round(sb["total"] / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),

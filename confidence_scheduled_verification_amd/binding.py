@@ -24,6 +24,8 @@ STATUS_CONF_SANITIZED = 2
 STATUS_COST_INVALID = 4
 STATUS_SYNC_TIMEOUT = 8
 STATUS_BAD_ALLOCATION = 16
+LAUNCH_RESIDENT = 0
+LAUNCH_COOPERATIVE = 1
 MAX_SLOTS = 16384
 RULE_ARGMAX = 0
 RULE_FIRST_DROP = 1
@@ -31,7 +33,8 @@ RULE_FIRST_DROP = 1
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
            "dspark_chain", "dspark_chain_sample", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
            "dspark_step", "dspark_step_sized", "dspark_accept_greedy", "dspark_set_timing_events",
-           "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table"]
+           "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table", "dspark_set_launch_mode",
+           "dspark_get_launch_mode"]
 
 # int fn(int shape, void* user, void* stream)
 SHAPE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p)
@@ -75,6 +78,8 @@ def lib():
                                         p, p, p, p, p, p, p, p, sz, p]
         L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
         L.dspark_set_timing_events.argtypes = [p, p]
+        L.dspark_set_launch_mode.argtypes = [i]
+        L.dspark_get_launch_mode.argtypes = []
         L.dspark_force_monotone.argtypes = [p, i]
         L.dspark_profile_shapes.argtypes = [SHAPE_FN, p, p, i, i, i, p, p]
         L.dspark_build_cost_table.argtypes = [p, i, p, i, i, p, i]
@@ -254,6 +259,15 @@ def dspark_accept_greedy(ver_tokens, offsets, target, R: int, K: int, accept_len
         raise ValueError("dspark_accept_greedy: inconsistent sizes")
     _check(lib().dspark_accept_greedy(_p(ver_tokens), _p(offsets), _p(target), R, K, _p(accept_len),
                                       _p(next_prev0), _p(out_tokens), _p(status), _stream(stream)))
+
+
+def dspark_set_launch_mode(mode: int):
+    """Launch of the persistent kernels: LAUNCH_RESIDENT (plain, default) or LAUNCH_COOPERATIVE."""
+    _check(lib().dspark_set_launch_mode(mode))
+
+
+def dspark_get_launch_mode() -> int:
+    return int(lib().dspark_get_launch_mode())
 
 
 def dspark_set_timing_events(before_chain=None, after_chain=None):

@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "dspark.h"
@@ -17,6 +18,7 @@ static_assert(dspark::kMaxSlotsWs == DSPARK_MAX_SLOTS, "the step counters are si
 namespace {
 
 thread_local char g_err[512] = "";
+std::atomic<int> g_launch_mode{DSPARK_LAUNCH_RESIDENT};
 thread_local hipEvent_t g_ev_before_chain = nullptr;
 thread_local hipEvent_t g_ev_after_chain = nullptr;
 
@@ -46,6 +48,8 @@ int num_cu() {
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int coop_launch() { return g_launch_mode.load(std::memory_order_relaxed) == DSPARK_LAUNCH_COOPERATIVE ? 1 : 0; }
 
 size_t keys_bytes(int R, int K) { return dspark::ws_total_bytes(R, K); }
 
@@ -127,7 +131,8 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
     char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
                         V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
-                        (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K))};
+                        (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)), dspark::SampleArgs{},
+                        coop_launch()};
     hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_chain_bytes(R, K) / 8, s);
     if (e != hipSuccess) return hip_fail(e, "chain (zero keys)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
@@ -151,7 +156,8 @@ int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dty
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
                         V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
                         (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
-                        dspark::SampleArgs{1, (uint32_t)seed, (uint32_t)(seed >> 32), 1.0f / temperature}};
+                        dspark::SampleArgs{1, (uint32_t)seed, (uint32_t)(seed >> 32), 1.0f / temperature},
+                        coop_launch()};
     hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_chain_bytes(R, K) / 8, s);
     if (e != hipSuccess) return hip_fail(e, "chain_sample (zero keys)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
@@ -245,7 +251,8 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
         dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status,
                             (uint64_t*)(w + dspark::ws_sync_bytes()), (uint32_t*)w, conf,
                             n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, sizing, surv, order,
-                            sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens};
+                            sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens,
+                            coop_launch()};
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
         e = dspark::launch_step_single(st, s);
@@ -266,7 +273,8 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
     if (n == 0) return DSPARK_OK;
     char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
     dspark::ChainArgs a{base,    A,      Bt,     dtype, prev0, R, K, V, rank, tokens, nullptr, status,
-                        (uint64_t*)chain_ws, (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K))};
+                        (uint64_t*)chain_ws, (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
+                        dspark::SampleArgs{}, coop_launch()};
     if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
         return hip_fail(e, "step (timing event)");
     e = dspark::launch_chain_positions(a, num_cu(), s);
@@ -301,6 +309,15 @@ int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, cons
                                                       out_tokens, status, (hipStream_t)stream);
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "accept_greedy");
 }
+
+int dspark_set_launch_mode(int mode) {
+    if (mode != DSPARK_LAUNCH_RESIDENT && mode != DSPARK_LAUNCH_COOPERATIVE)
+        return fail(DSPARK_EINVAL, "set_launch_mode: unknown mode %d", mode);
+    g_launch_mode.store(mode, std::memory_order_relaxed);
+    return DSPARK_OK;
+}
+
+int dspark_get_launch_mode(void) { return g_launch_mode.load(std::memory_order_relaxed); }
 
 int dspark_set_timing_events(void* before_chain, void* after_chain) {
     g_ev_before_chain = (hipEvent_t)before_chain;

@@ -208,6 +208,11 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
     int32_t* tokens = a.tokens;
     uint32_t* status = a.status;
     int R = a.R, K = a.K, V = a.V, rank = a.rank;
+    if (!a.coop) {
+        hipLaunchKernelGGL((chain_persist_bf16_kernel<KS, VEC>), dim3(grid), dim3(kNT), 0, s, base, A, Bt, prev0,
+                           keys, bar, tokens, status, R, K, V, rank);
+        return hipGetLastError();
+    }
     void* args[] = {&base, &A, &Bt, &prev0, &keys, &bar, &tokens, &status, &R, &K, &V, &rank};
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, 0, s);
 }

@@ -25,6 +25,9 @@ constexpr int kMB = DSPARK_CHAIN_MB;        // 16-row M blocks per wave (even)
 #ifndef DSPARK_CHAIN_PF
 #define DSPARK_CHAIN_PF 4
 #endif
+#ifndef DSPARK_BASE_AUX
+#define DSPARK_BASE_AUX 0
+#endif
 constexpr int kPF = DSPARK_CHAIN_PF;        // request blocks of base prefetched ahead
 constexpr int kWV = 16 * kMB;    // vocabulary entries per wave
 constexpr int kTileV = kWaves * kWV;
@@ -120,7 +123,8 @@ __device__ __forceinline__ void load_block(BaseFrag& f, const BaseSrc& src, __am
     if (VEC) {
         const uint32_t off = src.voff + (uint32_t)t * src.bstride;
 #pragma unroll
-        for (int p = 0; p < kMB / 2; ++p) f.q[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 64 * p), 0, 0);
+        for (int p = 0; p < kMB / 2; ++p)
+            f.q[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 64 * p), 0, DSPARK_BASE_AUX);
     } else {
         load_base<false>(f, src.base, c0 + t * 16 + n16, R, K, V, pos, vlane);
     }

@@ -50,6 +50,7 @@ struct ChainArgs {
     uint64_t* keys;  // [K, R] per-position argmax keys, zeroed before the first position
     uint32_t* bar;   // [K, kMaxGroups] barrier counters, zeroed before the first position
     SampleArgs smp;  // off unless the tokens are sampled
+    int coop;        // persistent kernel: cooperative launch (1) or plain launch of a resident grid (0)
 };
 
 // Budget sizing: from a separate confidence array [R][K] (separate != 0; conf may be
@@ -124,9 +125,17 @@ struct StepArgs {
     int32_t* offsets;
     int32_t* ver_idx;
     int32_t* ver_tokens;
+    int coop;  // cooperative launch (1) or plain launch of a resident grid (0)
 };
 
 int chain_tile_vocab();
+// Persistent kernels (the single-launch step, the single-launch chain) keep every
+// workgroup resident and synchronise them through counters in the workspace.  They are
+// launched either cooperatively (the runtime guarantees residency, at a cost of about
+// 17 us per launch on this part) or as a plain launch of a grid that fits on the
+// device at once (the caller keeps other kernels off the device meanwhile; every wait
+// is bounded, so a workgroup held back longer than the bound ends the step with
+// DSPARK_STATUS_SYNC_TIMEOUT instead of hanging).
 // bf16 with 1 <= R <= 256 when the grid fits on the device at once; otherwise
 // hipErrorCooperativeLaunchTooLarge (nothing enqueued) and the caller runs the
 // stage-wise launches.

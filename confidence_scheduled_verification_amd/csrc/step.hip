@@ -7,7 +7,7 @@
 // they run side by side: the grid is one workgroup per vocabulary tile for the
 // chain plus one more workgroup that schedules.  The vocabulary tiles leave a few
 // CUs free, so the schedule costs no chain time, and the step pays for one launch
-// instead of three (a cooperative launch alone costs about 17 us on this part).
+// instead of three.
 //
 // The extra workgroup also
 //   * zeroes the argmax keys first and then raises a ready flag, which the chain
@@ -108,6 +108,10 @@ hipError_t launch_single(const StepArgs& a, int grid, hipStream_t s) {
         resident[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
     }
     if (grid > resident[dev]) return hipErrorCooperativeLaunchTooLarge;
+    if (!a.coop) {
+        hipLaunchKernelGGL((step_single_bf16_kernel<KS, VEC>), dim3(grid), dim3(kNT), 0, s, a);
+        return hipGetLastError();
+    }
     StepArgs arg = a;
     void* args[] = {&arg};
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, 0, s);

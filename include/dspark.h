@@ -66,8 +66,9 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
 #define DSPARK_STATUS_CONF_SANITIZED 2u /* a confidence was NaN or outside [0,1]; NaN and <0 became 0, >1 became 1 */
 #define DSPARK_STATUS_COST_INVALID 4u   /* verify_cost[T+B] + draft_cost[num_reqs] was not a positive finite
                                            number for some B; that B's objective is -inf                    */
-#define DSPARK_STATUS_SYNC_TIMEOUT 8u   /* the single-launch chain waited too long at a grid barrier (its
-                                           workgroups were not all resident); tokens are then unreliable    */
+#define DSPARK_STATUS_SYNC_TIMEOUT 8u   /* a persistent kernel waited too long at a grid barrier (its
+                                           workgroups were not all resident; see dspark_set_launch_mode);
+                                           tokens are then unreliable                                       */
 #define DSPARK_STATUS_BAD_ALLOCATION 16u /* dspark_accept_greedy met an inconsistent offsets row; that request
                                            accepted nothing and its next prev0 is -1                        */
 
@@ -307,6 +308,27 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
 int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R, int K,
                          int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens, uint32_t* status,
                          void* stream);
+
+/*
+ * How the persistent kernels are launched.  The single-launch step (dspark_step,
+ * dspark_step_sized) and the single-launch bf16 chain (dspark_chain) keep every
+ * workgroup resident for the whole step and synchronise them through counters in the
+ * workspace, which needs all of their workgroups on the device at once (the grid is
+ * sized to fit: one workgroup per compute unit).
+ *   DSPARK_LAUNCH_RESIDENT (default): a plain kernel launch.  The caller keeps other
+ *       kernels off the device while a step runs (one engine stream, as a serving
+ *       engine has).  Should another kernel hold compute units, the step waits for
+ *       them; every wait is bounded, and a workgroup held back past the bound ends the
+ *       step with DSPARK_STATUS_SYNC_TIMEOUT (tokens then unreliable) instead of hanging.
+ *   DSPARK_LAUNCH_COOPERATIVE: hipLaunchCooperativeKernel, which guarantees residency
+ *       on a shared device; on MI355X it costs about 17 us more per launch.
+ * Process-wide; takes effect for calls made after it.  Returns DSPARK_EINVAL for an
+ * unknown mode.
+ */
+#define DSPARK_LAUNCH_RESIDENT 0
+#define DSPARK_LAUNCH_COOPERATIVE 1
+int dspark_set_launch_mode(int mode);
+int dspark_get_launch_mode(void);
 
 /*
  * Measurement hook.  When set (non-NULL hipEvent_t handles), every later

@@ -123,3 +123,27 @@ def test_single_launch_step_at_the_slot_limit():
     want = sched.schedule(conf, R, 0, R, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, R, K)
     assert 0 < got["b_star"] < R * K
+
+
+@pytest.mark.parametrize("name", ["small", "headline"])
+def test_launch_modes_give_identical_results(name):
+    # The persistent kernels run as a plain launch of a resident grid (default) or as a
+    # cooperative launch; the work is the same, so every output must match bit for bit.
+    w = inputs.WORKLOADS[name]
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    assert B.dspark_get_launch_mode() == B.LAUNCH_RESIDENT
+    res, st_r, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+    tok_r, _, st_cr = ch.run()
+    try:
+        B.dspark_set_launch_mode(B.LAUNCH_COOPERATIVE)
+        coop, st_c, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+        tok_c, _, st_cc = ch.run()
+    finally:
+        B.dspark_set_launch_mode(B.LAUNCH_RESIDENT)
+    assert st_r == st_c == st_cr == st_cc == 0
+    for k in res:
+        assert np.array_equal(np.asarray(res[k]), np.asarray(coop[k])), k
+    np.testing.assert_array_equal(tok_r.cpu().numpy(), tok_c.cpu().numpy())
+    np.testing.assert_array_equal(tok_r.cpu().numpy(), res["tokens"])

@@ -134,6 +134,11 @@ def test_schedule_argument_checks_return_before_launch():
     for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
         assert L.dspark_chain_sample(p, p, p, 1, p, 4, 7, 1024, 256, t, 1, p, None, None, p, 1 << 20, None) == -2
     assert L.dspark_chain_sample(p, p, p, 1, p, 0, 7, 1024, 256, 1.0, 1, p, None, None, None, 0, None) == 0
+    # launch mode: default resident, unknown modes rejected
+    assert L.dspark_get_launch_mode() == 0
+    assert L.dspark_set_launch_mode(7) == -1 and L.dspark_get_launch_mode() == 0
+    assert L.dspark_set_launch_mode(1) == 0 and L.dspark_get_launch_mode() == 1
+    assert L.dspark_set_launch_mode(0) == 0
     # acceptance lane: negative sizes, missing target, empty batch
     assert L.dspark_accept_greedy(p, p, p, -1, 7, p, p, None, None, None) == -1
     assert L.dspark_accept_greedy(p, p, None, 4, 7, p, p, None, None, None) == -1
