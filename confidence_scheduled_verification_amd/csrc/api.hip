@@ -146,7 +146,8 @@ int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dty
                         float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
     if (rc != DSPARK_OK) return rc;
-    if (!(temperature > 0.f) || !isfinite(temperature) || !isfinite(1.0f / temperature))
+    const float scale = 1.4426950408889634f / temperature;  // log2(e) / temperature
+    if (!(temperature > 0.f) || !isfinite(temperature) || !isfinite(scale))
         return fail(DSPARK_ERANGE, "chain_sample: temperature %g must be positive, finite and invertible",
                     (double)temperature);
     if (R == 0 || K == 0) return DSPARK_OK;
@@ -156,7 +157,7 @@ int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dty
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
                         V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
                         (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
-                        dspark::SampleArgs{1, (uint32_t)seed, (uint32_t)(seed >> 32), 1.0f / temperature},
+                        dspark::SampleArgs{1, (uint32_t)seed, (uint32_t)(seed >> 32), scale},
                         coop_launch()};
     hipError_t e = dspark::launch_zero_keys(a.keys, dspark::ws_chain_bytes(R, K) / 8, s);
     if (e != hipSuccess) return hip_fail(e, "chain_sample (zero keys)");

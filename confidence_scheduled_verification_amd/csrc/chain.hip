@@ -81,16 +81,16 @@ __global__ __launch_bounds__(kNT, 1) void chain_pos_bf16_kernel(
     }
 }
 
-// All K positions in one cooperative launch (R <= kReqChunk, gridDim.x <= resident
-// workgroups).
-template <int KS, bool VEC>
+// All K positions in one launch of a resident grid (R <= kReqChunk, gridDim.x <= resident
+// workgroups).  SAMPLE: tokens drawn by Gumbel-max (probabilistic drafting).
+template <int KS, bool VEC, bool SAMPLE>
 __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, uint32_t* __restrict__ bar,
-    int32_t* __restrict__ tokens, uint32_t* __restrict__ status, int R, int K, int V, int rank) {
+    int32_t* __restrict__ tokens, uint32_t* __restrict__ status, int R, int K, int V, int rank, SampleArgs smp) {
     __shared__ __attribute__((aligned(16))) ChainLds<KS> L;
-    chain_persist_body<KS, VEC>(L, base, A, Bt, prev0, keys, bar, tokens, status, R, K, V, rank, (int)gridDim.x,
-                                nullptr);
+    chain_persist_body<KS, VEC, SAMPLE>(L, base, A, Bt, prev0, keys, bar, tokens, status, R, K, V, rank,
+                                        (int)gridDim.x, nullptr, smp);
 }
 
 // fp32 factors: one thread per vocabulary entry, fused multiply-add in increasing k.
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kF32Threads) void chain_pos_f32_kernel(
             if (smp.on) {  // Gumbel-max sample of softmax(x / temperature)
                 uint32_t wd[4];
                 philox4x32_10((uint32_t)v >> 2, (uint32_t)pos, (uint32_t)r, 0u, smp.k0, smp.k1, wd);
-                x = x * smp.inv_tau + gumbel_from_bits(wd[v & 3]);
+                x = sampled_value(x, smp.scale, wd[v & 3]);
             }
             key = argmax_key(x, (uint32_t)v);
         }
@@ -184,9 +184,9 @@ __global__ void transpose_kernel(const T* __restrict__ src, int rows, int cols, 
 // workgroup per CU (the LDS footprint allows no more), so the grid must not exceed
 // the CUs reported by the occupancy query.  Returns hipErrorCooperativeLaunchTooLarge
 // when it does not fit; the caller then launches per position.
-template <int KS, bool VEC>
+template <int KS, bool VEC, bool SAMPLE>
 hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
-    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC>;
+    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC, SAMPLE>;
     static int resident[64] = {0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -208,19 +208,20 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
     int32_t* tokens = a.tokens;
     uint32_t* status = a.status;
     int R = a.R, K = a.K, V = a.V, rank = a.rank;
+    SampleArgs smp = a.smp;
     if (!a.coop) {
-        hipLaunchKernelGGL((chain_persist_bf16_kernel<KS, VEC>), dim3(grid), dim3(kNT), 0, s, base, A, Bt, prev0,
-                           keys, bar, tokens, status, R, K, V, rank);
+        hipLaunchKernelGGL((chain_persist_bf16_kernel<KS, VEC, SAMPLE>), dim3(grid), dim3(kNT), 0, s, base, A, Bt,
+                           prev0, keys, bar, tokens, status, R, K, V, rank, smp);
         return hipGetLastError();
     }
-    void* args[] = {&base, &A, &Bt, &prev0, &keys, &bar, &tokens, &status, &R, &K, &V, &rank};
+    void* args[] = {&base, &A, &Bt, &prev0, &keys, &bar, &tokens, &status, &R, &K, &V, &rank, &smp};
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, 0, s);
 }
 
 template <int KS, bool VEC>
 hipError_t launch_bf16(const ChainArgs& a, int grid, hipStream_t s) {
-    if (a.R <= kReqChunk && a.logits == nullptr && !a.smp.on) {
-        const hipError_t e = launch_persist<KS, VEC>(a, grid, s);
+    if (a.R <= kReqChunk && a.logits == nullptr) {
+        const hipError_t e = a.smp.on ? launch_persist<KS, VEC, true>(a, grid, s) : launch_persist<KS, VEC, false>(a, grid, s);
         if (e != hipErrorCooperativeLaunchTooLarge) return e;
         (void)hipGetLastError();  // clear the sticky launch error before falling back
     }

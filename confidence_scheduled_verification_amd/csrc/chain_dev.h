@@ -246,14 +246,31 @@ __device__ __forceinline__ void gather_rows(ChainLds<KS>& L, const uint16_t* __r
     if (WAIT) __builtin_amdgcn_s_waitcnt(0);  // this wave's slots have landed (the caller then syncs the workgroup)
 }
 
+// Probabilistic drafting: lane element e (vocabulary vlane + 32*(e/8) + e%8) of request r
+// becomes its sampled value (x / temperature + a Gumbel variate, in base 2) from
+// Philox4x32-10 word v % 4 at counter (v / 4, pos, r, 0) under the seed (one call per 4
+// consecutive entries).
+template <int NE>
+__device__ __forceinline__ void perturb(float (&x)[NE], const SampleArgs& smp, int vlane, int pos, int r) {
+    static_assert(NE == 16, "2 x 8 consecutive entries per lane");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t wd[4];
+            philox4x32_10((uint32_t)(vlane + 32 * h + 4 * q) >> 2, (uint32_t)pos, (uint32_t)r, 0u, smp.k0, smp.k1, wd);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[8 * h + 4 * q + j] = sampled_value(x[8 * h + 4 * q + j], smp.scale, wd[j]);
+        }
+    }
+}
+
 // Score the wave's 64 vocabulary rows against requests [c0, c0+RC) and raise each
 // request's key in L.best[l0 + j] to this wave's best.  pre[] holds the first kPF
 // base blocks of the range, already requested.  General form: optional logits
 // output, ragged tiles, and an exact ordered-key scan for blocks holding a NaN.
-// SAMPLE: the key ranks x / temperature + g instead of x, g a standard Gumbel variate
-// of Philox4x32-10 word v % 4 at counter (v / 4, pos, r, 0) under the seed, so the
-// winner is a sample of softmax(x / temperature) (Gumbel-max); the logits output
-// stays x.
+// SAMPLE: the key ranks the sampled value (see perturb) instead of x, so the winner is
+// a sample of softmax(x / temperature) (Gumbel-max); the logits output stays x.
 template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void score_generic(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
                                               const uint16_t* __restrict__ base, float* __restrict__ logits, int R,
@@ -304,23 +321,7 @@ __device__ __forceinline__ void score_generic(ChainLds<KS>& L, const bf16x8 (&bt
                         if (v < V) logits[((size_t)r * K + pos) * V + v] = x[e];
                     }
                 }
-                if (SAMPLE) {
-                    static_assert(4 * kMB == 16, "the sampled form covers 2 x 8 consecutive entries per lane");
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            uint32_t wd[4];
-                            philox4x32_10((uint32_t)(vlane + 32 * h + 4 * q) >> 2, (uint32_t)pos, (uint32_t)r, 0u,
-                                          smp.k0, smp.k1, wd);
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int e = 8 * h + 4 * q + j;
-                                x[e] = x[e] * smp.inv_tau + gumbel_from_bits(wd[j]);
-                            }
-                        }
-                    }
-                }
+                if (SAMPLE) perturb(x, smp, vlane, pos, r);
                 if (vb + kWV > V) {  // ragged last tile: entries past V cannot win
 #pragma unroll
                     for (int e = 0; e < 4 * MB; ++e)
@@ -479,13 +480,15 @@ struct Argmax {
 // One pipeline stage: start block b+1 (accumulators from its ring slot, refill of
 // the slot, then its matrix-core instructions one k-chunk at a time) and finish
 // block b's argmax, a slice after each k-chunk.
-template <int KS, bool TAIL, bool VEC, typename Refill>
+template <int KS, bool TAIL, bool VEC, bool SAMPLE, typename Refill>
 __device__ __forceinline__ void stage(f32x4 (&nxt)[kMB], BaseFrag& slot, Refill&& refill, int t,
                                       const bf16x8 (&bt)[kMB][KS], const uint16_t* arow, const f32x4 (&cur)[kMB],
-                                      uint64_t* best, int vlane, int V, uint64_t& nan_mask) {
+                                      uint64_t* best, int vlane, int V, uint64_t& nan_mask, const SampleArgs& smp,
+                                      int pos, int r) {
     init_acc<TAIL, VEC>(nxt, slot, vlane, V);
     refill(slot, t);
     Argmax am(cur);
+    if (SAMPLE) perturb(am.x, smp, vlane, pos, r);
     // key-row fragments are read one k-chunk ahead of their matrix-core use
     bf16x8 bfr = *(const bf16x8*)arow;
 #pragma unroll
@@ -501,8 +504,11 @@ __device__ __forceinline__ void stage(f32x4 (&nxt)[kMB], BaseFrag& slot, Refill&
     }
 }
 
-__device__ __forceinline__ void block_argmax(const f32x4 (&acc)[kMB], uint64_t* best, int vlane, uint64_t& nan_mask) {
+template <bool SAMPLE>
+__device__ __forceinline__ void block_argmax(const f32x4 (&acc)[kMB], uint64_t* best, int vlane, uint64_t& nan_mask,
+                                             const SampleArgs& smp, int pos, int r) {
     Argmax am(acc);
+    if (SAMPLE) perturb(am.x, smp, vlane, pos, r);
 #pragma unroll
     for (int s = 0; s < 8; ++s) am.slice(s, best, vlane, nan_mask);
 }
@@ -517,10 +523,11 @@ __device__ __forceinline__ void block_argmax(const f32x4 (&acc)[kMB], uint64_t* 
 // full when the next call starts.  The sweep covers fast_rows(RC) rows (whole ring
 // cycles); blocks past RC score zero key rows into keys never published.
 // Returns the wave's NaN mask (nonzero: rescore exactly).
-template <int KS, bool VEC, bool TAIL>
+template <int KS, bool VEC, bool TAIL, bool SAMPLE>
 __device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
                                                const uint16_t* __restrict__ base, int R, int K, int V, int pos,
-                                               int c0, int RC, int l0, int vb, int npos, int nc0) {
+                                               int c0, int RC, int l0, int vb, int npos, int nc0,
+                                               const SampleArgs& smp) {
     constexpr int LROW = ChainLds<KS>::LROW, PF = kPF;
     static_assert(PF % 2 == 0, "the two accumulator sets alternate within a ring cycle");
     const int lane = threadIdx.x & 63;
@@ -549,27 +556,30 @@ __device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&b
 #pragma unroll
         for (int q = 0; q < PF; ++q) {
             const int rb = rb0 + q;
-            stage<KS, TAIL, VEC>(acc[(q + 1) & 1], pre[(q + 1) % PF], refill, rb + 1 + PF, bt,
-                                 arow + (rb + 1) * 16 * LROW, acc[q & 1], best + rb * 16, vlane, V, nan_mask);
+            stage<KS, TAIL, VEC, SAMPLE>(acc[(q + 1) & 1], pre[(q + 1) % PF], refill, rb + 1 + PF, bt,
+                                         arow + (rb + 1) * 16 * LROW, acc[q & 1], best + rb * 16, vlane, V, nan_mask,
+                                         smp, pos, c0 + rb * 16 + n16);
         }
     }
     // last ring cycle: its final stage has no next block
 #pragma unroll
     for (int q = 0; q + 1 < PF; ++q) {
         const int rb = rb0 + q;
-        stage<KS, TAIL, VEC>(acc[(q + 1) & 1], pre[(q + 1) % PF], refill, rb + 1 + PF, bt,
-                             arow + (rb + 1) * 16 * LROW, acc[q & 1], best + rb * 16, vlane, V, nan_mask);
+        stage<KS, TAIL, VEC, SAMPLE>(acc[(q + 1) & 1], pre[(q + 1) % PF], refill, rb + 1 + PF, bt,
+                                     arow + (rb + 1) * 16 * LROW, acc[q & 1], best + rb * 16, vlane, V, nan_mask, smp,
+                                     pos, c0 + rb * 16 + n16);
     }
-    block_argmax(acc[(PF - 1) & 1], best + (rb0 + PF - 1) * 16, vlane, nan_mask);
+    block_argmax<SAMPLE>(acc[(PF - 1) & 1], best + (rb0 + PF - 1) * 16, vlane, nan_mask, smp, pos,
+                         c0 + (rb0 + PF - 1) * 16 + n16);
     return nan_mask;
 }
 
 // Exact rescore of the wave's blocks, one at a time (base loaded per block): the
 // ordered-key scan of every element, for waves whose fast pass met a NaN.
-template <int KS, bool VEC>
+template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void score_exact(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS],
                                             const uint16_t* __restrict__ base, int R, int K, int V, int pos, int c0,
-                                            int RC, int l0, int vb) {
+                                            int RC, int l0, int vb, const SampleArgs& smp = SampleArgs{}) {
     constexpr int LROW = ChainLds<KS>::LROW;
     const int lane = threadIdx.x & 63;
     const int n16 = lane & 15, g = lane >> 4;
@@ -581,11 +591,15 @@ __device__ __forceinline__ void score_exact(ChainLds<KS>& L, const bf16x8 (&bt)[
         f32x4 acc[kMB];
         init_acc<true, VEC>(acc, f, vlane, V);
         mfma_block<KS>(acc, bt, L.a + (l0 + rb * 16 + n16) * LROW + g * 8);
+        float x[4 * kMB];
+#pragma unroll
+        for (int e = 0; e < 4 * kMB; ++e) x[e] = acc[2 * (e >> 3) + ((e & 7) >> 2)][e & 3];
+        if (SAMPLE) perturb(x, smp, vlane, pos, c0 + rb * 16 + n16);
         uint32_t bu = 0u, bv = 0u;
 #pragma unroll
         for (int e = 0; e < 4 * kMB; ++e) {
             const uint32_t v = (uint32_t)(vlane + 32 * (e >> 3) + (e & 7));
-            const uint32_t u = ordered_u32(acc[2 * (e >> 3) + ((e & 7) >> 2)][e & 3]);
+            const uint32_t u = ordered_u32(x[e]);
             if (v < (uint32_t)V && u > bu) {
                 bu = u;
                 bv = v;
@@ -601,15 +615,17 @@ __device__ __forceinline__ void score_exact(ChainLds<KS>& L, const bf16x8 (&bt)[
 // Score dispatch without logits output: the pipelined form; waves wholly past V
 // have nothing to score; a NaN seen by the fast form triggers an exact rescore of
 // the wave (its keys only ever raise the stored ones).
-template <int KS, bool VEC>
+template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
                                            const uint16_t* __restrict__ base, int R, int K, int V, int pos, int c0,
-                                           int RC, int l0, int vb, int npos, int nc0) {
+                                           int RC, int l0, int vb, int npos, int nc0,
+                                           const SampleArgs& smp = SampleArgs{}) {
     if (vb >= V) return;
     const uint64_t nan_mask =
-        (vb + kWV > V) ? score_fast<KS, VEC, true>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0)
-                       : score_fast<KS, VEC, false>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0);
-    if (nan_mask != 0ull) score_exact<KS, VEC>(L, bt, base, R, K, V, pos, c0, RC, l0, vb);
+        (vb + kWV > V)
+            ? score_fast<KS, VEC, true, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp)
+            : score_fast<KS, VEC, false, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp);
+    if (nan_mask != 0ull) score_exact<KS, VEC, SAMPLE>(L, bt, base, R, K, V, pos, c0, RC, l0, vb, smp);
 }
 
 // Best key over the waves, raised into the device-wide key of each request by an
@@ -693,13 +709,13 @@ __device__ __forceinline__ int half_split(int R) {
 //   score h0 | wait h1(p-1), decode h1(p), gather h1 (async), publish h0(p), arrive h0
 //   score h1 | wait h0(p),   decode h0(p+1), gather h0 (async), publish h1(p), arrive h1
 // Barrier counters: bar[p * kMaxGroups + h].
-template <int KS, bool VEC>
+template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16_t* __restrict__ base,
                                                    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
                                                    const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys,
                                                    uint32_t* __restrict__ bar, int32_t* __restrict__ tokens,
                                                    uint32_t* __restrict__ status, int R, int K, int V, int rank,
-                                                   int G, const uint32_t* ready) {
+                                                   int G, const uint32_t* ready, const SampleArgs& smp = SampleArgs{}) {
     static_assert(kMaxGroups >= 2, "two request halves");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int vb = blockIdx.x * kTileV + w * kWV;
@@ -723,7 +739,8 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
         const bool more = ns < nseg;
         const int npos = two ? ns >> 1 : ns, nh = two ? ns & 1 : 0;
         const int nc0 = nh ? H : 0, nRC = nh ? RC1 : H, nrows = nh ? rows1 : rows0;
-        score_rows<KS, VEC>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos, more ? nc0 : c0);
+        score_rows<KS, VEC, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos,
+                                    more ? nc0 : c0, smp);
         __syncthreads();
         if (two) {
             // The key atomics go out first, from the upper half of the waves; their

@@ -84,14 +84,15 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
     out[3] = c3;
 }
 
-// Standard Gumbel variate -log(-log u) from 32 random bits: u = (2b + 1) / 2^24 for the
-// top 23 bits b (exact in float32, strictly inside (0, 1)); both logarithms through the
-// hardware base-2 logarithm, scaled by ln 2.
-__device__ __forceinline__ float gumbel_from_bits(uint32_t w) {
-    constexpr float kLn2 = 0.693147180559945309f;
-    const float u = (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
-    const float e = -__builtin_amdgcn_logf(u) * kLn2;  // -ln u, in (0, 16.7)
-    return -__builtin_amdgcn_logf(e) * kLn2;
+// The value a sampled entry is ranked by: x / T + g, g = -ln(-ln u) a standard Gumbel
+// variate, u = (2b + 1) / 2^24 for the top 23 bits b of w (exact in float32, strictly
+// inside (0, 1)) -- computed in base 2 as x * (log2(e) / T) - log2(-log2 u), which is
+// log2(e) (x / T + g) + log2(ln 2): a positive affine image with the same argmax, at
+// one fused multiply-add and two hardware base-2 logarithms.  scale = log2(e) / T.
+__device__ __forceinline__ float sampled_value(float x, float scale, uint32_t w) {
+    const float u = (float)((w >> 8) | 1u) * 0x1p-24f;
+    const float l = __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+    return __builtin_fmaf(x, scale, -l);
 }
 
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {

@@ -34,7 +34,7 @@ inline size_t ws_total_bytes(int R, int K) { return ws_sync_bytes() + ws_chain_b
 struct SampleArgs {
     int on;
     uint32_t k0, k1;
-    float inv_tau;  // 1 / temperature
+    float scale;  // log2(e) / temperature
 };
 
 struct ChainArgs {

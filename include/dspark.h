@@ -150,10 +150,11 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
  *       Philox4x32-10 (Salmon et al., SC 2011) at counter (v / 4, i, r, 0) under the
  *       key (seed & 0xFFFFFFFF, seed >> 32)
  * and the sampled token keys the next position, as in the greedy chain.  The same
- * (seed, inputs) always give the same tokens; use a new seed every step.  Both
- * logarithms use the hardware base-2 logarithm (about 1 ulp), so tokens match an
- * exact evaluation except where two perturbed values are within rounding of each
- * other.  chained_logits (optional) receives x, unperturbed.  temperature must be
+ * (seed, inputs) always give the same tokens; use a new seed every step.  The kernels
+ * rank the equivalent base-2 value x * (log2(e) / temperature) - log2(-log2 u), a
+ * positive affine image of the one above (same argmax), with the hardware base-2
+ * logarithm (about 1 ulp), so tokens match an exact evaluation except where two
+ * perturbed values are within rounding of each other.  chained_logits (optional) receives x, unperturbed.  temperature must be
  * positive and finite with a finite reciprocal (DSPARK_ERANGE otherwise).  Other
  * arguments, limits and the workspace are those of dspark_chain.  The tokens can be
  * scheduled with the stage calls (survival, top-B, budget, allocate with tokens).
