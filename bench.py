@@ -214,6 +214,63 @@ def cooperative_rate(B, run, steps) -> dict:
     return {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1), "steps": steps}
 
 
+def closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, steps) -> dict:
+    """A multi-step synthetic decode loop, all on the device: each iteration runs the step
+    sized from the previous step's confidences (dspark_step_sized), a stand-in for the
+    target model's greedy tokens whose acceptance is drawn from this step's confidences
+    (torch ops: draft j of a request matches with probability c[r, j], the bonus token is
+    uniform), the acceptance lane (dspark_accept_greedy), and keys the next step's chain on
+    the bonus tokens.  Reports the emitted tokens (accepted drafts + one bonus per request)."""
+    import torch
+    R, K, V, n = w.R, w.K, w.V, w.R * w.K
+    P = len(pool)
+    out = B.StepBuffers(R, K, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    prev0 = pool[0][1].clone()
+    acc_len, nxt = torch.empty(R, **i32), torch.empty(R, **i32)
+    target = torch.zeros(n + R + 1, **i32)       # the last entry takes the writes of unused slots
+    emitted = torch.zeros(1, dtype=torch.int64, device=dev)
+    j = torch.arange(n, device=dev)
+    rr = torch.arange(R, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2026)
+
+    def one(k):
+        base, _, conf = pool[k % P]
+        old = pool[(k - 1) % P][2]
+        B.dspark_step_sized(base, A, Bt, w.dtype, prev0, conf, old, B.RULE_ARGMAX, w.n_sampling, w.T, w.R_all,
+                            vc_d, dc_d, out, ws, status)
+        slot = out.ver_idx.long()
+        valid = j < out.b_star.long()
+        slot_c = slot.clamp(min=0)
+        req = slot_c // K
+        c = conf.reshape(-1)[slot_c]
+        u = torch.rand(n, device=dev, generator=gen)
+        other = torch.randint(1, V, (n,), device=dev, generator=gen, dtype=torch.int32)
+        draft = out.ver_tokens
+        answer = torch.where(u < c, draft, torch.remainder(draft + other, V))
+        dst = torch.where(valid, j + req, torch.full_like(j, n + R))
+        target.index_copy_(0, dst, answer)
+        bonus = torch.randint(0, V, (R,), device=dev, generator=gen, dtype=torch.int32)
+        target.index_copy_(0, out.offsets[1:].long() + rr, bonus)
+        B.dspark_accept_greedy(out.ver_tokens, out.offsets, target, R, K, acc_len, nxt, None, status)
+        emitted.add_(acc_len.sum() + R)
+        prev0.copy_(nxt)
+
+    for k in range(5):
+        one(k)
+    emitted.zero_()
+    us = _event_loop_us(one, steps)
+    per_step = float(emitted.item()) / steps
+    log(f"bench: closed loop {us:.1f} us/iteration, {per_step:.1f} emitted tokens per step "
+        f"({per_step / (us * 1e-6) / 1e6:.2f} M tokens/s), status {int(status.item())}")
+    return {"iteration_us": round(us, 2), "steps": steps, "emitted_tokens_per_step": round(per_step, 1),
+            "emitted_tokens_per_s": round(per_step / (us * 1e-6), 1), "status": int(status.item()),
+            "sizing": "one-step-old confidences, argmax rule",
+            "target": "synthetic stand-in (torch): draft j accepted with probability c[r, j]"}
+
+
 def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev) -> dict:
     """Cost tables measured on this GPU at start-up: a proxy verification step (4 bf16
     GEMMs [t, 7168] x [7168, 7168]) over the captured sizes up to the workload's capture
@@ -398,6 +455,7 @@ def main():
                                                min(args.event_steps, 100))
         extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
         extra["cooperative_launch"] = cooperative_rate(B, run, min(args.event_steps, K))
+        extra["closed_loop"] = closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, min(args.event_steps, K))
 
     sb = step_bytes(w)
     ck = chain_kernel(w)
