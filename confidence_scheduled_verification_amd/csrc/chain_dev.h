@@ -689,12 +689,17 @@ __device__ __forceinline__ void grid_arrive(uint32_t* ctr, uint64_t token = 0) {
 // All K positions in one cooperative launch (R <= kReqChunk, gridDim.x <= resident
 // workgroups).  Position pos waits for every workgroup to have published position
 // pos-1; the base ring already holds position pos's first blocks by then.
-// Split of the requests for the persistent schedule: half 0 = [0, H), half 1 =
-// [H, R), H a multiple of one ring cycle (64 requests); a single group when R <= 64.
-__device__ __forceinline__ int half_split(int R) {
+// Split of the requests for the persistent schedule into groups of Hg requests (whole
+// ring cycles of 64), at most kMaxGroups of them; a single group when R <= 64.
+__device__ __forceinline__ int group_rows(int R) {
     if (R <= 64) return R;
-    const int H = ((R + 1) / 2 + 63) / 64 * 64;
-    return H < R ? H : R;
+    const int want = (R + 63) / 64 < kMaxGroups ? (R + 63) / 64 : kMaxGroups;
+    return ((R + want - 1) / want + 63) / 64 * 64;
+}
+
+__device__ __forceinline__ int group_count(int R) {
+    const int Hg = group_rows(R);
+    return Hg > 0 ? (R + Hg - 1) / Hg : 1;
 }
 
 // All K positions of the chain in one launch.  G = the workgroups taking part
@@ -702,12 +707,14 @@ __device__ __forceinline__ int half_split(int R) {
 // first keys are published (the single-launch step kernel zeroes the keys in-launch
 // first).  tokens may be null.
 //
-// With two request halves the halves run out of phase: while a workgroup scores one
-// half, the other half's keys of the previous position finish arriving from every
+// The request groups run out of phase (two by default): while a workgroup scores one
+// group, the next group's keys of the previous position finish arriving from every
 // workgroup, so its barrier wait is (nearly) free; its key rows are gathered
-// asynchronously and its publish atomics overlap that gather.  Per position:
+// asynchronously and its publish atomics overlap that gather.  Per position, two groups:
 //   score h0 | wait h1(p-1), decode h1(p), gather h1 (async), publish h0(p), arrive h0
 //   score h1 | wait h0(p),   decode h0(p+1), gather h0 (async), publish h1(p), arrive h1
+// More groups give the barriers more slack but add a decode-gather-arrive chain per
+// group and position; on the headline shape four groups measured slower than two.
 // Barrier counters: bar[p * kMaxGroups + h].
 template <int KS, bool VEC, bool SAMPLE = false>
 __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16_t* __restrict__ base,
@@ -716,38 +723,38 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
                                                    uint32_t* __restrict__ bar, int32_t* __restrict__ tokens,
                                                    uint32_t* __restrict__ status, int R, int K, int V, int rank,
                                                    int G, const uint32_t* ready, const SampleArgs& smp = SampleArgs{}) {
-    static_assert(kMaxGroups >= 2, "two request halves");
+    static_assert(kMaxGroups >= 2, "at least two request groups");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int vb = blockIdx.x * kTileV + w * kWV;
     bf16x8 bt[kMB][KS];
     load_bt<KS>(bt, Bt, V, rank, vb, lane & 15, lane >> 4);
     BaseFrag pre[kPF];
     prefetch_rows<VEC>(pre, base, R, K, V, 0, 0, vb);
-    // Segments in order: (pos, half) for pos = 0..K-1 and each half.
-    const int H = half_split(R);
-    const bool two = H < R;
-    const int nseg = two ? 2 * K : K;
-    const int RC1 = R - H, rows0 = fast_rows(H), rows1 = two ? fast_rows(RC1) : 0;
-    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, H, 0, rows0);
+    // Segments in order: (pos, group) for pos = 0..K-1 and each group.
+    const int Hg = group_rows(R), ng = group_count(R);
+    const int nseg = ng * K;
+    const int RC0 = Hg < R ? Hg : R;
+    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, RC0, 0, fast_rows(RC0));
     __syncthreads();
-    gather_rows<KS>(L, A, V, rank, H, 0, rows0);
+    gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows(RC0));
     __syncthreads();
     for (int sg = 0; sg < nseg; ++sg) {
-        const int pos = two ? sg >> 1 : sg, h = two ? sg & 1 : 0;
-        const int c0 = h ? H : 0, RC = h ? RC1 : H;
+        const int pos = sg / ng, h = sg - pos * ng;
+        const int c0 = h * Hg, RC = (R - c0) < Hg ? (R - c0) : Hg;
         const int ns = sg + 1;  // the next segment
         const bool more = ns < nseg;
-        const int npos = two ? ns >> 1 : ns, nh = two ? ns & 1 : 0;
-        const int nc0 = nh ? H : 0, nRC = nh ? RC1 : H, nrows = nh ? rows1 : rows0;
+        const int npos = ns / ng, nh = ns - npos * ng;
+        const int nc0 = nh * Hg, nRC = (R - nc0) < Hg ? (R - nc0) : Hg, nrows = fast_rows(nRC);
         score_rows<KS, VEC, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos,
                                     more ? nc0 : c0, smp);
         __syncthreads();
-        if (two) {
+        if (ng > 1) {
             // The key atomics go out first, from the upper half of the waves; their
             // round trip overlaps the next segment's barrier poll, decode and gather
-            // (the next segment's barrier is the other half's, passed by every
-            // workgroup a segment ago), which run in waves 0-1 (at most 128 requests
-            // per half), whose in-order memory-counter waits then exclude the atomics.
+            // (the next segment's barrier is its group's previous position, passed by
+            // every workgroup ng - 1 segments ago), which run in waves 0-1 (at most 128
+            // requests per group), whose in-order memory-counter waits then exclude the
+            // atomics.
             if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
             uint64_t token = 0;
             publish_rows<KS>(L, keys, R, pos, c0, RC, c0, token, kNT / 2);
@@ -761,13 +768,13 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
         } else {
             if (sg == 0 && ready != nullptr) grid_wait(ready, 1u, status);
             uint64_t token = 0;
-            publish_rows<KS>(L, keys, R, pos, 0, H, 0, token);
+            publish_rows<KS>(L, keys, R, pos, 0, RC0, 0, token);
             grid_arrive(&bar[pos * kMaxGroups], token);
             if (more) {
                 grid_wait(&bar[pos * kMaxGroups], (uint32_t)G, status);
-                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, H, 0, rows0);
+                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, RC0, 0, fast_rows(RC0));
                 __syncthreads();
-                gather_rows<KS>(L, A, V, rank, H, 0, rows0);
+                gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows(RC0));
                 __syncthreads();
             }
         }

@@ -19,7 +19,10 @@ namespace dspark {
 // zeroes its keys in-launch and puts its counters and flag back to zero when it ends,
 // so once the workspace was zero-filled one time they are zero at every launch,
 // whatever R and K the earlier calls had.
-constexpr int kMaxGroups = 2;  // request halves of the persistent chain
+#ifndef DSPARK_GROUPS
+#define DSPARK_GROUPS 2
+#endif
+constexpr int kMaxGroups = DSPARK_GROUPS;  // request groups of the persistent chain, out of phase
 constexpr int kMaxSlotsWs = 16384;
 inline size_t ws_round(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t ws_sync_bytes() { return ws_round((size_t)(kMaxSlotsWs * kMaxGroups + 1) * 4); }

@@ -72,9 +72,8 @@ __global__ __launch_bounds__(kNT, 1) void step_single_bf16_kernel(StepArgs a) {
     sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, sz, a.surv, a.order,
                     a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_ver);
     __syncthreads();
-    // each chain workgroup arrives for half 0 before half 1 of a position
-    const int last = half_split(a.R) < a.R ? 1 : 0;
-    grid_wait(&bar[(a.K - 1) * kMaxGroups + last], (uint32_t)G, a.status);
+    // each chain workgroup arrives for the groups of a position in order
+    grid_wait(&bar[(a.K - 1) * kMaxGroups + group_count(a.R) - 1], (uint32_t)G, a.status);
     for (int f = threadIdx.x; f < n; f += kNT) a.tokens[f] = token_of(a.keys, a.R, a.K, f);
     if (a.ver_tokens != nullptr) {
         const int B = sh.b_star;
