@@ -494,12 +494,13 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const Cos
 }
 
 // Stage 5.  sel must already mark the chosen slots (1 byte per flat id, n entries).
-// lds_ver (may be null): an LDS copy of ver_idx[0, B).
+// lds_rows (may be null): per request r, lds_rows[2r] = its offset into ver_idx and
+// lds_rows[2r + 1] = its prefix length.
 template <int NT>
 __device__ __forceinline__ void allocate_lds(SchedShared<NT>& sh, const uint8_t* sel, int R, int K, int B,
                              const int32_t* __restrict__ tokens, int32_t* __restrict__ prefix_len,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ ver_idx,
-                             int32_t* __restrict__ ver_tokens, int32_t* lds_ver = nullptr) {
+                             int32_t* __restrict__ ver_tokens, int32_t* lds_rows = nullptr) {
     const int tid = threadIdx.x;
     const int n = R * K;
     const int CR = (R + NT - 1) / NT;
@@ -521,10 +522,13 @@ __device__ __forceinline__ void allocate_lds(SchedShared<NT>& sh, const uint8_t*
             const int f = r * K + i;
             if (sel[f]) {
                 ver_idx[o + L] = f;
-                if (lds_ver) lds_ver[o + L] = f;
                 if (ver_tokens) ver_tokens[o + L] = tokens[f];
                 ++L;
             }
+        }
+        if (lds_rows) {
+            lds_rows[2 * r] = (int32_t)o;
+            lds_rows[2 * r + 1] = (int32_t)L;
         }
         prefix_len[r] = (int32_t)L;
         o += L;
@@ -558,8 +562,9 @@ struct Sizing {
 
 // Stages 2-5 in sequence: survival (optionally written out), ranking (written out),
 // budget, selection and allocation.  Leaves B* in sh.b_star and the selection map in
-// LDS; every output pointer except the required ones may be null.  lds_ver (may be
-// null, may alias sh.key, which is free by then): an LDS copy of ver_idx[0, B*).
+// LDS; every output pointer except the required ones may be null.  lds_rows (may be
+// null, may alias sh.key, which is free by then): each request's offset and prefix
+// length (see allocate_lds).
 // With a separate sizing array, B is chosen from its survivals first (same survival,
 // ranking and budget code over its slots), capped at R*K, and best_obj is the sizing
 // objective.
@@ -571,7 +576,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
                                            float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
                                            double* __restrict__ best_obj, int32_t* __restrict__ prefix_len,
                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ver_idx,
-                                           uint32_t* status, int32_t* lds_ver = nullptr) {
+                                           uint32_t* status, int32_t* lds_rows = nullptr) {
     const int n = R * K;
     // One or two passes of the same code (a loop, so that the stage code exists once in
     // the kernel): with a separate sizing array, pass 0 sizes B from it and pass 1 ranks
@@ -608,7 +613,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     uint8_t* sel = selection_map<NT>(sh);
     for (int j = threadIdx.x; j < n; j += NT) sel[sh.id[j]] = (uint8_t)(j < B);
     __syncthreads();
-    allocate_lds<NT>(sh, sel, R, K, B, nullptr, prefix_len, offsets, ver_idx, nullptr, lds_ver);
+    allocate_lds<NT>(sh, sel, R, K, B, nullptr, prefix_len, offsets, ver_idx, nullptr, lds_rows);
 }
 
 }  // namespace

@@ -12,12 +12,11 @@
 // The extra workgroup also
 //   * zeroes the argmax keys first and then raises a ready flag, which the chain
 //     workgroups wait for before their first key atomics;
-//   * waits for the chain's last barrier and writes tokens [R, K] and the verified
-//     tokens ver_tokens[j] = tokens[ver_idx[j]] (j < B*, -1 after), both decoded
-//     from the keys with agent-scope loads;
-//   * finally puts the step counters and the flag back to zero, when no chain
-//     workgroup can read them any more (every one has passed its last wait once the
-//     last barrier is full), so the next launch starts from zero.
+//   * waits for the chain's last barrier, puts the step counters and the flag back to
+//     zero (no chain workgroup reads them any more: every one has passed its last wait
+//     once the last barrier is full), so the next launch starts from zero, and writes
+//     tokens [R, K] and the verified tokens ver_tokens[j] = tokens[ver_idx[j]] (j < B*,
+//     -1 after) in one pass over the keys (agent-scope loads).
 // Like the chain's own exchanges, these go through agent-scope atomics that return
 // a value, completed before the flag or counter that publishes them.
 #include "chain_dev.h"
@@ -67,29 +66,28 @@ __global__ __launch_bounds__(kNT, 1) void step_single_bf16_kernel(StepArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // every exchange has returned
     __syncthreads();
     if (threadIdx.x == 0) set_agent_u32(ready, 1u);
-    int32_t* lds_ver = reinterpret_cast<int32_t*>(sh.key);
+    int32_t* lds_rows = reinterpret_cast<int32_t*>(sh.key);  // per request: offset, prefix length
     const Sizing sz{a.sizing.separate, a.sizing.conf, a.sizing.R, a.sizing.bmax, a.sizing.rule};
     sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, sz, a.surv, a.order,
-                    a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_ver);
+                    a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_rows);
     __syncthreads();
     // each chain workgroup arrives for the groups of a position in order
     grid_wait(&bar[(a.K - 1) * kMaxGroups + group_count(a.R) - 1], (uint32_t)G, a.status);
-    for (int f = threadIdx.x; f < n; f += kNT) a.tokens[f] = token_of(a.keys, a.R, a.K, f);
-    if (a.ver_tokens != nullptr) {
-        const int B = sh.b_star;
-        for (int j = threadIdx.x; j < n; j += kNT) {
-            int32_t tok = -1;
-            if (j < B) {
-                const int f = lds_ver[j];
-                if (f >= 0 && f < n) tok = token_of(a.keys, a.R, a.K, f);
-            }
-            a.ver_tokens[j] = tok;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Every chain workgroup has passed its last wait: the counters and the flag go back
+    // to zero for the next launch, while the tokens are decoded.
     for (int p = threadIdx.x; p < a.K * kMaxGroups; p += kNT) set_agent_u32(&bar[p], 0u);
     if (threadIdx.x == 0) set_agent_u32(ready, 0u);
+    // One pass over the keys: tokens[r, i], and ver_tokens[offset_r + i] for the i below
+    // request r's prefix length (the verified slots are each request's first ones).
+    const int B = sh.b_star;
+    for (int f = threadIdx.x; f < n; f += kNT) {
+        const int r = f / a.K, i = f - r * a.K;
+        const int32_t tok = token_of(a.keys, a.R, a.K, f);
+        a.tokens[f] = tok;
+        if (a.ver_tokens != nullptr && i < lds_rows[2 * r + 1]) a.ver_tokens[lds_rows[2 * r] + i] = tok;
+    }
+    if (a.ver_tokens != nullptr)
+        for (int j = B + threadIdx.x; j < n; j += kNT) a.ver_tokens[j] = -1;
 }
 
 template <int KS, bool VEC>
