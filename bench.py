@@ -44,7 +44,7 @@ def step_bytes(w) -> dict:
 
 def chain_kernel(w) -> dict:
     """The dominant kernel of the step and its algorithmic bytes per launch.  bf16 with
-    R <= 256 runs the whole step in one cooperative launch (step_single_bf16_kernel):
+    R <= 256 runs the whole step in one launch of a resident grid (step_single_bf16_kernel):
     every base logit once, the second factor once, the K*R gathered key rows, the keys
     written and read back, the confidences, cost-table entries and every output once.
     Otherwise one chain launch per position moves its base slice, the whole second

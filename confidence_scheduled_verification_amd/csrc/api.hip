@@ -247,7 +247,7 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
                                     std::min((int)ns, verify_len - 1 - T), rule};
     hipError_t e;
     if (n > 0 && dtype == DSPARK_BF16) {
-        // One cooperative launch for the whole step when it fits on the device.
+        // One launch for the whole step when its grid fits on the device at once.
         char* w = (char*)ws;
         dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status,
                             (uint64_t*)(w + dspark::ws_sync_bytes()), (uint32_t*)w, conf,

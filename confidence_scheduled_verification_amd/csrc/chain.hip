@@ -25,7 +25,7 @@
 //     by one 64-bit atomicMax per request per workgroup (skipped when the stored
 //     key is already larger).
 //   * Persistent form (the default when the tiles fit on the CUs at once): ONE
-//     cooperative launch runs all K positions.  Bt stays in registers for the
+//     launch of a resident grid runs all K positions.  Bt stays in registers for the
 //     whole step (read from memory once instead of K times), and positions are
 //     separated by grid barriers on counters in the workspace.  Requests are
 //     split into two groups whose phases alternate, so a group's barrier wait

@@ -686,7 +686,7 @@ __device__ __forceinline__ void grid_arrive(uint32_t* ctr, uint64_t token = 0) {
     if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// All K positions in one cooperative launch (R <= kReqChunk, gridDim.x <= resident
+// All K positions in one launch of a resident grid (R <= kReqChunk, gridDim.x <= resident
 // workgroups).  Position pos waits for every workgroup to have published position
 // pos-1; the base ring already holds position pos's first blocks by then.
 // Split of the requests for the persistent schedule into groups of Hg requests (whole

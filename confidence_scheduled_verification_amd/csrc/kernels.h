@@ -100,7 +100,7 @@ struct FusedSchedArgs {
     int ws_words;    // its size in uint64 words
 };
 
-// Everything of one step in a single cooperative launch: the chain on one
+// Everything of one step in a single launch: the chain on one
 // workgroup per vocabulary tile plus one workgroup that runs stages 2-5 and writes
 // tokens and ver_tokens once the chain is done.
 struct StepArgs {

@@ -1,4 +1,4 @@
-// The whole chain-and-schedule step in ONE cooperative launch.
+// The whole chain-and-schedule step in ONE launch of a resident grid.
 //
 // Stages 2-5 (survival, ranking, budget, allocation; vLLM blog "Adaptive
 // Verification in vLLM", sections "Scheduling the budget" and "The cost model")
