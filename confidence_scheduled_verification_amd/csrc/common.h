@@ -59,18 +59,27 @@ __device__ __forceinline__ void publish_key(uint64_t* p, uint64_t k) {
     }
 }
 
+// a ^ b ^ c in one instruction: gfx950's three-input bitwise operation with the truth
+// table of a three-way exclusive or (0x96); c is wave-uniform.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(__builtin_amdgcn_readfirstlane(c)));
+    return r;
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
 // 1, 2, 3", SC 2011): ten rounds of the Philox S-box over the counter (c0, c1, c2, c3)
 // under the key (k0, k1), the key advanced by the two Weyl constants between rounds.
-// Each round's two 32x32 -> 64-bit products are one multiply-add each.
+// Each round's two 32x32 -> 64-bit products are one multiply-add each and its two
+// three-way exclusive ors one instruction each.
 __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                               uint32_t k1, uint32_t (&out)[4]) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
