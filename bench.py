@@ -24,6 +24,8 @@ if ROOT not in sys.path:
 
 METRIC = "chain+schedule steps/sec at R=256,K=7,V=129280,r=256; % HBM roofline; sched µs"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+FP32_VECTOR_PEAK_TFLOPS = 157.3     # fp32 vector
 
 
 def log(msg):
@@ -42,7 +44,7 @@ def step_bytes(w) -> dict:
     return d
 
 
-def chain_kernel(w) -> dict:
+def chain_kernel(w, num_cu: int = 256) -> dict:
     """The dominant kernel of the step and its algorithmic bytes per launch.  bf16 with
     R <= 256 runs the whole step in one launch of a resident grid (step_single_bf16_kernel):
     every base logit once, the second factor once, the K*R gathered key rows, the keys
@@ -50,7 +52,8 @@ def chain_kernel(w) -> dict:
     Otherwise one chain launch per position moves its base slice, the whole second
     factor, its R key rows and keys."""
     e = 2 if w.dtype == 1 else 4
-    if w.dtype == 1 and w.R <= 256:
+    tiles = (w.V + 511) // 512  # one 512-entry vocabulary tile per workgroup, one workgroup per CU
+    if w.dtype == 1 and w.R <= 256 and tiles + 1 <= num_cu:
         b = step_bytes(w)["total"] + w.R * w.K * 8 * 2
         return {"kernel": "step_single_bf16_kernel", "bytes_per_launch": b, "launches_per_step": 1}
     b = w.R * w.V * e + w.V * w.rank * e + w.R * w.rank * e + w.R * (8 * 2 + 4)
@@ -79,6 +82,20 @@ def traffic_per_launch(kernel: str):
     return int(round(rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]))
 
 
+def host_info() -> dict:
+    """The host the oracle is timed on: its logical CPU count and model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpus": os.cpu_count(), "host_cpu_model": model}
+
+
 def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
     """The oracle as it stands, timed on this host: the chain of `rows` requests (all
     positions, whole vocabulary) scaled to R requests, plus the full schedule."""
@@ -92,7 +109,7 @@ def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
     sched.schedule(step_in["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
     t_sched = time.perf_counter() - t0
     per_step = t_chain * (w.R / rows) + t_sched
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle", **host_info(),
             "sample": f"fp64 chain of {rows} of {w.R} requests (all {w.K} positions, V={w.V}) timed "
                       f"{t_chain:.2f} s and scaled x{w.R / rows:.0f}; schedule of all {w.R * w.K} slots "
                       f"timed {t_sched:.2f} s; single-threaded"}
@@ -198,6 +215,80 @@ def sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, steps) -> dict:
     return {"step_us": round(us, 2), "steps": steps, "temperature": 1.0,
             "entries_per_s": round(elems / (us * 1e-6), 1), "philox_calls_per_step": elems // 4,
             "parity_row0": "ok" if ok else "MISMATCH"}
+
+
+def sched_kernel_us(B, pool, w, vc_d, dc_d, dev, calls) -> float:
+    """Stages 2-5 alone (dspark_schedule: one 1024-thread workgroup) on the pool's
+    confidences; mean microseconds per call.  Inside the single-launch step the same work
+    runs on a 512-thread workgroup beside the chain."""
+    import torch
+    out = B.StepBuffers(w.R, w.K, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    P = len(pool)
+
+    def run(k):
+        B.dspark_schedule(pool[k % P][-1], w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, status=st)
+
+    for k in range(5):
+        run(k)
+    us = _event_loop_us(run, calls)
+    log(f"bench: schedule kernel alone {us:.1f} us per call")
+    return round(us, 2)
+
+
+def sched_only(args, w, B, inputs, osched, dev):
+    """Scheduler-only workload (no chain): one step = dspark_schedule over all R*K slots."""
+    import torch
+    log(f"bench: scheduler-only workload {w.name} R={w.R} K={w.K} ({w.R * w.K} slots)")
+    ins = inputs.generate(w)
+    vc = B.dspark_force_monotone(ins.verify_cost_raw)
+    dc = B.dspark_force_monotone(ins.draft_cost_raw)
+    vc_d, dc_d = torch.from_numpy(vc).to(dev), torch.from_numpy(dc).to(dev)
+    host = [inputs.generate_step(w, k) for k in range(args.pool)]
+    pool = [(torch.from_numpy(h["conf"]).to(dev),) for h in host]
+    out = B.StepBuffers(w.R, w.K, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(k):
+        B.dspark_schedule(pool[k % len(pool)][0], w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, status=status)
+
+    for k in range(args.warmup):
+        run(k)
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        run(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = _event_loop_us(run, min(args.event_steps, K))
+    # the last call of the event loop wrote `out`
+    want = osched.schedule(host[(min(args.event_steps, K) - 1) % len(pool)]["conf"], w.n_sampling, w.T, w.R_all,
+                           vc, dc)
+    ok = (int(out.b_star.item()) == want["b_star"] and float(out.best_obj.item()) == want["best_obj"]
+          and np.array_equal(out.ver_idx.cpu().numpy(), want["ver_idx"])
+          and np.array_equal(out.order.cpu().numpy(), want["order"]))
+    n = w.R * w.K
+    bmax = min(n, w.verify_len - 1 - w.T)
+    nbytes = n * 4 + (bmax + 1) * 4 + 4 + n * 4 * 4 + w.R * 4 + (w.R + 1) * 4 + 12
+    ach = nbytes / (us * 1e-6) / 1e9
+    res = {"metric": "schedule steps/sec (stages 2-5 alone)", "value": round(K / wall, 2), "unit": "steps/s",
+           "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: R={w.R}, K={w.K} ({n} slots), T={w.T}, N_sampling={w.n_sampling}"},
+           "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 6), "traffic": None, "kernel": "sched_fused_kernel",
+                        "bytes_per_launch": nbytes, "launch_us": round(us, 2),
+                        "note": "one workgroup out of LDS; bound by its sort and scan latency, not by HBM"},
+           "sched_kernel_us": round(us, 2), "parity_last_step": "ok" if ok else "MISMATCH",
+           "status": int(status.item())}
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        osched.schedule(host[0]["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 1.0 / t, "unit": "steps/s", "cores": 1, "kind": "oracle", **host_info(),
+                               "sample": f"the whole schedule of {n} slots, timed {t:.2f} s; single-threaded"}
+    print(json.dumps(res), flush=True)
 
 
 def cooperative_rate(B, run, steps) -> dict:
@@ -308,7 +399,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="headline", choices=["tiny", "small", "mid", "headline", "large"])
+    ap.add_argument("--workload", default="headline", choices=["tiny", "small", "mid", "headline", "large", "sweep"])
     ap.add_argument("--pool", type=int, default=4, help="distinct per-step input sets cycled through")
     ap.add_argument("--cpu-rows", type=int, default=128, help="requests in the oracle's timed chain sample")
     ap.add_argument("--event-steps", type=int, default=200,
@@ -349,6 +440,8 @@ def main():
         print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
+    if not w.has_chain:
+        return sched_only(args, w, B, inputs, osched, dev)
     log(f"bench: workload {w.name} R={w.R} K={w.K} V={w.V} rank={w.rank}; generating inputs")
     ins = inputs.generate(w)
     vc = B.dspark_force_monotone(ins.verify_cost_raw)
@@ -445,6 +538,7 @@ def main():
     parity = "ok" if ok else "MISMATCH"
     log(f"bench: parity of the last step: {parity}")
 
+    sched_us = sched_kernel_us(B, pool, w, vc_d, dc_d, dev, min(args.event_steps, K))
     extra = None
     if not args.no_variants:
         extra = {"accept_greedy": accept_lane(w, B, inputs, out, st, dev)}
@@ -458,12 +552,19 @@ def main():
         extra["closed_loop"] = closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, min(args.event_steps, K))
 
     sb = step_bytes(w)
-    ck = chain_kernel(w)
+    ck = chain_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count)
     launch_s = chain_ms.mean() * 1e-3 / ck["launches_per_step"]   # event-timed chain phase per launch
     achieved = ck["bytes_per_launch"] / launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ck["kernel"]), **ck,
                 "launch_us": round(launch_s * 1e6, 2)}
+    # the contraction on the matrix cores (bf16) or the vector FMA units (fp32 factors)
+    flops = 2.0 * w.R * w.K * w.V * w.rank
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == 1 else FP32_VECTOR_PEAK_TFLOPS
+    mfma_tf = flops / (chain_ms.mean() * 1e-3) / 1e12
+    compute = {"unit": "TFLOP/s", "flops_per_step": flops, "achieved": round(mfma_tf, 1), "peak": mfma_peak,
+               "frac": round(mfma_tf / mfma_peak, 4),
+               "engine": "bf16 MFMA" if w.dtype == 1 else "fp32 vector FMA"}
     ms_per_step = wall * 1e3 / K
     res = {
         "metric": METRIC,
@@ -482,6 +583,8 @@ def main():
                                f"N_sampling={w.n_sampling}", "input_pool": len(pool),
                    "launch": "resident (plain launch of a grid that fits the device; one stream)"},
         "roofline": roofline,
+        "compute": compute,
+        "sched_kernel_us": sched_us,
         "step_bytes": sb["total"],
         "step_hbm_frac": round(sb["total"] / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "step_us_loop_events": round(loop_ms * 1e3 / K, 2),

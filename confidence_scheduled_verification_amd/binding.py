@@ -32,7 +32,7 @@ RULE_FIRST_DROP = 1
 
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
            "dspark_chain", "dspark_chain_sample", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
-           "dspark_step", "dspark_step_sized", "dspark_accept_greedy", "dspark_set_timing_events",
+           "dspark_step", "dspark_step_sized", "dspark_schedule", "dspark_accept_greedy", "dspark_set_timing_events",
            "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table", "dspark_set_launch_mode",
            "dspark_get_launch_mode"]
 
@@ -77,6 +77,7 @@ def lib():
         L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, i, i, p, i, p, i, p, p, p, p,
                                         p, p, p, p, p, p, p, p, sz, p]
         L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
+        L.dspark_schedule.argtypes = [p, i, i, p, i, i, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p, p, p, p, p]
         L.dspark_set_timing_events.argtypes = [p, p]
         L.dspark_set_launch_mode.argtypes = [i]
         L.dspark_get_launch_mode.argtypes = []
@@ -222,6 +223,26 @@ def dspark_step(base, A, Bt, dtype: int, prev0, conf, n_sampling: int, T: int, n
                              _p(out.tokens), _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
                              _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
                              _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+
+
+def dspark_schedule(conf, n_sampling: int, T: int, num_reqs: int, verify_cost, draft_cost, out: "StepBuffers",
+                    size_conf=None, rule: int = RULE_ARGMAX, tokens=None, status=None, stream=None):
+    """Stages 2-5 alone (one kernel) into `out` (its tokens buffer is not touched;
+    ver_tokens is filled from `tokens` when given)."""
+    R, K = conf.shape
+    size_R = -1
+    if size_conf is not None:
+        if size_conf.dim() != 2 or size_conf.shape[1] != K:
+            raise ValueError("dspark_schedule: size_conf must be [R', K]")
+        size_R = size_conf.shape[0]
+    if tokens is not None and tuple(tokens.shape) != (R, K):
+        raise ValueError("dspark_schedule: tokens must be [R, K]")
+    _contig(conf, size_conf, verify_cost, draft_cost, tokens)
+    _check(lib().dspark_schedule(_p(conf), R, K, _p(size_conf), size_R, rule, n_sampling, T, num_reqs,
+                                 _p(verify_cost), verify_cost.numel(), _p(draft_cost), draft_cost.numel(),
+                                 _p(tokens), _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
+                                 _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
+                                 _p(out.ver_tokens) if tokens is not None else None, _p(status), _stream(stream)))
 
 
 def dspark_step_sized(base, A, Bt, dtype: int, prev0, conf, size_conf, rule: int, n_sampling: int, T: int,

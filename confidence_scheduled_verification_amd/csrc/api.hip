@@ -311,6 +311,37 @@ int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, cons
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "accept_greedy");
 }
 
+int dspark_schedule(const float* conf, int R, int K, const float* size_conf, int size_R, int rule, int n_sampling,
+                    int T, int num_reqs, const float* verify_cost, int verify_len, const float* draft_cost,
+                    int draft_len, const int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                    int32_t* b_star, double* best_obj, int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx,
+                    int32_t* ver_tokens, uint32_t* status, void* stream) {
+    if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "schedule: negative R (%d) or K (%d)", R, K);
+    const long long n = (long long)R * K;
+    if (n > DSPARK_MAX_SLOTS) return fail(DSPARK_EUNSUPPORTED, "schedule: %lld slots exceed %d", n, DSPARK_MAX_SLOTS);
+    if (!b_star || !best_obj || !offsets || (R > 0 && !prefix_len) || (n > 0 && (!ver_idx || !conf)))
+        return fail(DSPARK_EINVAL, "schedule: a required pointer is NULL");
+    if (ver_tokens && !tokens) return fail(DSPARK_EINVAL, "schedule: ver_tokens needs tokens");
+    if (rule != DSPARK_RULE_ARGMAX && rule != DSPARK_RULE_FIRST_DROP)
+        return fail(DSPARK_EINVAL, "schedule: unknown admission rule %d", rule);
+    if (size_R < -1) return fail(DSPARK_EINVAL, "schedule: size_R %d < -1", size_R);
+    const bool stale = size_R >= 0;
+    const long long ns = stale ? (long long)size_R * K : n;
+    if (ns > DSPARK_MAX_SLOTS)
+        return fail(DSPARK_EUNSUPPORTED, "schedule: %lld sizing slots exceed %d", ns, DSPARK_MAX_SLOTS);
+    if (stale && ns > 0 && !size_conf) return fail(DSPARK_EINVAL, "schedule: NULL size_conf with %d rows", size_R);
+    int rc = check_sched_scalars((int)n, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
+    if (rc != DSPARK_OK) return rc;
+    const int bmax = std::min((int)n, verify_len - 1 - T);
+    const dspark::SizingArgs sizing{stale ? 1 : 0, size_conf, stale ? size_R : R,
+                                    std::min((int)ns, verify_len - 1 - T), rule};
+    dspark::FusedSchedArgs sa{conf,       R,     K,       n_sampling, T,          num_reqs, verify_cost, draft_cost,
+                              bmax,       sizing, surv,   order,      sorted_surv, b_star,  best_obj,    prefix_len,
+                              offsets,    ver_idx, status, nullptr,   0,           tokens,  ver_tokens};
+    const hipError_t e = dspark::launch_sched_fused(sa, (hipStream_t)stream);
+    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "schedule");
+}
+
 int dspark_set_launch_mode(int mode) {
     if (mode != DSPARK_LAUNCH_RESIDENT && mode != DSPARK_LAUNCH_COOPERATIVE)
         return fail(DSPARK_EINVAL, "set_launch_mode: unknown mode %d", mode);

@@ -96,8 +96,10 @@ struct FusedSchedArgs {
     int32_t* offsets;
     int32_t* ver_idx;
     uint32_t* status;
-    uint64_t* ws;    // chain workspace to zero (keys and barrier counters)
+    uint64_t* ws;    // chain workspace to zero (keys and barrier counters), or null
     int ws_words;    // its size in uint64 words
+    const int32_t* tokens = nullptr;  // draft tokens for ver_tokens, or null
+    int32_t* ver_tokens = nullptr;    // verified tokens, or null
 };
 
 // Everything of one step in a single launch: the chain on one

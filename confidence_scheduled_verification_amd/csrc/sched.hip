@@ -18,14 +18,15 @@ __global__ __launch_bounds__(kST, 1) void sched_fused_kernel(
     const float* __restrict__ vc, const float* __restrict__ dc, int bmax, SizingArgs sizing, float* __restrict__ surv_out,
     int32_t* __restrict__ order, float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
     double* __restrict__ best_obj, int32_t* __restrict__ prefix_len, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ ver_idx, uint32_t* status, uint64_t* __restrict__ ws, int ws_words) {
+    int32_t* __restrict__ ver_idx, uint32_t* status, uint64_t* __restrict__ ws, int ws_words,
+    const int32_t* __restrict__ tokens, int32_t* __restrict__ ver_tokens) {
     __shared__ SchedShared<kST> sh;
     // The chain's workspace (argmax keys, barrier counters) starts from zero; this launch
     // precedes the chain kernels on the stream.
     for (int j = threadIdx.x; j < ws_words; j += kST) ws[j] = 0ull;
     const Sizing sz{sizing.separate, sizing.conf, sizing.R, sizing.bmax, sizing.rule};
     sched_pass<kST>(sh, conf, R, K, n_sampling, T, num_reqs, vc, dc, bmax, sz, surv_out, order, sorted_surv, b_star,
-                    best_obj, prefix_len, offsets, ver_idx, status);
+                    best_obj, prefix_len, offsets, ver_idx, status, nullptr, tokens, ver_tokens);
 }
 
 __global__ __launch_bounds__(256) void survival_kernel(const float* __restrict__ conf, int R, int K,
@@ -125,7 +126,7 @@ hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, i
 hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sched_fused_kernel, dim3(1), dim3(kST), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T,
                        a.num_reqs, a.vc, a.dc, a.bmax, a.sizing, a.surv, a.order, a.sorted_surv, a.b_star, a.best_obj,
-                       a.prefix_len, a.offsets, a.ver_idx, a.status, a.ws, a.ws_words);
+                       a.prefix_len, a.offsets, a.ver_idx, a.status, a.ws, a.ws_words, a.tokens, a.ver_tokens);
     return hipGetLastError();
 }
 

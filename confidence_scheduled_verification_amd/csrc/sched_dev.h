@@ -564,7 +564,8 @@ struct Sizing {
 // budget, selection and allocation.  Leaves B* in sh.b_star and the selection map in
 // LDS; every output pointer except the required ones may be null.  lds_rows (may be
 // null, may alias sh.key, which is free by then): each request's offset and prefix
-// length (see allocate_lds).
+// length (see allocate_lds).  tokens and ver_tokens (may be null): the draft tokens and
+// the verified-token output of allocate_lds.
 // With a separate sizing array, B is chosen from its survivals first (same survival,
 // ranking and budget code over its slots), capped at R*K, and best_obj is the sizing
 // objective.
@@ -576,7 +577,9 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
                                            float* __restrict__ sorted_surv, int32_t* __restrict__ b_star,
                                            double* __restrict__ best_obj, int32_t* __restrict__ prefix_len,
                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ver_idx,
-                                           uint32_t* status, int32_t* lds_rows = nullptr) {
+                                           uint32_t* status, int32_t* lds_rows = nullptr,
+                                           const int32_t* __restrict__ tokens = nullptr,
+                                           int32_t* __restrict__ ver_tokens = nullptr) {
     const int n = R * K;
     // One or two passes of the same code (a loop, so that the stage code exists once in
     // the kernel): with a separate sizing array, pass 0 sizes B from it and pass 1 ranks
@@ -613,7 +616,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     uint8_t* sel = selection_map<NT>(sh);
     for (int j = threadIdx.x; j < n; j += NT) sel[sh.id[j]] = (uint8_t)(j < B);
     __syncthreads();
-    allocate_lds<NT>(sh, sel, R, K, B, nullptr, prefix_len, offsets, ver_idx, nullptr, lds_rows);
+    allocate_lds<NT>(sh, sel, R, K, B, tokens, prefix_len, offsets, ver_idx, ver_tokens, lds_rows);
 }
 
 }  // namespace

@@ -251,6 +251,26 @@ int dspark_step(const void* base, const void* A, const void* Bt, int dtype, cons
                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stages 2-5 alone, in one kernel (one workgroup of 1024 threads working out of LDS):
+ * survival, global top-B, the budget under `rule` (optionally sized from another
+ * confidence array, as in dspark_step_sized) and the allocation, with no host
+ * read-back (vLLM blog, "Scheduling the budget").  For a step whose drafts come from
+ * elsewhere, and for scheduler-only batches (up to DSPARK_MAX_SLOTS slots, e.g.
+ * 1024 requests x 15 positions).
+ *   conf [R,K] fp32; size_conf / size_R / rule as in dspark_step_sized (size_R = -1:
+ *   size from conf); scalars and tables as in dspark_choose_budget;
+ *   tokens [R,K] int32 draft tokens or NULL; outputs as in dspark_step (surv, order,
+ *   sorted_surv and ver_tokens may be NULL; ver_tokens needs tokens).
+ */
+int dspark_schedule(const float* conf, int R, int K, const float* size_conf, int size_R, int rule,
+                    int n_sampling, int T, int num_reqs,
+                    const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                    const int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                    int32_t* b_star, double* best_obj,
+                    int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                    uint32_t* status, void* stream);
+
+/*
  * dspark_step with the budget sized from a separate confidence array and a chosen
  * admission rule (vLLM blog, "Scheduling the budget": B is sized from a
  * double-buffered confidence array one step old, while the slots are handed to the

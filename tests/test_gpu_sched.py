@@ -196,3 +196,33 @@ def test_budget_rules_match_the_oracle(rule):
         differ += wb != sched.choose_budget(ss, ns, T, nr, vc, dc)[0]
     if rule == B.RULE_FIRST_DROP:
         assert differ >= 3
+
+
+@pytest.mark.parametrize("rule", [B.RULE_ARGMAX, B.RULE_FIRST_DROP])
+@pytest.mark.parametrize("name", ["tiny", "small", "mid", "headline", "large", "sweep"])
+def test_fused_schedule_entry_point(name, rule):
+    # dspark_schedule: stages 2-5 in one kernel, on every workload's slots (the sweep is
+    # 1024 requests x 15 positions), with verified tokens, then sized from another array.
+    w = inputs.WORKLOADS[name]
+    rng = np.random.default_rng(w.seed + 40)
+    conf = inputs._confidences(w, rng)
+    vc = sched.force_monotone(inputs.raw_verify_cost(w, np.random.default_rng(w.seed)))
+    dc = sched.force_monotone(inputs.raw_draft_cost(w))
+    R, K = conf.shape
+    tokens = rng.integers(0, 50000, size=(R, K)).astype(np.int32)
+    out = B.StepBuffers(R, K)
+    status = torch.zeros(1, dtype=torch.int32, device=gu.DEV)
+    args = (w.n_sampling, w.T, w.R_all, gu.to_dev(vc), gu.to_dev(dc), out)
+    B.dspark_schedule(gu.to_dev(conf), *args, rule=rule, tokens=gu.to_dev(tokens), status=status)
+    torch.cuda.synchronize()
+    got = gu.step_numpy(out)
+    want = sched.schedule(conf, w.n_sampling, w.T, w.R_all, vc, dc, tokens=tokens, rule=rule)
+    gu.assert_sched_parity(got, want, R, K)
+    assert int(status.item()) == want["status"] == 0
+    old = inputs._confidences(w, np.random.default_rng(w.seed + 41))
+    B.dspark_schedule(gu.to_dev(conf), *args, size_conf=gu.to_dev(old), rule=rule, status=status)
+    torch.cuda.synchronize()
+    got = gu.step_numpy(out)
+    got["ver_tokens"] = None
+    want = sched.schedule(conf, w.n_sampling, w.T, w.R_all, vc, dc, size_conf=old, rule=rule)
+    gu.assert_sched_parity(got, want, R, K)

@@ -134,6 +134,13 @@ def test_schedule_argument_checks_return_before_launch():
     for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
         assert L.dspark_chain_sample(p, p, p, 1, p, 4, 7, 1024, 256, t, 1, p, None, None, p, 1 << 20, None) == -2
     assert L.dspark_chain_sample(p, p, p, 1, p, 0, 7, 1024, 256, 1.0, 1, p, None, None, None, 0, None) == 0
+    # the fused schedule: too many slots, ver_tokens without tokens, unknown rule
+    assert L.dspark_schedule(p, 2000, 9, None, -1, 0, 4, 0, 4, p, 65, p, 257, None, None, None, None, p, p, p, p, p,
+                             None, None, None) == -3
+    assert L.dspark_schedule(p, 4, 7, None, -1, 0, 4, 0, 4, p, 65, p, 257, None, None, None, None, p, p, p, p, p,
+                             p, None, None) == -1
+    assert L.dspark_schedule(p, 4, 7, None, -1, 5, 4, 0, 4, p, 65, p, 257, None, None, None, None, p, p, p, p, p,
+                             None, None, None) == -1
     # launch mode: default resident, unknown modes rejected
     assert L.dspark_get_launch_mode() == 0
     assert L.dspark_set_launch_mode(7) == -1 and L.dspark_get_launch_mode() == 0
