@@ -46,16 +46,19 @@ def step_bytes(w) -> dict:
 
 def chain_kernel(w, num_cu: int = 256) -> dict:
     """The dominant kernel of the step and its algorithmic bytes per launch.  bf16 with
-    R <= 256 runs the whole step in one launch of a resident grid (step_single_bf16_kernel):
-    every base logit once, the second factor once, the K*R gathered key rows, the keys
-    written and read back, the confidences, cost-table entries and every output once.
-    Otherwise one chain launch per position moves its base slice, the whole second
-    factor, its R key rows and keys."""
+    R <= 256, and fp32 with R <= 64 and rank <= 64, run the whole step in one launch of a
+    resident grid (step_single_bf16_kernel, step_single_f32_kernel): every base logit
+    once, the second factor once, the K*R gathered key rows, the keys written and read
+    back, the confidences, cost-table entries and every output once.  Otherwise one chain
+    launch per position moves its base slice, the whole second factor, its R key rows and
+    keys."""
     e = 2 if w.dtype == 1 else 4
     tiles = (w.V + 511) // 512  # one 512-entry vocabulary tile per workgroup, one workgroup per CU
-    if w.dtype == 1 and w.R <= 256 and tiles + 1 <= num_cu:
+    single = (w.R <= 256) if w.dtype == 1 else (w.R <= 64 and w.rank <= 64)
+    if single and tiles + 1 <= num_cu:
         b = step_bytes(w)["total"] + w.R * w.K * 8 * 2
-        return {"kernel": "step_single_bf16_kernel", "bytes_per_launch": b, "launches_per_step": 1}
+        name = "step_single_bf16_kernel" if w.dtype == 1 else "step_single_f32_kernel"
+        return {"kernel": name, "bytes_per_launch": b, "launches_per_step": 1}
     b = w.R * w.V * e + w.V * w.rank * e + w.R * w.rank * e + w.R * (8 * 2 + 4)
     name = "chain_pos_bf16_kernel" if w.dtype == 1 else "chain_pos_f32_kernel"
     return {"kernel": name, "bytes_per_launch": b, "launches_per_step": w.K}

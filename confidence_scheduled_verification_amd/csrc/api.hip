@@ -246,8 +246,9 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
     const dspark::SizingArgs sizing{stale ? 1 : 0, size_conf, stale ? size_R : R,
                                     std::min((int)ns, verify_len - 1 - T), rule};
     hipError_t e;
-    if (n > 0 && dtype == DSPARK_BF16) {
-        // One launch for the whole step when its grid fits on the device at once.
+    if (n > 0) {
+        // One launch for the whole step when its grid fits on the device at once (fp32
+        // factors: small batches only).
         char* w = (char*)ws;
         dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status,
                             (uint64_t*)(w + dspark::ws_sync_bytes()), (uint32_t*)w, conf,
@@ -256,7 +257,7 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
                             coop_launch()};
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
-        e = dspark::launch_step_single(st, s);
+        e = dtype == DSPARK_BF16 ? dspark::launch_step_single(st, s) : dspark::launch_step_single_f32(st, s);
         if (e == hipSuccess) {
             if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
                 return hip_fail(e, "step (timing event)");

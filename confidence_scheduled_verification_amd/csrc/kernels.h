@@ -145,6 +145,9 @@ int chain_tile_vocab();
 // hipErrorCooperativeLaunchTooLarge (nothing enqueued) and the caller runs the
 // stage-wise launches.
 hipError_t launch_step_single(const StepArgs& a, hipStream_t s);
+// fp32 factors, R <= 64 and rank <= 64: the same single launch (chain workgroups +
+// scheduling workgroup).
+hipError_t launch_step_single_f32(const StepArgs& a, hipStream_t s);
 hipError_t launch_zero_keys(uint64_t* keys, size_t n, hipStream_t s);
 hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s);
 hipError_t launch_chain_finalize(const uint64_t* keys, int32_t* tokens, int R, int K, const int32_t* ver_idx,

@@ -240,6 +240,11 @@ int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, c
  * `surv`, `order`, `sorted_surv`, `prefix_len`, `offsets`, `ver_idx`, `ver_tokens`
  * and `best_obj` are outputs (surv, order, sorted_surv may be NULL).
  * conf holds R rows (the drafting requests), R*K <= DSPARK_MAX_SLOTS.
+ * It runs as ONE kernel launch when the grid fits on the device at once (one
+ * workgroup per 512 vocabulary entries plus one scheduling workgroup): bf16 with
+ * R <= 256, and fp32 with R <= 64 and rank <= 64 (with the whole vocabulary in one
+ * workgroup, V <= 2048 and rank <= 16, positions need no device-wide barrier);
+ * otherwise as the stage-wise launches.  Results are the same either way.
  */
 int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
                 int R, int K, int V, int rank,
