@@ -158,8 +158,10 @@ struct SchedShared {
     int32_t b_star;
 };
 
-// Exclusive scan of one uint32 per thread over the block.
-template <int NT>
+// Exclusive scan of one uint32 per thread over the block.  TRAIL: end with a barrier so
+// that the next call may reuse sh.wsum at once (callers with barriers of their own in
+// between pass false).
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_scan(SchedShared<NT>& sh, uint32_t v, uint32_t* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t x = v;
@@ -176,7 +178,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(SchedShared<NT>& sh, uint32_
         if (q < w) off += s;
         tot += s;
     }
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     if (total) *total = tot;
     return off + x - v;
 }
@@ -277,7 +279,11 @@ __device__ __forceinline__ void surv_global_to_lds(SchedShared<NT>& sh, const fl
 // One stable counting pass over the 8-bit digit at `shift`.  Wave w owns items
 // [w*S, (w+1)*S) of the current order, 64 per round; an item's rank among equal
 // digits of its wave comes from a ballot match of the digit bits and a running
-// per-(digit, wave) counter.
+// per-(digit, wave) counter.  Entered after a barrier that follows the last writes of
+// the keys (the previous pass's scatter, or the survival stage).  A wave's counter
+// column is written and read by that wave alone until the barrier before the offset
+// scan, so clearing it needs no barrier of its own; the scan's scratch is not written
+// again before this pass's later barriers, so it needs no trailing one either.
 template <int NT>
 __device__ __forceinline__ void radix_pass(SchedShared<NT>& sh, int n_pad, int shift) {
     constexpr int kSW = NT / 64, JM = kMaxN / NT;
@@ -295,7 +301,6 @@ __device__ __forceinline__ void radix_pass(SchedShared<NT>& sh, int n_pad, int s
             il[j] = sh.id[p];
         }
     }
-    __syncthreads();
     const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
@@ -324,7 +329,7 @@ __device__ __forceinline__ void radix_pass(SchedShared<NT>& sh, int n_pad, int s
         c[q] = sh.hist[hist_at<NT>(e / kSW, e % kSW)];
         s += c[q];
     }
-    uint32_t ex = block_excl_scan<NT>(sh, s, nullptr);
+    uint32_t ex = block_excl_scan<NT, false>(sh, s, nullptr);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
@@ -592,12 +597,18 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
         const float* src = sz.separate && sizing ? sz.conf : conf;
         const int rows = sz.separate && sizing ? sz.R : R;
         const int m = rows * K, m_pad = pad_slots<NT>(m);
+        const int bm = sz.separate ? sz.bmax : bmax;
+        // The cost-table entries are requested before the ranking where the registers
+        // allow (up to 512 threads), so their memory round trip overlaps the confidences'
+        // and the sort; with more threads, after the sort (overlapping the write-out and
+        // the exact scan).
+        constexpr bool kEarly = NT <= 512;
+        CostPrefetch<NT> cp;
+        if (kEarly && sizing) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
         survival_to_lds<NT>(sh, src, rows, K, m_pad, last ? surv_out : nullptr, status);
         sort_slots<NT>(sh, m_pad);
         if (sizing) {
-            const int bm = sz.separate ? sz.bmax : bmax;
-            CostPrefetch<NT> cp;  // requested here so the loads overlap the write-out and the exact scan
-            prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
+            if (!kEarly) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
             if (last) write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
             choose_budget_lds<NT>(sh, cp, m, m_pad, n_sampling, bm, sz.rule, last ? b_star : nullptr, best_obj,
                                   nullptr, status);
