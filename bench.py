@@ -438,7 +438,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the chain-and-schedule step has "
-                                   "no multi-GPU path in this build (see DESIGN.md for how it would shard)",
+                                   "no multi-GPU path (it would shard by requests, which are independent, "
+                                   "or by vocabulary, with one 64-bit max all-reduce of the keys per position)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -8,7 +8,7 @@ the capture range a step of t tokens runs (and pays for) the smallest captured
 graph that holds it, so the table is a staircase; past the capture limit the cost
 is continuous; and the finished table is forced monotone.
 
-Readings (each one is also listed in the design doc):
+Readings:
   * the median of an even number of runs is the mean of the two middle ones
     (computed in double);
   * shapes <= graph_max are the captured graph sizes and must include graph_max;

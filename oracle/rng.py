@@ -11,7 +11,7 @@ with the key bumped by two Weyl constants between rounds.  One implementation fo
 both word widths: at 64 bits it must reproduce numpy's Philox bit generator (which
 is Philox4x64-10), and the draft sampler uses the 32-bit generator Philox4x32-10.
 
-Draft sampling (readings, also listed in the design doc): the drafted token at (r, i)
+Draft sampling (readings): the drafted token at (r, i)
 is a sample from softmax(x / temperature) over the chained logits x (the vLLM blog's
 benchmark runs at temperature 1.0, "Results"), drawn by the Gumbel-max rule:
 argmax_v x[v] / temperature + g[v] with g[v] = -log(-log u[v]).  u[v] comes from

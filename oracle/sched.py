@@ -7,7 +7,7 @@ Plain Python loops over plain numbers: float32 products through numpy scalars,
 sums of survivals as exact rationals (``fractions.Fraction``), IEEE double
 division through Python floats.
 
-Readings of what the pages leave open (each one is also listed in the design doc):
+Readings of what the pages leave open:
   * survival is the inclusive running product s[r,i] = c[r,0] * ... * c[r,i]
     (the confidence is the chance a token survives given that all before it
     were accepted -- DSpark summary, "Verify smarter" -- so s[r,i] is the chance

@@ -11,7 +11,7 @@ bonus token of the budget's numerator (vLLM blog "Adaptive Verification in
 vLLM", section "Scheduling the budget") -- which is the target's token right
 after the accepted run, and which the next step's chain is keyed on.
 
-Layout readings (each one is also listed in the design doc):
+Layout readings:
   * request r's verified drafts are ver_tokens[offsets[r] .. offsets[r+1]), the
     compacted list of the allocation stage, L_r = offsets[r+1] - offsets[r];
   * the target pass runs 1 + L_r tokens per request (the last accepted token and
