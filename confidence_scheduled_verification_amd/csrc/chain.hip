@@ -83,14 +83,14 @@ __global__ __launch_bounds__(kNT, 1) void chain_pos_bf16_kernel(
 
 // All K positions in one launch of a resident grid (R <= kReqChunk, gridDim.x <= resident
 // workgroups).  SAMPLE: tokens drawn by Gumbel-max (probabilistic drafting).
-template <int KS, bool VEC, bool SAMPLE>
+template <int KS, bool VEC, bool SAMPLE, int PF>
 __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
     const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, uint32_t* __restrict__ bar,
     int32_t* __restrict__ tokens, uint32_t* __restrict__ status, int R, int K, int V, int rank, SampleArgs smp) {
     __shared__ __attribute__((aligned(16))) ChainLds<KS> L;
-    chain_persist_body<KS, VEC, SAMPLE>(L, base, A, Bt, prev0, keys, bar, tokens, status, R, K, V, rank,
-                                        (int)gridDim.x, nullptr, smp);
+    chain_persist_body<KS, VEC, SAMPLE, PF>(L, base, A, Bt, prev0, keys, bar, tokens, status, R, K, V, rank,
+                                            (int)gridDim.x, nullptr, smp);
 }
 
 // fp32 factors: one thread per vocabulary entry, fused multiply-add in increasing k.
@@ -184,9 +184,9 @@ __global__ void transpose_kernel(const T* __restrict__ src, int rows, int cols, 
 // workgroup per CU (the LDS footprint allows no more), so the grid must not exceed
 // the CUs reported by the occupancy query.  Returns hipErrorCooperativeLaunchTooLarge
 // when it does not fit; the caller then launches per position.
-template <int KS, bool VEC, bool SAMPLE>
+template <int KS, bool VEC, bool SAMPLE, int PF>
 hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
-    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC, SAMPLE>;
+    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC, SAMPLE, PF>;
     static int resident[64] = {0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -210,7 +210,7 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
     int R = a.R, K = a.K, V = a.V, rank = a.rank;
     SampleArgs smp = a.smp;
     if (!a.coop) {
-        hipLaunchKernelGGL((chain_persist_bf16_kernel<KS, VEC, SAMPLE>), dim3(grid), dim3(kNT), 0, s, base, A, Bt,
+        hipLaunchKernelGGL((chain_persist_bf16_kernel<KS, VEC, SAMPLE, PF>), dim3(grid), dim3(kNT), 0, s, base, A, Bt,
                            prev0, keys, bar, tokens, status, R, K, V, rank, smp);
         return hipGetLastError();
     }
@@ -221,7 +221,13 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
 template <int KS, bool VEC>
 hipError_t launch_bf16(const ChainArgs& a, int grid, hipStream_t s) {
     if (a.R <= kReqChunk && a.logits == nullptr) {
-        const hipError_t e = a.smp.on ? launch_persist<KS, VEC, true>(a, grid, s) : launch_persist<KS, VEC, false>(a, grid, s);
+        // A single group of at most 64 requests sweeps whole 2-block ring cycles (the full
+        // rank only; other ranks keep the 4-block ring).
+        hipError_t e;
+        if (KS == 8 && a.R <= 64)
+            e = a.smp.on ? launch_persist<KS, VEC, true, 2>(a, grid, s) : launch_persist<KS, VEC, false, 2>(a, grid, s);
+        else
+            e = a.smp.on ? launch_persist<KS, VEC, true, kPF>(a, grid, s) : launch_persist<KS, VEC, false, kPF>(a, grid, s);
         if (e != hipErrorCooperativeLaunchTooLarge) return e;
         (void)hipGetLastError();  // clear the sticky launch error before falling back
     }

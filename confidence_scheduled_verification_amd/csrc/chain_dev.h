@@ -173,10 +173,14 @@ __device__ __forceinline__ int phase_tid() {
 // Requests [c0, c0+RC) use LDS rows l0 .. l0+RC; rows RC .. `rows` (the padded
 // count the scoring form works on) hold zero key rows and are never published.
 
-// Rows the pipelined scorer sweeps: whole ring cycles of kPF blocks of 16.
+// Rows the pipelined scorer sweeps: whole ring cycles of PF blocks of 16 (PF base
+// blocks in flight per wave: kPF, or 2 for a single group of at most 64 requests, where
+// a 4-block ring would sweep padding rows -- 32 requests in a 64-row cycle).
 static_assert(kPF % 2 == 0 && kReqChunk % (16 * kPF) == 0, "ring cycles must tile an LDS chunk of requests");
+template <int PF = kPF>
 __device__ __forceinline__ int fast_rows(int RC) {
-    constexpr int C = 16 * kPF;
+    static_assert(PF % 2 == 0 && kReqChunk % (16 * PF) == 0, "ring cycles must tile an LDS chunk of requests");
+    constexpr int C = 16 * PF;
     return (RC + C - 1) / C * C;
 }
 
@@ -523,17 +527,17 @@ __device__ __forceinline__ void block_argmax(const f32x4 (&acc)[kMB], uint64_t* 
 // full when the next call starts.  The sweep covers fast_rows(RC) rows (whole ring
 // cycles); blocks past RC score zero key rows into keys never published.
 // Returns the wave's NaN mask (nonzero: rescore exactly).
-template <int KS, bool VEC, bool TAIL, bool SAMPLE>
-__device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
+template <int KS, bool VEC, bool TAIL, bool SAMPLE, int PF>
+__device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[PF],
                                                const uint16_t* __restrict__ base, int R, int K, int V, int pos,
                                                int c0, int RC, int l0, int vb, int npos, int nc0,
                                                const SampleArgs& smp) {
-    constexpr int LROW = ChainLds<KS>::LROW, PF = kPF;
+    constexpr int LROW = ChainLds<KS>::LROW;
     static_assert(PF % 2 == 0, "the two accumulator sets alternate within a ring cycle");
     const int lane = threadIdx.x & 63;
     const int n16 = lane & 15, g = lane >> 4;
     const int vlane = vb + 8 * g;
-    const int nB = fast_rows(RC) >> 4;  // a multiple of PF
+    const int nB = fast_rows<PF>(RC) >> 4;  // a multiple of PF
     const uint16_t* arow = L.a + (l0 + n16) * LROW + g * 8;
     uint64_t* best = L.best + l0 + n16;
     uint64_t nan_mask = 0ull;
@@ -615,16 +619,16 @@ __device__ __forceinline__ void score_exact(ChainLds<KS>& L, const bf16x8 (&bt)[
 // Score dispatch without logits output: the pipelined form; waves wholly past V
 // have nothing to score; a NaN seen by the fast form triggers an exact rescore of
 // the wave (its keys only ever raise the stored ones).
-template <int KS, bool VEC, bool SAMPLE = false>
-__device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[kPF],
+template <int KS, bool VEC, bool SAMPLE = false, int PF = kPF>
+__device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[PF],
                                            const uint16_t* __restrict__ base, int R, int K, int V, int pos, int c0,
                                            int RC, int l0, int vb, int npos, int nc0,
                                            const SampleArgs& smp = SampleArgs{}) {
     if (vb >= V) return;
     const uint64_t nan_mask =
         (vb + kWV > V)
-            ? score_fast<KS, VEC, true, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp)
-            : score_fast<KS, VEC, false, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp);
+            ? score_fast<KS, VEC, true, SAMPLE, PF>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp)
+            : score_fast<KS, VEC, false, SAMPLE, PF>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp);
     if (nan_mask != 0ull) score_exact<KS, VEC, SAMPLE>(L, bt, base, R, K, V, pos, c0, RC, l0, vb, smp);
 }
 
@@ -646,16 +650,16 @@ __device__ __forceinline__ void publish_rows(const ChainLds<KS>& L, uint64_t* ke
     }
 }
 
-// First kPF base blocks of segment (pos, c0) into the ring (rows past R clamp).
-template <bool VEC>
-__device__ __forceinline__ void prefetch_rows(BaseFrag (&pre)[kPF], const uint16_t* __restrict__ base, int R, int K,
+// First PF base blocks of segment (pos, c0) into the ring (rows past R clamp).
+template <bool VEC, int PF = kPF>
+__device__ __forceinline__ void prefetch_rows(BaseFrag (&pre)[PF], const uint16_t* __restrict__ base, int R, int K,
                                               int V, int pos, int c0, int vb) {
     const int lane = threadIdx.x & 63;
     const int n16 = lane & 15, vlane = vb + 8 * (lane >> 4);
     const BaseSrc src = base_src(base, R, K, V, n16, vlane);
     const __amdgpu_buffer_rsrc_t rs = seg_rsrc(src, c0, pos, K, V);
 #pragma unroll
-    for (int q = 0; q < kPF; ++q) load_block<VEC>(pre[q], src, rs, q, c0, pos, R, K, V, n16, vlane);
+    for (int q = 0; q < PF; ++q) load_block<VEC>(pre[q], src, rs, q, c0, pos, R, K, V, n16, vlane);
 }
 
 // Grid barrier.  Everything workgroups exchange inside the launch -- the argmax keys
@@ -716,7 +720,7 @@ __device__ __forceinline__ int group_count(int R) {
 // More groups give the barriers more slack but add a decode-gather-arrive chain per
 // group and position; on the headline shape four groups measured slower than two.
 // Barrier counters: bar[p * kMaxGroups + h].
-template <int KS, bool VEC, bool SAMPLE = false>
+template <int KS, bool VEC, bool SAMPLE = false, int PF = kPF>
 __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16_t* __restrict__ base,
                                                    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
                                                    const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys,
@@ -728,15 +732,15 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
     const int vb = blockIdx.x * kTileV + w * kWV;
     bf16x8 bt[kMB][KS];
     load_bt<KS>(bt, Bt, V, rank, vb, lane & 15, lane >> 4);
-    BaseFrag pre[kPF];
-    prefetch_rows<VEC>(pre, base, R, K, V, 0, 0, vb);
+    BaseFrag pre[PF];
+    prefetch_rows<VEC, PF>(pre, base, R, K, V, 0, 0, vb);
     // Segments in order: (pos, group) for pos = 0..K-1 and each group.
     const int Hg = group_rows(R), ng = group_count(R);
     const int nseg = ng * K;
     const int RC0 = Hg < R ? Hg : R;
-    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, RC0, 0, fast_rows(RC0));
+    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, RC0, 0, fast_rows<PF>(RC0));
     __syncthreads();
-    gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows(RC0));
+    gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows<PF>(RC0));
     __syncthreads();
     for (int sg = 0; sg < nseg; ++sg) {
         const int pos = sg / ng, h = sg - pos * ng;
@@ -744,8 +748,8 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
         const int ns = sg + 1;  // the next segment
         const bool more = ns < nseg;
         const int npos = ns / ng, nh = ns - npos * ng;
-        const int nc0 = nh * Hg, nRC = (R - nc0) < Hg ? (R - nc0) : Hg, nrows = fast_rows(nRC);
-        score_rows<KS, VEC, SAMPLE>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos,
+        const int nc0 = nh * Hg, nRC = (R - nc0) < Hg ? (R - nc0) : Hg, nrows = fast_rows<PF>(nRC);
+        score_rows<KS, VEC, SAMPLE, PF>(L, bt, pre, base, R, K, V, pos, c0, RC, c0, vb, more ? npos : pos,
                                     more ? nc0 : c0, smp);
         __syncthreads();
         if (ng > 1) {
@@ -772,9 +776,9 @@ __device__ __forceinline__ void chain_persist_body(ChainLds<KS>& L, const uint16
             grid_arrive(&bar[pos * kMaxGroups], token);
             if (more) {
                 grid_wait(&bar[pos * kMaxGroups], (uint32_t)G, status);
-                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, RC0, 0, fast_rows(RC0));
+                decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, npos, 0, RC0, 0, fast_rows<PF>(RC0));
                 __syncthreads();
-                gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows(RC0));
+                gather_rows<KS>(L, A, V, rank, RC0, 0, fast_rows<PF>(RC0));
                 __syncthreads();
             }
         }

@@ -83,12 +83,12 @@ __device__ __forceinline__ void step_schedule_wg(const StepArgs& a, unsigned cha
         for (int j = B + threadIdx.x; j < n; j += kNT) a.ver_tokens[j] = -1;
 }
 
-template <int KS, bool VEC>
+template <int KS, bool VEC, int PF>
 __global__ __launch_bounds__(kNT, 1) void step_single_bf16_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[StepLds<KS>::kBytes];
     const int G = (int)gridDim.x - 1;  // chain workgroups
     if ((int)blockIdx.x < G) {
-        chain_persist_body<KS, VEC>(*reinterpret_cast<ChainLds<KS>*>(smem), (const uint16_t*)a.base,
+        chain_persist_body<KS, VEC, false, PF>(*reinterpret_cast<ChainLds<KS>*>(smem), (const uint16_t*)a.base,
                                     (const uint16_t*)a.A, (const uint16_t*)a.Bt, a.prev0, a.keys, a.sync, nullptr,
                                     a.status, a.R, a.K, a.V, a.rank, G, a.sync + a.K * kMaxGroups);
         return;
@@ -240,8 +240,14 @@ hipError_t launch_resident(const void* fn, int* resident, const StepArgs& a, int
 
 template <int KS, bool VEC>
 hipError_t launch_single(const StepArgs& a, int grid, hipStream_t s) {
+    // A single group of at most 64 requests sweeps whole 2-block ring cycles (the full
+    // rank only; other ranks keep the 4-block ring).
+    if (KS == 8 && a.R <= 64) {
+        static int resident[64] = {0};
+        return launch_resident((const void*)step_single_bf16_kernel<KS, VEC, 2>, resident, a, grid, s);
+    }
     static int resident[64] = {0};
-    return launch_resident((const void*)step_single_bf16_kernel<KS, VEC>, resident, a, grid, s);
+    return launch_resident((const void*)step_single_bf16_kernel<KS, VEC, kPF>, resident, a, grid, s);
 }
 
 template <int KS>

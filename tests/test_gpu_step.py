@@ -147,3 +147,24 @@ def test_launch_modes_give_identical_results(name):
         assert np.array_equal(np.asarray(res[k]), np.asarray(coop[k])), k
     np.testing.assert_array_equal(tok_r.cpu().numpy(), tok_c.cpu().numpy())
     np.testing.assert_array_equal(tok_r.cpu().numpy(), res["tokens"])
+
+
+@pytest.mark.parametrize("R", [1, 17, 33, 64, 65])
+def test_ring_depth_boundaries(R):
+    # Up to 64 requests at the full rank the chain sweeps 2-block base rings (one group);
+    # from 65 on, 4-block rings in two groups.  Both must give the oracle's tokens, the same
+    # tokens through the step and the chain entry point, and the oracle's schedule.
+    K, V, rank = 3, 3001, 256
+    c = inputs.random_case(900 + R, R=R, K=K, V=V, rank=rank, dtype=inputs.BF16)
+    rng = np.random.default_rng(R)
+    vc = np.maximum.accumulate(80.0 + 0.7 * np.arange(R * K + 64) + rng.normal(0, 0.4, R * K + 64)).astype(np.float32)
+    dc = np.maximum.accumulate(9.0 + 0.3 * np.arange(R + 1)).astype(np.float32)
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    got, status, _ = gu.run_step(ch, c["conf"], R, 0, R, vc, dc)
+    assert status == 0
+    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    tok, _, st = ch.run()
+    assert st == 0
+    np.testing.assert_array_equal(tok.cpu().numpy(), got["tokens"])
+    want = sched.schedule(c["conf"], R, 0, R, vc, dc, tokens=got["tokens"])
+    gu.assert_sched_parity(got, want, R, K)
