@@ -59,6 +59,14 @@ def chain_kernel(w, num_cu: int = 256) -> dict:
         b = step_bytes(w)["total"] + w.R * w.K * 8 * 2
         name = "step_single_bf16_kernel" if w.dtype == 1 else "step_single_f32_kernel"
         return {"kernel": name, "bytes_per_launch": b, "launches_per_step": 1}
+    if w.dtype == 1 and (w.R <= 256 and tiles <= num_cu or w.R <= 64 and tiles <= 2 * num_cu):
+        # the whole chain in one launch (two vocabulary tiles per workgroup past num_cu
+        # tiles); the schedule runs in its own launch.  Algorithmic bytes: base, both
+        # factors' used rows and the keys once, though the two-tile form reads half of the
+        # second factor again at every position after the first.
+        b = (w.R * w.K * w.V * e + w.V * w.rank * e + w.R * w.K * w.rank * e + w.R * 4 + w.R * w.K * (8 * 2 + 4))
+        name = "chain_persist_bf16_kernel" if tiles <= num_cu else "chain_persist2_bf16_kernel"
+        return {"kernel": name, "bytes_per_launch": b, "launches_per_step": 1}
     b = w.R * w.V * e + w.V * w.rank * e + w.R * w.rank * e + w.R * (8 * 2 + 4)
     name = "chain_pos_bf16_kernel" if w.dtype == 1 else "chain_pos_f32_kernel"
     return {"kernel": name, "bytes_per_launch": b, "launches_per_step": w.K}

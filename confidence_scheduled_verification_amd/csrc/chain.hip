@@ -93,6 +93,67 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
                                             (int)gridDim.x, nullptr, smp);
 }
 
+// Two vocabulary tiles per workgroup, for vocabularies with more tiles than the CUs
+// hold at once (up to twice as many): workgroup b owns tiles b and b + G.  The
+// registers hold one tile's second-factor rows, so each position scores the tile
+// already held, then loads the other tile's rows and scores it, and the order flips
+// every position (b, b+G | b+G, b | b, b+G ...): the tile scored last at one position
+// is scored first at the next.  A position then reads half of the second factor from
+// memory instead of all of it, and the K positions are one launch with grid barriers
+// instead of K launches.  One request group (R <= 64): the key rows are gathered once
+// per position for both tiles, and each request's key goes out once per workgroup.
+template <int KS, bool VEC, int PF>
+__global__ __launch_bounds__(kNT, 1) void chain_persist2_bf16_kernel(
+    const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
+    const int32_t* __restrict__ prev0, uint64_t* __restrict__ keys, uint32_t* __restrict__ bar,
+    int32_t* __restrict__ tokens, uint32_t* __restrict__ status, int R, int K, int V, int rank) {
+    __shared__ __attribute__((aligned(16))) ChainLds<KS> L;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int G = (int)gridDim.x;
+    const int vb0 = (int)blockIdx.x * kTileV + w * kWV, vb1 = ((int)blockIdx.x + G) * kTileV + w * kWV;
+    const int rows = fast_rows<PF>(R);
+    decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, R, 0, rows);
+    __syncthreads();
+    gather_rows<KS, false>(L, A, V, rank, R, 0, rows);
+    bf16x8 bt[kMB][KS];
+    load_bt<KS>(bt, Bt, V, rank, vb0, lane & 15, lane >> 4);
+    BaseFrag pre[PF];
+    prefetch_rows<VEC, PF>(pre, base, R, K, V, 0, 0, vb0);
+    int ring_pos = 0, ring_vb = vb0;  // the ring holds the first blocks of (position, wave slice)
+    __builtin_amdgcn_s_waitcnt(0);    // this wave's gather slots have landed
+    __syncthreads();
+    for (int pos = 0; pos < K; ++pos) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool second = ((pos + h) & 1) != 0;
+            const int vb = second ? vb1 : vb0;
+            if (h == 1) load_bt<KS>(bt, Bt, V, rank, vb, lane & 15, lane >> 4);
+            // the next slice this wave scores: the other tile at this position, else this
+            // tile at the next position
+            const int npos = h == 0 ? pos : (pos + 1 < K ? pos + 1 : pos);
+            const int nvb = h == 0 ? (second ? vb0 : vb1) : vb;
+            if (vb < V) {
+                if (ring_pos != pos || ring_vb != vb) prefetch_rows<VEC, PF>(pre, base, R, K, V, pos, 0, vb);
+                score_rows<KS, VEC, false, PF, true>(L, bt, pre, base, R, K, V, pos, 0, R, 0, vb, npos, 0,
+                                                     SampleArgs{}, nvb);
+                ring_pos = npos;
+                ring_vb = nvb;
+            }
+        }
+        __syncthreads();
+        uint64_t token = 0;
+        publish_rows<KS>(L, keys, R, pos, 0, R, 0, token);
+        grid_arrive(&bar[pos * kMaxGroups], token);
+        if (pos + 1 < K) {
+            grid_wait(&bar[pos * kMaxGroups], (uint32_t)G, status);
+            decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, pos + 1, 0, R, 0, rows);
+            __syncthreads();
+            gather_rows<KS>(L, A, V, rank, R, 0, rows);
+            __syncthreads();
+        }
+    }
+}
+
 // fp32 factors: one thread per vocabulary entry, fused multiply-add in increasing k.
 __global__ __launch_bounds__(kF32Threads) void chain_pos_f32_kernel(
     const float* __restrict__ base, const float* __restrict__ A, const float* __restrict__ Bt,
@@ -184,10 +245,9 @@ __global__ void transpose_kernel(const T* __restrict__ src, int rows, int cols, 
 // workgroup per CU (the LDS footprint allows no more), so the grid must not exceed
 // the CUs reported by the occupancy query.  Returns hipErrorCooperativeLaunchTooLarge
 // when it does not fit; the caller then launches per position.
-template <int KS, bool VEC, bool SAMPLE, int PF>
-hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
-    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC, SAMPLE, PF>;
-    static int resident[64] = {0};
+// hipSuccess when a grid of `grid` workgroups of `fn` fits on the current device at
+// once (cached per device and kernel instantiation through `resident`).
+hipError_t check_resident(const void* fn, int (&resident)[64], int grid) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -198,7 +258,15 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         resident[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
     }
-    if (grid > resident[dev]) return hipErrorCooperativeLaunchTooLarge;
+    return grid > resident[dev] ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
+}
+
+template <int KS, bool VEC, bool SAMPLE, int PF>
+hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
+    const void* fn = (const void*)chain_persist_bf16_kernel<KS, VEC, SAMPLE, PF>;
+    static int resident[64] = {0};
+    hipError_t e = check_resident(fn, resident, grid);
+    if (e != hipSuccess) return e;
     const uint16_t* base = (const uint16_t*)a.base;
     const uint16_t* A = (const uint16_t*)a.A;
     const uint16_t* Bt = (const uint16_t*)a.Bt;
@@ -218,6 +286,30 @@ hipError_t launch_persist(const ChainArgs& a, int grid, hipStream_t s) {
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, 0, s);
 }
 
+template <int KS, bool VEC, int PF>
+hipError_t launch_persist2(const ChainArgs& a, int grid, hipStream_t s) {
+    const void* fn = (const void*)chain_persist2_bf16_kernel<KS, VEC, PF>;
+    static int resident[64] = {0};
+    hipError_t e = check_resident(fn, resident, grid);
+    if (e != hipSuccess) return e;
+    const uint16_t* base = (const uint16_t*)a.base;
+    const uint16_t* A = (const uint16_t*)a.A;
+    const uint16_t* Bt = (const uint16_t*)a.Bt;
+    const int32_t* prev0 = a.prev0;
+    uint64_t* keys = a.keys;
+    uint32_t* bar = a.bar;
+    int32_t* tokens = a.tokens;
+    uint32_t* status = a.status;
+    int R = a.R, K = a.K, V = a.V, rank = a.rank;
+    if (!a.coop) {
+        hipLaunchKernelGGL((chain_persist2_bf16_kernel<KS, VEC, PF>), dim3(grid), dim3(kNT), 0, s, base, A, Bt, prev0,
+                           keys, bar, tokens, status, R, K, V, rank);
+        return hipGetLastError();
+    }
+    void* args[] = {&base, &A, &Bt, &prev0, &keys, &bar, &tokens, &status, &R, &K, &V, &rank};
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, 0, s);
+}
+
 template <int KS, bool VEC>
 hipError_t launch_bf16(const ChainArgs& a, int grid, hipStream_t s) {
     if (a.R <= kReqChunk && a.logits == nullptr) {
@@ -230,6 +322,12 @@ hipError_t launch_bf16(const ChainArgs& a, int grid, hipStream_t s) {
             e = a.smp.on ? launch_persist<KS, VEC, true, kPF>(a, grid, s) : launch_persist<KS, VEC, false, kPF>(a, grid, s);
         if (e != hipErrorCooperativeLaunchTooLarge) return e;
         (void)hipGetLastError();  // clear the sticky launch error before falling back
+        if (a.R <= 64 && !a.smp.on) {  // one request group, greedy: two tiles per workgroup
+            e = KS == 8 ? launch_persist2<KS, VEC, 2>(a, (grid + 1) / 2, s)
+                        : launch_persist2<KS, VEC, kPF>(a, (grid + 1) / 2, s);
+            if (e != hipErrorCooperativeLaunchTooLarge) return e;
+            (void)hipGetLastError();
+        }
     }
     for (int pos = 0; pos < a.K; ++pos) {
         if (a.smp.on)

@@ -524,14 +524,15 @@ __device__ __forceinline__ void block_argmax(const f32x4 (&acc)[kMB], uint64_t* 
 // kPF-slot register ring; slot b % kPF is refilled, unconditionally, right after
 // block b is taken from it, with the block kPF further on -- past this segment's
 // last block that is the next segment's (npos, nc0) first blocks, so the ring is
-// full when the next call starts.  The sweep covers fast_rows(RC) rows (whole ring
-// cycles); blocks past RC score zero key rows into keys never published.
-// Returns the wave's NaN mask (nonzero: rescore exactly).
-template <int KS, bool VEC, bool TAIL, bool SAMPLE, int PF>
+// full when the next call starts.  XT: the next segment belongs to another
+// vocabulary tile, whose wave slice starts at nvb.  The sweep covers fast_rows(RC)
+// rows (whole ring cycles); blocks past RC score zero key rows into keys never
+// published.  Returns the wave's NaN mask (nonzero: rescore exactly).
+template <int KS, bool VEC, bool TAIL, bool SAMPLE, int PF, bool XT = false>
 __device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[PF],
                                                const uint16_t* __restrict__ base, int R, int K, int V, int pos,
                                                int c0, int RC, int l0, int vb, int npos, int nc0,
-                                               const SampleArgs& smp) {
+                                               const SampleArgs& smp, int nvb = 0) {
     constexpr int LROW = ChainLds<KS>::LROW;
     static_assert(PF % 2 == 0, "the two accumulator sets alternate within a ring cycle");
     const int lane = threadIdx.x & 63;
@@ -542,12 +543,14 @@ __device__ __forceinline__ uint64_t score_fast(ChainLds<KS>& L, const bf16x8 (&b
     uint64_t* best = L.best + l0 + n16;
     uint64_t nan_mask = 0ull;
     const BaseSrc src = base_src(base, R, K, V, n16, vlane);
+    const int nvlane = XT ? nvb + 8 * g : vlane;
+    const BaseSrc src_n = XT ? base_src(base, R, K, V, n16, nvlane) : src;
     const __amdgpu_buffer_rsrc_t rs_cur = seg_rsrc(src, c0, pos, K, V), rs_nxt = seg_rsrc(src, nc0, npos, K, V);
     // refill of the slot just emptied with ring block t (t >= PF)
     auto refill = [&](BaseFrag& f, int t) {
         const bool next = t >= nB;
-        load_block<VEC>(f, src, next ? rs_nxt : rs_cur, next ? t - nB : t, next ? nc0 : c0, next ? npos : pos, R, K,
-                        V, n16, vlane);
+        load_block<VEC>(f, next ? src_n : src, next ? rs_nxt : rs_cur, next ? t - nB : t, next ? nc0 : c0,
+                        next ? npos : pos, R, K, V, n16, next ? nvlane : vlane);
     };
     f32x4 acc[2][kMB];
     init_acc<TAIL, VEC>(acc[0], pre[0], vlane, V);
@@ -619,16 +622,18 @@ __device__ __forceinline__ void score_exact(ChainLds<KS>& L, const bf16x8 (&bt)[
 // Score dispatch without logits output: the pipelined form; waves wholly past V
 // have nothing to score; a NaN seen by the fast form triggers an exact rescore of
 // the wave (its keys only ever raise the stored ones).
-template <int KS, bool VEC, bool SAMPLE = false, int PF = kPF>
+template <int KS, bool VEC, bool SAMPLE = false, int PF = kPF, bool XT = false>
 __device__ __forceinline__ void score_rows(ChainLds<KS>& L, const bf16x8 (&bt)[kMB][KS], BaseFrag (&pre)[PF],
                                            const uint16_t* __restrict__ base, int R, int K, int V, int pos, int c0,
                                            int RC, int l0, int vb, int npos, int nc0,
-                                           const SampleArgs& smp = SampleArgs{}) {
+                                           const SampleArgs& smp = SampleArgs{}, int nvb = 0) {
     if (vb >= V) return;
     const uint64_t nan_mask =
         (vb + kWV > V)
-            ? score_fast<KS, VEC, true, SAMPLE, PF>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp)
-            : score_fast<KS, VEC, false, SAMPLE, PF>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0, smp);
+            ? score_fast<KS, VEC, true, SAMPLE, PF, XT>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0,
+                                                        smp, nvb)
+            : score_fast<KS, VEC, false, SAMPLE, PF, XT>(L, bt, pre, base, R, K, V, pos, c0, RC, l0, vb, npos, nc0,
+                                                         smp, nvb);
     if (nan_mask != 0ull) score_exact<KS, VEC, SAMPLE>(L, bt, base, R, K, V, pos, c0, RC, l0, vb, smp);
 }
 

@@ -192,3 +192,52 @@ def test_fast_scorer_special_values_match_numpy_argmax(R, V):
     ch = gu.Chain(base, A, Bmat, inputs.BF16, prev0)
     tok, _, _ = ch.run()
     np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))
+
+
+# Vocabularies with more 512-entry tiles than the CUs hold at once (over 131072 entries on
+# 256 CUs) and one request group (R <= 64) run two tiles per workgroup in one launch, the
+# tile order flipping every position.  Shapes: ragged last tile, V not a multiple of 8, an
+# odd tile count (the last workgroup's second tile is empty), ranks below 256.
+@pytest.mark.parametrize("R,K,V,rank,rows", [
+    (40, 5, 140000, 256, [0, 17, 39]),
+    (64, 4, 133635, 256, [1, 63]),
+    (7, 6, 131372, 128, None),
+    (33, 3, 262144, 64, [0, 32]),
+])
+def test_two_tile_chain_parity(R, K, V, rank, rows):
+    c = _case(400 + R + K, R, K, V, rank, inputs.BF16)
+    gu.say(f"two-tile chain bf16 R={R} K={K} V={V} rank={rank}")
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    tok, _, st = ch.run()
+    assert st == 0
+    gu.assert_chain_parity(tok.cpu().numpy(), None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"], rows=rows)
+    tok2, _, _ = ch.run()
+    assert torch.equal(tok, tok2)
+
+
+def test_two_tile_chain_special_values_match_numpy_argmax():
+    # Bmat = 0: every position is numpy's argmax of its base row; NaNs (the exact rescore),
+    # infinities and ties sit in both tiles of a workgroup and in the empty-tile workgroup.
+    R, K, V, rank = 10, 3, 131372, 32
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((R, K, V)).astype(np.float32)
+    x[0, 0, 5] = np.nan
+    x[0, 0, V - 1] = np.nan
+    x[1, 1, 131000] = np.nan
+    x[2, 2, :] = -np.inf
+    x[3, 0, V - 2] = np.inf
+    x[3, 0, V - 1] = np.inf
+    x[4, 1, 200] = 40.0
+    x[4, 1, 131100] = 40.0
+    x[5, 2, 66000] = 30.0
+    base = inputs.round_to_bf16(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+    base[np.isnan(x)] = 0x7FC0
+    base[np.isposinf(x)] = 0x7F80
+    base[np.isneginf(x)] = 0xFF80
+    ref = inputs.bf16_to_f32(base)
+    A = inputs.round_to_bf16(np.ones((V, rank), dtype=np.float32))
+    Bmat = inputs.round_to_bf16(np.zeros((rank, V), dtype=np.float32))
+    prev0 = rng.integers(0, V, size=R, dtype=np.int32)
+    ch = gu.Chain(base, A, Bmat, inputs.BF16, prev0)
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))
