@@ -125,10 +125,11 @@ def test_single_launch_step_at_the_slot_limit():
     assert 0 < got["b_star"] < R * K
 
 
-@pytest.mark.parametrize("name", ["small", "headline"])
+@pytest.mark.parametrize("name", ["small", "headline", "large"])
 def test_launch_modes_give_identical_results(name):
     # The persistent kernels run as a plain launch of a resident grid (default) or as a
     # cooperative launch; the work is the same, so every output must match bit for bit.
+    # Large runs the two-tile chain beside a separate schedule launch.
     w = inputs.WORKLOADS[name]
     ins = inputs.generate(w)
     vc, dc = gu.forced_tables(w, ins)
