@@ -408,40 +408,21 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[kMB], const bf16x8 (&bt)
     }
 }
 
-// Pairwise exchanges between lane l and lane l^16 / l^32 (gfx950 lane-swap
-// instructions); both results of a swap are {own, partner} in some order, so a
-// symmetric combine of the two needs no lane test.
-__device__ __forceinline__ float max_xor16(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ uint32_t min_xor16(uint32_t x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return min((uint32_t)r[0], (uint32_t)r[1]);
-}
-__device__ __forceinline__ uint32_t min_xor32(uint32_t x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return min((uint32_t)r[0], (uint32_t)r[1]);
-}
-
 // Argmax of one scored block, without branches, in 8 slices that a pipeline
 // stage spreads between its matrix-core instructions (source order is what the
 // compiler keeps when a reordered schedule would need more registers).  Per lane:
-// NaN-propagating maximum3 tree, then the first element equal to it; across the 4
-// lanes of a request: the maximum, then the smallest vocabulary index holding it;
-// one LDS atomic max of the key per lane (the 4 lanes of a request carry equal
-// keys).  Exact unless the block holds a NaN: then the key it gives is (NaN rank,
-// index bits 0), never above the exact key, and the wave's NaN mask tells the
-// caller to rescore with the exact scan.  Entries past V arrive as -inf and sit at
-// larger indices than every real entry of the wave, so they cannot be chosen.
+// NaN-propagating maximum3 tree, then the first element equal to it, then one LDS
+// atomic max of the lane's 64-bit key (ordered value, ~index).  The 4 lanes of a
+// request raise the same LDS word, so the atomic itself takes their maximum and, among
+// equal values, the smallest index: no cross-lane exchange is needed.  Exact unless
+// the block holds a NaN: then the lane's key is (NaN rank, index bits 0), never above
+// the exact key, and the wave's NaN mask tells the caller to rescore with the exact
+// scan.  Entries past V arrive as -inf and sit at larger indices than every real entry
+// of the wave, so they cannot be chosen.
 struct Argmax {
     static constexpr int NE = 4 * kMB;
     float x[NE];
-    float m, mr;
+    float m;
     uint32_t off, c;
 
     __device__ __forceinline__ explicit Argmax(const f32x4 (&acc)[kMB]) {
@@ -465,17 +446,13 @@ struct Argmax {
             nan_mask |= __ballot(m != m);
             off = 1u << 20;  // no element equal (m is NaN)
         } else if (s >= 2 && s <= 5) {
-            if (s == 2) mr = max_xor16(m);
-            if (s == 3) mr = max_xor32(mr);
             const int e1 = NE - 1 - (s - 2) * Q;
 #pragma unroll
             for (int e = e1; e > e1 - Q; --e) off = (x[e] == m) ? (uint32_t)(32 * (e >> 3) + (e & 7)) : off;
-            if (s == 5) c = (m == mr) ? (uint32_t)vlane + off : 0xFFFFFFFFu;
         } else if (s == 6) {
-            c = min_xor16(c);
+            c = (m == m) ? (uint32_t)vlane + off : 0xFFFFFFFFu;
         } else {
-            c = min_xor32(c);
-            const uint64_t key = ((uint64_t)ordered_u32(mr) << 32) | (uint64_t)(~c);
+            const uint64_t key = ((uint64_t)ordered_u32(m) << 32) | (uint64_t)(~c);
             atomicMax((unsigned long long*)best, (unsigned long long)key);
         }
     }
