@@ -20,10 +20,9 @@
 //     to make that so), so base logits stream in as 16-byte coalesced loads,
 //     prefetched a few request blocks ahead.
 //   * The argmax is fused: per lane a NaN-propagating maximum3 tree and the first
-//     index holding the maximum, then 64-bit keys (ordered value, ~index)
-//     reduced by cross-lane shuffles, across waves in LDS, and across workgroups
-//     by one 64-bit atomicMax per request per workgroup (skipped when the stored
-//     key is already larger).
+//     index holding the maximum, then 64-bit keys (ordered value, ~index) raised by
+//     LDS atomic max over the lanes and waves of the workgroup, and across
+//     workgroups by one 64-bit atomic max per request per workgroup.
 //   * Persistent form (the default when the tiles fit on the CUs at once): ONE
 //     launch of a resident grid runs all K positions.  Bt stays in registers for the
 //     whole step (read from memory once instead of K times), and positions are
