@@ -337,10 +337,12 @@ int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, cons
 
 /*
  * How the persistent kernels are launched.  The single-launch step (dspark_step,
- * dspark_step_sized) and the single-launch bf16 chain (dspark_chain) keep every
- * workgroup resident for the whole step and synchronise them through counters in the
- * workspace, which needs all of their workgroups on the device at once (the grid is
- * sized to fit: one workgroup per compute unit).
+ * dspark_step_sized), the single-launch bf16 chain (dspark_chain), and the bf16 chain
+ * that takes two vocabulary tiles per workgroup (dspark_chain and the steps, when the
+ * vocabulary has more 512-entry tiles than compute units, up to twice as many, with at
+ * most 64 requests) keep every workgroup resident for the whole step and synchronise
+ * them through counters in the workspace, which needs all of their workgroups on the
+ * device at once (the grid is sized to fit: one workgroup per compute unit).
  *   DSPARK_LAUNCH_RESIDENT (default): a plain kernel launch.  The caller keeps other
  *       kernels off the device while a step runs (one engine stream, as a serving
  *       engine has).  Should another kernel hold compute units, the step waits for
