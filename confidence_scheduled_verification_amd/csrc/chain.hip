@@ -92,6 +92,98 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
                                             (int)gridDim.x, nullptr, smp);
 }
 
+// Second-factor fragments of one wave's vocabulary slice kept in LDS, lane-linear:
+// fragment (mb, ks) of lane l at byte ((mb * KS + ks) * 64 + l) * 16 of the slice, the
+// layout load_bt gives in registers.  kLdsWaves waves of a two-tile workgroup keep their
+// second tile there (in the key-row rows that at most 64 requests leave free), so they
+// never reload it.
+template <int KS>
+constexpr int lds_waves() {
+    constexpr int free_bytes = (kReqChunk - 64) * ChainLds<KS>::LROW * 2;
+    constexpr int slice = kMB * KS * 64 * 16;
+    return free_bytes / slice < kWaves ? free_bytes / slice : kWaves;
+}
+
+template <int KS>
+__device__ __forceinline__ char* lds_slice(ChainLds<KS>& L, int s) {
+    return reinterpret_cast<char*>(L.a + 64 * ChainLds<KS>::LROW) + s * (kMB * KS * 64 * 16);
+}
+
+// The wave slice starting at vocabulary vb into LDS by direct-to-LDS loads (rows past V
+// and k past rank land as zeros).
+template <int KS>
+__device__ __forceinline__ void load_slice_lds(char* slice, const uint16_t* __restrict__ Bt, int V, int rank, int vb) {
+    const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+    const u32x4 rs = buffer_rsrc(Bt, (uint32_t)V * (uint32_t)rank * 2u);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+        const int v = vb + 32 * (mb >> 1) + 8 * (n16 >> 2) + 4 * (mb & 1) + (n16 & 3);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = ks * 32 + g * 8;
+            const uint32_t voff = (v < V && k0 < rank) ? ((uint32_t)v * (uint32_t)rank + (uint32_t)k0) * 2u : 0xFFFFFFF0u;
+            dma16_to_lds(rs, lds_addr(slice + (mb * KS + ks) * 1024), voff);
+        }
+    }
+}
+
+// Score the (at most 4) request blocks of requests [0, RC) against the wave slice held in
+// LDS at `slice` (vocabulary vb).  EXACT: the ordered-key scan of every element (for a
+// wave whose fast pass met a NaN); otherwise the fused argmax, returning the NaN mask.
+// Base blocks are all requested first.
+template <int KS, bool VEC, bool EXACT>
+__device__ __forceinline__ uint64_t score_slice_lds(ChainLds<KS>& L, const char* slice,
+                                                    const uint16_t* __restrict__ base, int R, int K, int V, int pos,
+                                                    int RC, int vb) {
+    constexpr int LROW = ChainLds<KS>::LROW;
+    const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+    const int vlane = vb + 8 * g;
+    const int nB = (RC + 15) >> 4;
+    const BaseSrc src = base_src(base, R, K, V, n16, vlane);
+    const __amdgpu_buffer_rsrc_t rs = seg_rsrc(src, 0, pos, K, V);
+    BaseFrag f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        if (b < nB) load_block<VEC>(f[b], src, rs, b, 0, pos, R, K, V, n16, vlane);
+    uint64_t nan_mask = 0ull;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        if (b < nB) {
+            f32x4 acc[kMB];
+            if (EXACT || vb + kWV > V) init_acc<true, VEC>(acc, f[b], vlane, V);
+            else init_acc<false, VEC>(acc, f[b], vlane, V);
+            const uint16_t* arow = L.a + (b * 16 + n16) * LROW + g * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bfr = *(const bf16x8*)(arow + ks * 32);
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
+                    const bf16x8 afr = *(const bf16x8*)(slice + ((mb * KS + ks) * 64 + lane) * 16);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[mb], 0, 0, 0);
+                }
+            }
+            uint64_t* best = L.best + b * 16 + n16;
+            if (!EXACT) {
+                block_argmax<false>(acc, best, vlane, nan_mask, SampleArgs{}, pos, 0);
+            } else {
+                uint32_t bu = 0u, bv = 0u;
+#pragma unroll
+                for (int e = 0; e < 4 * kMB; ++e) {
+                    const uint32_t v = (uint32_t)(vlane + 32 * (e >> 3) + (e & 7));
+                    const uint32_t u = ordered_u32(acc[2 * (e >> 3) + ((e & 7) >> 2)][e & 3]);
+                    if (v < (uint32_t)V && u > bu) {
+                        bu = u;
+                        bv = v;
+                    }
+                }
+                const uint64_t key = bu ? (((uint64_t)bu << 32) | (uint64_t)(~bv)) : 0ull;
+                atomicMax((unsigned long long*)best, (unsigned long long)key);
+            }
+        }
+    }
+    return nan_mask;
+}
+
 // Two vocabulary tiles per workgroup, for vocabularies with more tiles than the CUs
 // hold at once (up to twice as many): workgroup b owns tiles b and b + G.  The
 // registers hold one tile's second-factor rows, so each position scores the tile
@@ -99,8 +191,10 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist_bf16_kernel(
 // every position (b, b+G | b+G, b | b, b+G ...): the tile scored last at one position
 // is scored first at the next.  A position then reads half of the second factor from
 // memory instead of all of it, and the K positions are one launch with grid barriers
-// instead of K launches.  One request group (R <= 64): the key rows are gathered once
-// per position for both tiles, and each request's key goes out once per workgroup.
+// instead of K launches.  At the full rank with 16-byte base loads, the last
+// lds_waves<KS>() waves keep their second tile's slice in LDS instead (loaded once) and
+// score it from there at every position, so they never reload.  One request group (R <= 64): the key rows are gathered once per
+// position for both tiles, and each request's key goes out once per workgroup.
 template <int KS, bool VEC, int PF>
 __global__ __launch_bounds__(kNT, 1) void chain_persist2_bf16_kernel(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
@@ -114,14 +208,29 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist2_bf16_kernel(
     decode_rows(L.prev, L.best, prev0, keys, tokens, status, R, K, V, 0, 0, R, 0, rows);
     __syncthreads();
     gather_rows<KS, false>(L, A, V, rank, R, 0, rows);
+    // LDS slices only with 16-byte base loads at the full rank (the other forms would
+    // run out of registers beside them)
+    constexpr int NL = (VEC && KS == 8) ? lds_waves<KS>() : 0;
+    const bool in_lds = NL > 0 && w >= kWaves - NL;  // this wave's second tile lives in LDS
+    char* slice = lds_slice(L, in_lds ? w - (kWaves - NL) : 0);
     bf16x8 bt[kMB][KS];
     load_bt<KS>(bt, Bt, V, rank, vb0, lane & 15, lane >> 4);
+    if (in_lds) load_slice_lds<KS>(slice, Bt, V, rank, vb1);
     BaseFrag pre[PF];
     prefetch_rows<VEC, PF>(pre, base, R, K, V, 0, 0, vb0);
     int ring_pos = 0, ring_vb = vb0;  // the ring holds the first blocks of (position, wave slice)
-    __builtin_amdgcn_s_waitcnt(0);    // this wave's gather slots have landed
+    __builtin_amdgcn_s_waitcnt(0);    // this wave's gather and LDS slots have landed
     __syncthreads();
     for (int pos = 0; pos < K; ++pos) {
+        if (in_lds) {
+            // the first tile from registers (its ring runs on to the next position), the
+            // second from LDS
+            if (vb0 < V)
+                score_rows<KS, VEC, false, PF>(L, bt, pre, base, R, K, V, pos, 0, R, 0, vb0,
+                                               pos + 1 < K ? pos + 1 : pos, 0);
+            if (vb1 < V && score_slice_lds<KS, VEC, false>(L, slice, base, R, K, V, pos, R, vb1) != 0ull)
+                score_slice_lds<KS, VEC, true>(L, slice, base, R, K, V, pos, R, vb1);
+        } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool second = ((pos + h) & 1) != 0;
@@ -138,6 +247,7 @@ __global__ __launch_bounds__(kNT, 1) void chain_persist2_bf16_kernel(
                 ring_pos = npos;
                 ring_vb = nvb;
             }
+        }
         }
         __syncthreads();
         uint64_t token = 0;

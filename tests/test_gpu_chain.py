@@ -241,3 +241,34 @@ def test_two_tile_chain_special_values_match_numpy_argmax():
     ch = gu.Chain(base, A, Bmat, inputs.BF16, prev0)
     tok, _, _ = ch.run()
     np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))
+
+
+def test_two_tile_chain_lds_slices_special_values():
+    # Full rank, V a multiple of 8: the last waves of each workgroup score their second tile
+    # from LDS.  Bmat = 0, so every position is numpy's argmax of its base row; NaNs (the
+    # exact rescore from LDS), infinities and ties sit in those waves' vocabulary slices
+    # (second tile b + G, G = 137 workgroups for V = 140000, wave offsets 320..511).
+    R, K, V, rank = 10, 3, 140000, 256
+    G = ((V + 511) // 512 + 1) // 2
+    t2 = lambda b, off: (b + G) * 512 + off  # noqa: E731
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((R, K, V)).astype(np.float32)
+    x[0, 0, t2(0, 400)] = np.nan
+    x[0, 0, t2(5, 330)] = np.nan
+    x[1, 1, t2(3, 511)] = np.inf
+    x[1, 1, t2(2, 320)] = np.inf
+    x[2, 2, t2(7, 350)] = 40.0
+    x[2, 2, t2(1, 350)] = 40.0
+    x[3, 0, :] = -np.inf
+    x[4, 1, t2(135, 450)] = 35.0   # the last full second tile
+    base = inputs.round_to_bf16(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+    base[np.isnan(x)] = 0x7FC0
+    base[np.isposinf(x)] = 0x7F80
+    base[np.isneginf(x)] = 0xFF80
+    ref = inputs.bf16_to_f32(base)
+    A = inputs.round_to_bf16(np.ones((V, rank), dtype=np.float32))
+    Bmat = inputs.round_to_bf16(np.zeros((rank, V), dtype=np.float32))
+    prev0 = rng.integers(0, V, size=R, dtype=np.int32)
+    ch = gu.Chain(base, A, Bmat, inputs.BF16, prev0)
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), np.argmax(ref, axis=2))
