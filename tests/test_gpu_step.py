@@ -1,6 +1,8 @@
 """GPU parity of the fused step (dspark_step) on every workload at its full size,
 in the launch configuration the benchmark times.  Chain rows are sampled (the
 fp64 oracle runs them one by one); the schedule is compared in full."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -169,3 +171,31 @@ def test_ring_depth_boundaries(R):
     np.testing.assert_array_equal(tok.cpu().numpy(), got["tokens"])
     want = sched.schedule(c["conf"], R, 0, R, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, R, K)
+
+
+# Vocabulary sizes on the boundaries between the step's launch forms (256 compute units,
+# 512-entry tiles): 255 tiles take the single launch with its scheduling workgroup; 256
+# tiles, the schedule launch and the single-launch chain; 257 tiles with R <= 64, the
+# two-tile chain; 514 tiles, one chain launch per position.  Every form must give the
+# oracle's tokens and schedule.
+@pytest.mark.parametrize("R,K,V,rank", [
+    (16, 3, 255 * 512, 256),
+    (16, 3, 255 * 512 + 8, 256),
+    (16, 3, 256 * 512 + 8, 256),
+    (8, 2, 514 * 512 - 40, 64),
+])
+def test_step_launch_form_boundaries(R, K, V, rank):
+    c = inputs.random_case(700 + V % 97, R=R, K=K, V=V, rank=rank, dtype=inputs.BF16)
+    w = dataclasses.replace(inputs.WORKLOADS["small"], R=R, R_all=R, K=K, V=V, rank=rank, n_sampling=R)
+    vc = sched.force_monotone(inputs.raw_verify_cost(w, None))
+    dc = sched.force_monotone(inputs.raw_draft_cost(w))
+    gu.say(f"launch-form boundary R={R} K={K} V={V} rank={rank}")
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    got, status, _ = gu.run_step(ch, c["conf"], R, 0, R, vc, dc)
+    assert status == 0
+    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"],
+                           rows=[0, R - 1])
+    want = sched.schedule(c["conf"], R, 0, R, vc, dc, tokens=got["tokens"])
+    gu.assert_sched_parity(got, want, R, K)
+    tok, _, _ = ch.run()
+    np.testing.assert_array_equal(tok.cpu().numpy(), got["tokens"])
