@@ -43,14 +43,13 @@ __device__ __forceinline__ void set_agent_u32(uint32_t* p, uint32_t v) {
     asm volatile("" ::"v"(old));
 }
 
-__device__ __forceinline__ int32_t token_of(const uint64_t* keys, int R, int K, int f) {
-    const int r = f / K, i = f - r * K;
-    return key_index(load_agent_u64(&keys[(size_t)i * R + r]));
-}
-
 // The scheduling workgroup of a single-launch step: G chain workgroups precede it in
-// the grid; the chain's last barrier counter is bar[last_bar].
-__device__ __forceinline__ void step_schedule_wg(const StepArgs& a, unsigned char* smem, int G, int last_bar) {
+// the grid; the chain's last barrier counter is bar[last_bar].  pos_bar >= 0: every
+// position's barriers are passed in order, position p's last one at
+// bar[p * kMaxGroups + pos_bar], so the tokens of each position are written as soon as
+// it is final, while the chain runs on, and only the last position's wait for the end.
+__device__ __forceinline__ void step_schedule_wg(const StepArgs& a, unsigned char* smem, int G, int last_bar,
+                                                 int pos_bar = -1) {
     uint32_t* bar = a.sync;
     uint32_t* ready = a.sync + a.K * kMaxGroups;
     SchedShared<kNT>& sh = *reinterpret_cast<SchedShared<kNT>*>(smem);
@@ -64,23 +63,34 @@ __device__ __forceinline__ void step_schedule_wg(const StepArgs& a, unsigned cha
     sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, sz, a.surv, a.order,
                     a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_rows);
     __syncthreads();
+    // tokens[r, i], and ver_tokens[offset_r + i] for the i below request r's prefix length
+    // (the verified slots are each request's first ones), for positions [p0, p1)
+    auto write_tokens = [&](int p0, int p1) {
+        const int np = p1 - p0;
+        for (int q = threadIdx.x; q < a.R * np; q += kNT) {
+            const int r = q / np, i = p0 + (q - r * np);
+            const int32_t tok = key_index(load_agent_u64(&a.keys[(size_t)i * a.R + r]));
+            a.tokens[r * a.K + i] = tok;
+            if (a.ver_tokens != nullptr && i < lds_rows[2 * r + 1]) a.ver_tokens[lds_rows[2 * r] + i] = tok;
+        }
+    };
+    const int B = sh.b_star;
+    if (a.ver_tokens != nullptr)
+        for (int j = B + threadIdx.x; j < n; j += kNT) a.ver_tokens[j] = -1;
+    int p0 = 0;
+    if (pos_bar >= 0) {
+        for (; p0 + 1 < a.K; ++p0) {
+            grid_wait(&bar[p0 * kMaxGroups + pos_bar], (uint32_t)G, a.status);
+            write_tokens(p0, p0 + 1);
+        }
+    }
     // each chain workgroup arrives for the groups of a position in order
     grid_wait(&bar[last_bar], (uint32_t)G, a.status);
     // Every chain workgroup has passed its last wait: the counters and the flag go back
-    // to zero for the next launch, while the tokens are decoded.
+    // to zero for the next launch, while the remaining tokens are decoded.
     for (int p = threadIdx.x; p < a.K * kMaxGroups; p += kNT) set_agent_u32(&bar[p], 0u);
     if (threadIdx.x == 0) set_agent_u32(ready, 0u);
-    // One pass over the keys: tokens[r, i], and ver_tokens[offset_r + i] for the i below
-    // request r's prefix length (the verified slots are each request's first ones).
-    const int B = sh.b_star;
-    for (int f = threadIdx.x; f < n; f += kNT) {
-        const int r = f / a.K, i = f - r * a.K;
-        const int32_t tok = token_of(a.keys, a.R, a.K, f);
-        a.tokens[f] = tok;
-        if (a.ver_tokens != nullptr && i < lds_rows[2 * r + 1]) a.ver_tokens[lds_rows[2 * r] + i] = tok;
-    }
-    if (a.ver_tokens != nullptr)
-        for (int j = B + threadIdx.x; j < n; j += kNT) a.ver_tokens[j] = -1;
+    write_tokens(p0, a.K);
 }
 
 template <int KS, bool VEC, int PF>
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(kNT, 1) void step_single_bf16_kernel(StepArgs a) {
                                     a.status, a.R, a.K, a.V, a.rank, G, a.sync + a.K * kMaxGroups);
         return;
     }
-    step_schedule_wg(a, smem, G, (a.K - 1) * kMaxGroups + group_count(a.R) - 1);
+    step_schedule_wg(a, smem, G, (a.K - 1) * kMaxGroups + group_count(a.R) - 1, group_count(a.R) - 1);
 }
 
 // fp32 factors, small batches (R <= kF32StepRows, rank <= kF32StepRank): each chain
