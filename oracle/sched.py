@@ -110,19 +110,6 @@ def topb_order(surv):
     return order, sorted_surv.astype(np.float32), rank.reshape(R, K)
 
 
-def objective(sorted_surv, B, n_sampling, T, num_reqs, verify_cost, draft_cost):
-    """f(B) = (N_sampling + sum of the B best survivals) / (verify_cost[T+B] + draft_cost[num_reqs])
-    (vLLM blog, "Scheduling the budget"; the two tables are summed, "The cost model")."""
-    S = Fraction(0)
-    for j in range(B):
-        S += Fraction(float(sorted_surv[j]))
-    num = float(Fraction(n_sampling) + S)
-    den = float(np.float32(verify_cost[T + B])) + float(np.float32(draft_cost[num_reqs]))
-    if not (math.isfinite(den) and den > 0.0):
-        return -math.inf, True
-    return num / den, False
-
-
 def choose_budget(sorted_surv, n_sampling, T, num_reqs, verify_cost, draft_cost, rule=RULE_ARGMAX):
     """Stage 4: the budget B in [0, Bmax].
 

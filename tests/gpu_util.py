@@ -13,7 +13,9 @@ through the C ABI, and compare with the oracle under the parity rules:
 """
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -72,14 +74,14 @@ def _close(g, o, rtol):
     return both_nan | same_inf | ok
 
 
-def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows=None, sample=None):
-    """Compare GPU tokens (and logits for the same rows, if given) with the teacher-forced oracle.
-    gpu_tokens: [R,K] numpy; gpu_logits: [len(rows),K,V] numpy or None.  sample=(temperature, seed):
-    the tokens are Gumbel-max samples and the near-tie rule applies to the perturbed values
-    x / temperature + g (the oracle's, in double).  Returns the near-tie count."""
+def oracle_threads() -> int:
+    """Threads for the C oracle (its ctypes calls release the GIL): the host's CPUs, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _check_rows(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows, sample):
+    """Parity of `rows` (teacher-forced oracle); gpu_logits holds those rows' logits or is None."""
     R, K, V = base.shape
-    rows = np.arange(R) if rows is None else np.asarray(rows)
-    assert gpu_tokens.min() >= 0 and gpu_tokens.max() < V, "token index outside [0, V)"
     if sample is not None:
         otok, olog, _ = oracle.chain_sample(base, A, Bmat, dtype, prev0, sample[0], sample[1], rows=rows,
                                             forced=gpu_tokens, want_perturbed=True)
@@ -107,6 +109,37 @@ def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, row
             raise AssertionError(f"chained logits outside tolerance at {bad.tolist()}: "
                                  f"gpu {[gpu_logits[tuple(b)] for b in bad]} oracle {[olog[tuple(b)] for b in bad]}")
     return near
+
+
+def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, rows=None, sample=None):
+    """Compare GPU tokens (and logits for the same rows, if given) with the teacher-forced oracle.
+    gpu_tokens: [R,K] numpy; gpu_logits: [len(rows),K,V] numpy or None; rows: None for every row.
+    sample=(temperature, seed): the tokens are Gumbel-max samples and the near-tie rule applies to
+    the perturbed values x / temperature + g (the oracle's, in double).  The rows are split over
+    oracle_threads() threads (each request's chain is independent under teacher forcing).
+    Returns the near-tie count."""
+    R, K, V = base.shape
+    rows = np.arange(R) if rows is None else np.asarray(rows)
+    assert gpu_tokens.min() >= 0 and gpu_tokens.max() < V, "token index outside [0, V)"
+    want = np.uint16 if dtype == 1 else np.float32
+    base, A, Bmat = (np.ascontiguousarray(x, dtype=want) for x in (base, A, Bmat))
+    prev0 = np.ascontiguousarray(prev0, dtype=np.int32)
+    gpu_tokens = np.ascontiguousarray(gpu_tokens, dtype=np.int32)
+    n = len(rows)
+    if n == 0:
+        return 0
+    # chunks small enough that the oracle's float64 logits of one chunk stay near 64 MB
+    per = max(1, min(-(-n // oracle_threads()), (8 << 20) // max(1, K * V)))
+    chunks = [np.arange(q0, min(n, q0 + per)) for q0 in range(0, n, per)]
+
+    def work(qs):
+        lg = None if gpu_logits is None else gpu_logits[qs]
+        return _check_rows(gpu_tokens, lg, base, A, Bmat, dtype, prev0, rows[qs], sample)
+
+    if len(chunks) == 1:
+        return work(chunks[0])
+    with ThreadPoolExecutor(max_workers=oracle_threads()) as ex:
+        return sum(ex.map(work, chunks))
 
 
 def sched_oracle(conf, n_sampling, T, num_reqs, vc, dc, tokens=None):

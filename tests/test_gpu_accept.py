@@ -72,8 +72,8 @@ def test_inconsistent_rows_are_flagged():
     np.testing.assert_array_equal(out, wo)
 
 
-@pytest.mark.parametrize("name,steps,rows", [("small", 4, [0, 13, 31]), ("headline", 2, [0, 255])])
-def test_closed_loop_of_steps(name, steps, rows):
+@pytest.mark.parametrize("name,steps", [("small", 4), ("headline", 2)])
+def test_closed_loop_of_steps(name, steps):
     # step k's bonus tokens key step k+1's chain; acceptance is drawn from step k's confidences
     w = inputs.WORKLOADS[name]
     ins = inputs.generate(w)
@@ -91,7 +91,7 @@ def test_closed_loop_of_steps(name, steps, rows):
         ch.prev0.copy_(gu.to_dev(prev0))
         got, status, _ = gu.run_step(ch, st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, out=out)
         assert status == 0
-        gu.assert_chain_parity(got["tokens"], None, st["base"], ins.A, ins.Bmat, w.dtype, prev0, rows=rows)
+        gu.assert_chain_parity(got["tokens"], None, st["base"], ins.A, ins.Bmat, w.dtype, prev0)
         want = sched.schedule(st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
         gu.assert_sched_parity(got, want, w.R, w.K)
         target = inputs.synthetic_target(got["ver_tokens"], got["offsets"], st["conf"], w.V, seed=500 + k)

@@ -198,19 +198,19 @@ def test_fast_scorer_special_values_match_numpy_argmax(R, V):
 # 256 CUs) and one request group (R <= 64) run two tiles per workgroup in one launch, the
 # tile order flipping every position.  Shapes: ragged last tile, V not a multiple of 8, an
 # odd tile count (the last workgroup's second tile is empty), ranks below 256.
-@pytest.mark.parametrize("R,K,V,rank,rows", [
-    (40, 5, 140000, 256, [0, 17, 39]),
-    (64, 4, 133635, 256, [1, 63]),
-    (7, 6, 131372, 128, None),
-    (33, 3, 262144, 64, [0, 32]),
+@pytest.mark.parametrize("R,K,V,rank", [
+    (40, 5, 140000, 256),
+    (64, 4, 133635, 256),
+    (7, 6, 131372, 128),
+    (33, 3, 262144, 64),
 ])
-def test_two_tile_chain_parity(R, K, V, rank, rows):
+def test_two_tile_chain_parity(R, K, V, rank):
     c = _case(400 + R + K, R, K, V, rank, inputs.BF16)
     gu.say(f"two-tile chain bf16 R={R} K={K} V={V} rank={rank}")
     ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     tok, _, st = ch.run()
     assert st == 0
-    gu.assert_chain_parity(tok.cpu().numpy(), None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"], rows=rows)
+    gu.assert_chain_parity(tok.cpu().numpy(), None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     tok2, _, _ = ch.run()
     assert torch.equal(tok, tok2)
 

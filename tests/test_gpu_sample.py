@@ -39,11 +39,9 @@ def test_sampled_chain_matches_the_oracle(R, K, V, rank, dtype, temperature):
     seed = 0x123456789ABCDEF0 + R
     tok, lg, st = _sample(ch, temperature, seed, want_logits=True)
     assert st == 0
-    rows = None if R <= 40 else [0, 17, 255, 299]
-    sel = np.arange(R) if rows is None else np.array(rows)
-    near = gu.assert_chain_parity(tok, lg[sel], c["base"], c["A"], c["Bmat"], dtype, c["prev0"], rows=rows,
+    near = gu.assert_chain_parity(tok, lg, c["base"], c["A"], c["Bmat"], dtype, c["prev0"],
                                   sample=(temperature, seed))
-    assert near <= max(1, len(sel) * K // 50)
+    assert near <= max(1, R * K // 50)
     # same seed, same tokens; another seed, other tokens; the greedy chain differs too
     again, _, _ = _sample(ch, temperature, seed)
     np.testing.assert_array_equal(again, tok)
@@ -59,9 +57,9 @@ def test_headline_shape_sampled_rows():
     ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
     tok, _, st = _sample(ch, 1.0, 77)
     assert st == 0
-    gu.say("headline sampled: oracle on rows 0, 128, 255")
-    gu.assert_chain_parity(tok, None, ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0, rows=[0, 128, 255],
-                           sample=(1.0, 77))
+    gu.say(f"headline sampled: oracle on all {w.R} rows")
+    near = gu.assert_chain_parity(tok, None, ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0, sample=(1.0, 77))
+    gu.say(f"headline sampled: every row ok ({near} near-ties)")
 
 
 @pytest.mark.parametrize("temperature", [1.0, 0.5])

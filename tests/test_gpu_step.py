@@ -1,6 +1,7 @@
 """GPU parity of the fused step (dspark_step) on every workload at its full size,
-in the launch configuration the benchmark times.  Chain rows are sampled (the
-fp64 oracle runs them one by one); the schedule is compared in full."""
+in the launch configuration the benchmark times.  Every chain row's tokens are
+compared with the teacher-forced fp64 oracle (rows split over host threads) and the
+schedule in full; the debug logits output is checked on a few rows."""
 import dataclasses
 
 import numpy as np
@@ -14,8 +15,10 @@ from oracle import sched
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_ROWS = {"tiny": None, "small": None, "mid": [0, 37, 111], "headline": [0, 101, 255],
-               "large": [0, 63]}
+# rows whose float32 chained logits (the debug output of the stage-1 entry point) are
+# compared within the logit tolerance; tokens are compared on every row
+LOGIT_ROWS = {"tiny": None, "small": None, "mid": [0, 37, 111], "headline": [0, 101, 255],
+              "large": [0, 63]}
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "mid", "headline", "large"])
@@ -28,9 +31,10 @@ def test_full_size_step_parity(name):
     gu.say(f"step {name}: running")
     got, status, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
     assert status == 0
-    rows = SAMPLE_ROWS[name]
-    gu.say(f"step {name}: oracle on rows {rows}")
-    gu.assert_chain_parity(got["tokens"], None, ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0, rows=rows)
+    gu.say(f"step {name}: oracle on all {w.R} rows")
+    near = gu.assert_chain_parity(got["tokens"], None, ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+    gu.say(f"step {name}: tokens ok on every row ({near} near-ties)")
+    rows = LOGIT_ROWS[name]
     want = sched.schedule(ins.conf, w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, w.R, w.K)
     # the chained logits of the sampled rows, from the stage-1 entry point on the same inputs
@@ -68,7 +72,7 @@ def test_multi_step_inputs_change_the_result():
         ch.base.copy_(gu.to_dev(st["base"]))
         ch.prev0.copy_(gu.to_dev(st["prev0"]))
         got, _, _ = gu.run_step(ch, st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, out=out)
-        gu.assert_chain_parity(got["tokens"], None, st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=[0, 31])
+        gu.assert_chain_parity(got["tokens"], None, st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"])
         want = sched.schedule(st["conf"], w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
         gu.assert_sched_parity(got, want, w.R, w.K)
 
@@ -121,7 +125,7 @@ def test_single_launch_step_at_the_slot_limit():
     ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     got, status, _ = gu.run_step(ch, conf, R, 0, R, vc, dc)
     assert status == 0
-    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"], rows=[0, 128, 255])
+    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     want = sched.schedule(conf, R, 0, R, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, R, K)
     assert 0 < got["b_star"] < R * K
@@ -193,8 +197,7 @@ def test_step_launch_form_boundaries(R, K, V, rank):
     ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     got, status, _ = gu.run_step(ch, c["conf"], R, 0, R, vc, dc)
     assert status == 0
-    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"],
-                           rows=[0, R - 1])
+    gu.assert_chain_parity(got["tokens"], None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
     want = sched.schedule(c["conf"], R, 0, R, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, R, K)
     tok, _, _ = ch.run()
