@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the chain-and-schedule step on one MI355X.
 
-One step = the whole pass (schedule kernels + chain kernels + verified-token
-gather) through dspark_step on one batch of synthetic inputs already resident in
-HBM.  Per-step inputs (base logits, prev0, confidences) cycle through a pool of
-distinct seeded draws (far larger together than the 256 MB last-level cache);
-the Markov-head factors and cost tables stay fixed, as weights and start-up
-profiles do.  Prints ONE JSON line.
+One step = the whole pass through dspark_step on one batch of synthetic inputs
+already resident in HBM: the chain (stage 1), then stages 2-5 over the
+confidences and the verified-token gather, in that order (the schedule starts
+once the chain has ended, as in the method, where the confidences score the
+drafted tokens).  Per-step inputs (base logits, prev0, confidences) cycle through
+a pool of distinct seeded draws (far larger together than the 256 MB last-level
+cache); the Markov-head factors and cost tables stay fixed, as weights and
+start-up profiles do.  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -44,8 +46,13 @@ def step_bytes(w) -> dict:
     return d
 
 
-def chain_kernel(w, num_cu: int = 256) -> dict:
+def chain_kernel(w, num_cu: int = 256, form: int = 0) -> dict:
     """The dominant kernel of the step and its algorithmic bytes per launch.  bf16 with
+    K <= 32 and V <= 262144 in the pruned form (the default) runs stage 1 as one launch
+    of cand_chain_kernel, whose algorithmic bytes are the chain's share of the step's:
+    every base logit and the second factor once, the K*R key rows, prev0 and the tokens
+    (the kernel itself reads the base logits and only the candidates' factor rows).
+    Otherwise: bf16 with
     R <= 256, and fp32 with R <= 64 and rank <= 64, run the whole step in one launch of a
     resident grid (step_single_bf16_kernel, step_single_f32_kernel): every base logit
     once, the second factor once, the K*R gathered key rows, the keys written and read
@@ -53,6 +60,9 @@ def chain_kernel(w, num_cu: int = 256) -> dict:
     launch per position moves its base slice, the whole second factor, its R key rows and
     keys."""
     e = 2 if w.dtype == 1 else 4
+    if form == 0 and w.dtype == 1 and w.K <= 32 and w.V <= 262144:
+        b = w.R * w.K * w.V * e + w.V * w.rank * e + w.R * w.K * w.rank * e + w.R * 4 + w.R * w.K * 4
+        return {"kernel": "cand_chain_kernel", "bytes_per_launch": b, "launches_per_step": 1}
     tiles = (w.V + 511) // 512  # one 512-entry vocabulary tile per workgroup, one workgroup per CU
     single = (w.R <= 256) if w.dtype == 1 else (w.R <= 64 and w.rank <= 64)
     if single and tiles + 1 <= num_cu:
@@ -112,6 +122,14 @@ def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
     positions, whole vocabulary) scaled to R requests, plus the full schedule."""
     import oracle
     from oracle import sched
+    # one core, enforced: the oracle is single-threaded and is timed as such
+    cores = None
+    try:
+        before = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(before)})
+        cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        before = None
     sel = np.linspace(0, w.R - 1, rows).astype(np.int32)
     t0 = time.perf_counter()
     oracle.chain(step_in["base"], ins.A, ins.Bmat, w.dtype, step_in["prev0"], rows=sel)
@@ -120,7 +138,10 @@ def cpu_baseline(w, ins, step_in, vc, dc, rows: int) -> dict:
     sched.schedule(step_in["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
     t_sched = time.perf_counter() - t0
     per_step = t_chain * (w.R / rows) + t_sched
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle", **host_info(),
+    if before is not None:
+        os.sched_setaffinity(0, before)
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": cores or 1, "kind": "oracle",
+            "affinity": "pinned to one core (sched_setaffinity)" if cores else "not pinned", **host_info(),
             "sample": f"fp64 chain of {rows} of {w.R} requests (all {w.K} positions, V={w.V}) timed "
                       f"{t_chain:.2f} s and scaled x{w.R / rows:.0f}; schedule of all {w.R * w.K} slots "
                       f"timed {t_sched:.2f} s; single-threaded"}
@@ -188,16 +209,15 @@ def accept_lane(w, B, inputs, out, st, dev, calls: int = 200) -> dict:
             "parity": "ok" if ok else "MISMATCH"}
 
 
-def stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status, rule, steps) -> dict:
+def stale_sized(w, B, osched, pool, host_steps, mk, vc_d, dc_d, vc, dc, out, ws, status, rule, steps) -> dict:
     """dspark_step_sized with B sized from the previous pool entry's confidences (a
     one-step-old buffer) under `rule`; timed over `steps` steps and checked on the last."""
     P = len(pool)
+    plan = B.StepPlan(mk, w.R, w.K, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status, rule=rule)
 
     def run(k):
         base, prev0, conf = pool[k % P]
-        old = pool[(k - 1) % P][2]
-        B.dspark_step_sized(base, A, Bt, w.dtype, prev0, conf, old, rule, w.n_sampling, w.T, w.R_all, vc_d, dc_d,
-                            out, ws, status)
+        plan(base, prev0, conf, pool[(k - 1) % P][2])
 
     for k in range(10):
         run(k)
@@ -214,7 +234,7 @@ def stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, 
             "b_last": int(want["b_star"]), "b_same_step": int(same["b_star"]), "parity": "ok" if ok else "MISMATCH"}
 
 
-def sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, steps) -> dict:
+def sampled_chain(w, B, pool, host_steps, ins, mk, ws, dev, steps) -> dict:
     """Stage 1 with probabilistic drafting (dspark_chain_sample, temperature 1.0, a new
     seed every step): one launch per position of the general scorer with a Gumbel
     variate (Philox4x32-10 + two logarithms) per vocabulary entry; timed, and one row of
@@ -226,7 +246,7 @@ def sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev, steps) -> dict:
 
     def run(k):
         base, prev0, _ = pool[k % P]
-        B.dspark_chain_sample(base, A, Bt, w.dtype, prev0, 1.0, 1000 + k, tokens, None, None, ws)
+        B.dspark_chain_sample(base, mk, prev0, 1.0, 1000 + k, tokens, None, None, ws)
 
     for k in range(3):
         run(k)
@@ -322,21 +342,64 @@ def sched_only(args, w, B, inputs, osched, dev):
     print(json.dumps(res), flush=True)
 
 
-def cooperative_rate(B, run, steps) -> dict:
-    """The same step with its kernel launched cooperatively (the runtime-guaranteed
-    residency mode) instead of the default plain launch of a resident grid."""
-    B.dspark_set_launch_mode(B.LAUNCH_COOPERATIVE)
+def dense_forms(B, run, steps) -> dict:
+    """The same step in the dense form (the matrix-core chain over the whole vocabulary,
+    with stages 2-5 on a workgroup of the same single launch, beside the chain), launched
+    as a plain launch of a resident grid and cooperatively."""
+    out = {}
+    B.dspark_set_chain_form(B.CHAIN_DENSE)
     try:
-        for k in range(10):
-            run(k)
-        us = _event_loop_us(run, steps)
+        for label, mode in (("dense_overlapped", B.LAUNCH_RESIDENT), ("dense_overlapped_cooperative",
+                                                                      B.LAUNCH_COOPERATIVE)):
+            B.dspark_set_launch_mode(mode)
+            for k in range(10):
+                run(k)
+            us = _event_loop_us(run, steps)
+            log(f"bench: {label} {us:.1f} us/step")
+            out[label] = {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1), "steps": steps}
     finally:
         B.dspark_set_launch_mode(B.LAUNCH_RESIDENT)
-    log(f"bench: cooperative launch {us:.1f} us/step")
-    return {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1), "steps": steps}
+        B.dspark_set_chain_form(B.CHAIN_PRUNED)
+    return out
 
 
-def closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, steps) -> dict:
+def vocab_shard(B, inputs, dev, steps) -> dict:
+    """One GPU's share of the headline chain under an 8-way vocabulary split (V / 8 =
+    16160 columns, all 256 requests): the step's chain and schedule on that shard, pruned
+    and dense.  (Across GPUs each position's keys would meet in one small max all-reduce,
+    which one GPU does not show.)"""
+    import torch
+    w = inputs.WORKLOADS["shard"]
+    ins = inputs.generate(w)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    mk = B.MarkovHead(d(ins.A), d(ins.Bmat), w.dtype)
+    vc_d = d(B.dspark_force_monotone(ins.verify_cost_raw))
+    dc_d = d(B.dspark_force_monotone(ins.draft_cost_raw))
+    base, prev0, conf = d(ins.base), d(ins.prev0), d(ins.conf)
+    ws = B.workspace(w.R, w.K, w.V, w.rank, w.dtype, device=dev)
+    out = B.StepBuffers(w.R, w.K, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    plan = B.StepPlan(mk, w.R, w.K, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, st)
+    res = {"workload": f"{w.name}: R={w.R}, K={w.K}, V={w.V}, r={w.rank}"}
+    for label, form in (("pruned", B.CHAIN_PRUNED), ("dense", B.CHAIN_DENSE)):
+        B.dspark_set_chain_form(form)
+        try:
+            for _ in range(10):
+                plan(base, prev0, conf)
+            us = _event_loop_us(lambda k: plan(base, prev0, conf), steps)
+        finally:
+            B.dspark_set_chain_form(B.CHAIN_PRUNED)
+        res[label] = {"step_us": round(us, 2), "steps_per_s": round(1e6 / us, 1)}
+        log(f"bench: vocabulary shard ({label}) {us:.1f} us/step")
+    res["status"] = int(st.item())
+    return res
+
+
+def closed_loop(w, B, pool, mk, vc_d, dc_d, ws, dev, steps) -> dict:
     """A multi-step synthetic decode loop, all on the device: each iteration runs the step
     sized from the previous step's confidences (dspark_step_sized), a stand-in for the
     target model's greedy tokens whose acceptance is drawn from this step's confidences
@@ -361,8 +424,8 @@ def closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, steps) -> dict:
     def one(k):
         base, _, conf = pool[k % P]
         old = pool[(k - 1) % P][2]
-        B.dspark_step_sized(base, A, Bt, w.dtype, prev0, conf, old, B.RULE_ARGMAX, w.n_sampling, w.T, w.R_all,
-                            vc_d, dc_d, out, ws, status)
+        B.dspark_step_sized(base, mk, prev0, conf, old, B.RULE_ARGMAX, w.n_sampling, w.T, w.R_all, vc_d, dc_d,
+                            out, ws, status)
         slot = out.ver_idx.long()
         valid = j < out.b_star.long()
         slot_c = slot.clamp(min=0)
@@ -393,7 +456,7 @@ def closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, steps) -> dict:
             "target": "synthetic stand-in (torch): draft j accepted with probability c[r, j]"}
 
 
-def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev) -> dict:
+def measured_tables(w, B, osched, pool, host_steps, mk, out, ws, status, dev) -> dict:
     """Cost tables measured on this GPU at start-up: a proxy verification step (4 bf16
     GEMMs [t, 7168] x [7168, 7168]) over the captured sizes up to the workload's capture
     limit plus 1.5x and 2x above it, and a proxy drafting step (one GEMM over the K
@@ -412,7 +475,7 @@ def measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
     build_s = time.perf_counter() - t0
     base, prev0, conf = pool[0]
     vc_d, dc_d = torch.from_numpy(vc).to(dev), torch.from_numpy(dc).to(dev)
-    B.dspark_step(base, A, Bt, w.dtype, prev0, conf, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
+    B.dspark_step(base, mk, prev0, conf, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
     torch.cuda.synchronize()
     want = osched.schedule(host_steps[0]["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
     ok = (int(out.b_star.item()) == want["b_star"] and float(out.best_obj.item()) == want["best_obj"]
@@ -483,11 +546,7 @@ def main():
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    A = dev_t(ins.A)
-    Bm = dev_t(ins.Bmat)
-    Bt = torch.empty((w.V, w.rank), dtype=Bm.dtype, device=dev)
-    B.dspark_markov_prepare(Bm, w.dtype, Bt)
-    del Bm
+    mk = B.MarkovHead(dev_t(ins.A), dev_t(ins.Bmat), w.dtype)
     vc_d, dc_d = dev_t(vc), dev_t(dc)
     pool, host_steps = [], []
     for k in range(args.pool):
@@ -498,10 +557,12 @@ def main():
     ws = B.workspace(w.R, w.K, w.V, w.rank, w.dtype, device=dev)
     out = B.StepBuffers(w.R, w.K, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # every argument that stays fixed across steps is marshalled once: a step is one C call
+    plan = B.StepPlan(mk, w.R, w.K, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
 
     def run(k):
         base, prev0, conf = pool[k % len(pool)]
-        B.dspark_step(base, A, Bt, w.dtype, prev0, conf, w.n_sampling, w.T, w.R_all, vc_d, dc_d, out, ws, status)
+        plan(base, prev0, conf)
 
     for k in range(args.warmup):
         run(k)
@@ -543,28 +604,43 @@ def main():
     torch.cuda.synchronize()
     B.dspark_set_timing_events(None, None)
     step_ms = np.array([ev[k][0].elapsed_time(ev[k][3]) for k in range(KE)])
-    sched_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(KE)])
+    pre_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(KE)])
     chain_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(KE)])
+    post_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(KE)])
     log(f"bench: event pass {KE} steps: {step_ms.mean() * 1e3:.1f} us/step "
-        f"(sched {sched_ms.mean() * 1e3:.1f} us, chain {chain_ms.mean() * 1e3:.1f} us)")
+        f"(chain {chain_ms.mean() * 1e3:.1f} us, after it {post_ms.mean() * 1e3:.1f} us)")
 
     # Parity against the oracle (two sampled rows + the whole schedule) on steps 0, 1, 499
     # and the last of the timed sequence, each run again untimed (a step's result
     # depends only on its inputs, which cycle through the pool).
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
 
-    def check(k) -> bool:
-        st = host_steps[k % len(pool)]
-        tok = out.tokens.cpu().numpy()
-        rows = [0, w.R - 1]
-        otok, olog, _ = oracle.chain(st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=rows, forced=tok,
+    def rows_ok(st, tok, rows) -> bool:
+        # teacher-forced oracle on these rows; a differing token must be an oracle near-tie
+        otok, _, _ = oracle.chain(st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=rows, forced=tok)
+        bad = [q for q in range(len(rows)) if not np.array_equal(otok[q], tok[rows[q]])]
+        if not bad:
+            return True
+        sel = np.asarray(rows)[bad]
+        otok, olog, _ = oracle.chain(st["base"], ins.A, ins.Bmat, w.dtype, st["prev0"], rows=sel, forced=tok,
                                      want_logits=True)
         ok = True
-        for q, r in enumerate(rows):
+        for q, r in enumerate(sel):
             for i in range(w.K):
                 if otok[q, i] != tok[r, i]:
                     xo, xg = olog[q, i, otok[q, i]], olog[q, i, tok[r, i]]
                     ok &= bool(xo - xg <= 1e-4 * max(abs(xo), 1.0))
+        return ok
+
+    def check(k) -> bool:
+        # every chain row (threads: the C oracle releases the interpreter lock) and the schedule
+        st = host_steps[k % len(pool)]
+        tok = out.tokens.cpu().numpy()
+        nthr = max(1, min(16, os.cpu_count() or 1))
+        chunks = np.array_split(np.arange(w.R, dtype=np.int32), min(w.R, 4 * nthr))
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            ok = all(ex.map(lambda rows: rows_ok(st, tok, rows), [c for c in chunks if len(c)]))
         want = osched.schedule(st["conf"], w.n_sampling, w.T, w.R_all, vc, dc)
         ok &= int(out.b_star.item()) == want["b_star"]
         ok &= float(out.best_obj.item()) == want["best_obj"]
@@ -585,19 +661,21 @@ def main():
     extra = None
     if not args.no_variants:
         extra = {"accept_greedy": accept_lane(w, B, inputs, out, st, dev)}
+        extra.update(dense_forms(B, run, min(args.event_steps, K)))
         for label, rule in (("stale_sizing_argmax", B.RULE_ARGMAX), ("stale_sizing_first_drop", B.RULE_FIRST_DROP)):
-            extra[label] = stale_sized(w, B, osched, pool, host_steps, A, Bt, vc_d, dc_d, vc, dc, out, ws, status,
+            extra[label] = stale_sized(w, B, osched, pool, host_steps, mk, vc_d, dc_d, vc, dc, out, ws, status,
                                        rule, min(args.event_steps, K))
-        extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, A, Bt, ws, dev,
+        extra["sampled_chain"] = sampled_chain(w, B, pool, host_steps, ins, mk, ws, dev,
                                                min(args.event_steps, 100))
-        extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, A, Bt, out, ws, status, dev)
-        extra["cooperative_launch"] = cooperative_rate(B, run, min(args.event_steps, K))
-        extra["closed_loop"] = closed_loop(w, B, pool, A, Bt, vc_d, dc_d, ws, dev, min(args.event_steps, K))
+        extra["measured_cost_tables"] = measured_tables(w, B, osched, pool, host_steps, mk, out, ws, status, dev)
+        extra["closed_loop"] = closed_loop(w, B, pool, mk, vc_d, dc_d, ws, dev, min(args.event_steps, K))
+        if w.name == "headline":
+            extra["vocab_shard"] = vocab_shard(B, inputs, dev, min(args.event_steps, K))
 
     copy_gbs = copy_bandwidth(dev)
     log(f"bench: plain device copy {copy_gbs:.0f} GB/s (read + write)")
     sb = step_bytes(w)
-    ck = chain_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count)
+    ck = chain_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count, B.dspark_get_chain_form())
     launch_s = chain_ms.mean() * 1e-3 / ck["launches_per_step"]   # event-timed chain phase per launch
     achieved = ck["bytes_per_launch"] / launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -605,13 +683,17 @@ def main():
                 "launch_us": round(launch_s * 1e6, 2),
                 "practical_peak": {"kind": "plain device copy, 1 GiB read + 1 GiB written", "gbs": round(copy_gbs, 1),
                                    "frac": round(achieved / copy_gbs, 4)}}
-    # the contraction on the matrix cores (bf16) or the vector FMA units (fp32 factors)
+    # the dense contraction's flop count over the chain's time; the pruned form evaluates
+    # the bias for the candidates alone, so this is the work it avoids, not work it does
     flops = 2.0 * w.R * w.K * w.V * w.rank
+    pruned = ck["kernel"] == "cand_chain_kernel"
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == 1 else FP32_VECTOR_PEAK_TFLOPS
     mfma_tf = flops / (chain_ms.mean() * 1e-3) / 1e12
     compute = {"unit": "TFLOP/s", "flops_per_step": flops, "achieved": round(mfma_tf, 1), "peak": mfma_peak,
                "frac": round(mfma_tf / mfma_peak, 4),
-               "engine": "bf16 MFMA" if w.dtype == 1 else "fp32 vector FMA"}
+               "engine": ("none: the bias is evaluated for the candidates only (fp32 FMA); this is the dense "
+                          "contraction's flop count per chain time" if pruned else
+                          ("bf16 MFMA" if w.dtype == 1 else "fp32 vector FMA"))}
     ms_per_step = wall * 1e3 / K
     res = {
         "metric": METRIC,
@@ -628,7 +710,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: R={w.R} (of {w.R_all}), K={w.K}, V={w.V}, r={w.rank}, T={w.T}, "
                                f"N_sampling={w.n_sampling}", "input_pool": len(pool),
-                   "launch": "resident (plain launch of a grid that fits the device; one stream)"},
+                   "order": ("serial: the chain, then stages 2-5 over the confidences (two launches, one stream)"
+                             if pruned else "one launch: stages 2-5 on a workgroup beside the chain"),
+                   "chain_form": "pruned" if pruned else "dense"},
         "roofline": roofline,
         "compute": compute,
         "sched_kernel_us": sched_us,
@@ -636,8 +720,10 @@ def main():
         "step_hbm_frac": round(sb["total"] / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "step_us_loop_events": round(loop_ms * 1e3 / K, 2),
         "event_pass": {"steps": KE, "step_us": round(float(step_ms.mean()) * 1e3, 2),
-                       "sched_us": round(float(sched_ms.mean()) * 1e3, 2),
-                       "chain_us": round(float(chain_ms.mean()) * 1e3, 2)},
+                       "before_chain_us": round(float(pre_ms.mean()) * 1e3, 2),
+                       "chain_us": round(float(chain_ms.mean()) * 1e3, 2),
+                       "after_chain_us": round(float(post_ms.mean()) * 1e3, 2),
+                       "note": "four timing events per step add their own time between launches"},
         "parity_last_step": "ok" if checked[K - 1] else "MISMATCH",
         "parity": parity,
         "parity_steps": {str(k): ("ok" if v else "MISMATCH") for k, v in sorted(checked.items())},
@@ -648,6 +734,15 @@ def main():
         log("bench: timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, ins, host_steps[0], vc, dc, min(args.cpu_rows, w.R))
     print(json.dumps(res), flush=True)
+    # Orderly teardown before the interpreter exits: no library-held event handles, every
+    # queued kernel done, device buffers released while the runtime is fully up.
+    B.dspark_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    del plan, pool, out, ws, status, mk, ev
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

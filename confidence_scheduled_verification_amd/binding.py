@@ -29,8 +29,13 @@ LAUNCH_COOPERATIVE = 1
 MAX_SLOTS = 16384
 RULE_ARGMAX = 0
 RULE_FIRST_DROP = 1
+CHAIN_PRUNED = 0
+CHAIN_DENSE = 1
+MARKOV_MAGIC = 0x31766b6d6b707364
+MARKOV_HEADER_BYTES = 256
 
-EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_prepare",
+EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_state_bytes",
+           "dspark_markov_prepare", "dspark_set_chain_form", "dspark_get_chain_form",
            "dspark_chain", "dspark_chain_sample", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
            "dspark_step", "dspark_step_sized", "dspark_schedule", "dspark_accept_greedy", "dspark_set_timing_events",
            "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table", "dspark_set_launch_mode",
@@ -38,6 +43,13 @@ EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dsp
 
 # int fn(int shape, void* user, void* stream)
 SHAPE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class dspark_markov_t(ctypes.Structure):
+    """The C handle of a prepared Markov head (include/dspark.h)."""
+    _fields_ = [("magic", ctypes.c_uint64), ("A", ctypes.c_void_p), ("Bmat", ctypes.c_void_p),
+                ("state", ctypes.c_void_p), ("state_bytes", ctypes.c_size_t), ("V", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class DSparkError(RuntimeError):
@@ -64,18 +76,22 @@ def lib():
         L.dspark_version.argtypes = []
         L.dspark_workspace_bytes.restype = sz
         L.dspark_workspace_bytes.argtypes = [i, i, i, i, i]
-        L.dspark_markov_prepare.argtypes = [p, i, i, i, p, p]
-        L.dspark_chain.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, p, sz, p]
-        L.dspark_chain_sample.argtypes = [p, p, p, i, p, i, i, i, i, ctypes.c_float, ctypes.c_uint64, p, p, p, p,
-                                          sz, p]
+        L.dspark_markov_state_bytes.restype = sz
+        L.dspark_markov_state_bytes.argtypes = [i, i, i]
+        L.dspark_markov_prepare.argtypes = [p, p, p, i, i, i, p, sz, p]
+        L.dspark_set_chain_form.argtypes = [i]
+        L.dspark_get_chain_form.argtypes = []
+        L.dspark_chain.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, p, p, sz, p]
+        L.dspark_chain_sample.argtypes = [p, p, p, i, p, i, i, i, i, p, ctypes.c_float, ctypes.c_uint64, p, p, p,
+                                          p, sz, p]
         L.dspark_survival.argtypes = [p, i, i, p, p, p]
         L.dspark_topb_select.argtypes = [p, i, i, p, p, p, p]
         L.dspark_choose_budget.argtypes = [p, i, i, i, i, p, i, p, i, i, p, p, p, p, p]
         L.dspark_allocate.argtypes = [p, p, i, i, p, p, p, p, p, p]
-        L.dspark_step.argtypes = [p, p, p, i, p, i, i, i, i, p, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p, p,
-                                  p, p, p, sz, p]
-        L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, i, i, p, i, p, i, p, p, p, p,
-                                        p, p, p, p, p, p, p, p, sz, p]
+        L.dspark_step.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p,
+                                  p, p, p, p, sz, p]
+        L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, i, i, i, i, i, p, i, p, i, p, p, p,
+                                        p, p, p, p, p, p, p, p, p, sz, p]
         L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
         L.dspark_schedule.argtypes = [p, i, i, p, i, i, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p, p, p, p, p]
         L.dspark_set_timing_events.argtypes = [p, p]
@@ -85,7 +101,8 @@ def lib():
         L.dspark_profile_shapes.argtypes = [SHAPE_FN, p, p, i, i, i, p, p]
         L.dspark_build_cost_table.argtypes = [p, i, p, i, i, p, i]
         for name in EXPORTS:
-            if name not in ("dspark_last_error", "dspark_version", "dspark_workspace_bytes"):
+            if name not in ("dspark_last_error", "dspark_version", "dspark_workspace_bytes",
+                            "dspark_markov_state_bytes"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -127,50 +144,97 @@ def dspark_workspace_bytes(R: int, K: int, V: int, rank: int, dtype: int) -> int
     return int(lib().dspark_workspace_bytes(R, K, V, rank, dtype))
 
 
-def dspark_markov_prepare(Bmat, dtype: int, Bt, stream=None):
-    """Bt [V, rank] = Bmat [rank, V] transposed (start-up weight layout)."""
-    rank, V = Bmat.shape
-    if tuple(Bt.shape) != (V, rank):
-        raise ValueError("Bt must be [V, rank]")
-    _contig(Bmat, Bt)
-    _elem_ok(Bmat, dtype, "Bmat")
-    _elem_ok(Bt, dtype, "Bt")
-    _check(lib().dspark_markov_prepare(_p(Bmat), rank, V, dtype, _p(Bt), _stream(stream)))
+class MarkovHead:
+    """The Markov head's factors A [V, rank] and Bmat [rank, V] (device tensors, kept
+    referenced here) with the library's prepared state (the transposed factor and the
+    bias bound, in a device buffer owned here) and the handle the chain and step calls
+    take (dspark_markov_prepare)."""
+
+    def __init__(self, A, Bmat, dtype: int, stream=None):
+        import torch
+        if A.dim() != 2 or Bmat.dim() != 2:
+            raise ValueError("MarkovHead: A must be [V, rank] and Bmat [rank, V]")
+        V, rank = A.shape
+        if tuple(Bmat.shape) != (rank, V):
+            raise ValueError(f"MarkovHead: Bmat must be [rank, V] = [{rank}, {V}], got {tuple(Bmat.shape)}")
+        _contig(A, Bmat)
+        _elem_ok(A, dtype, "A")
+        _elem_ok(Bmat, dtype, "Bmat")
+        nbytes = int(lib().dspark_markov_state_bytes(V, rank, dtype))
+        self.state = torch.empty(nbytes + 256, dtype=torch.uint8, device=A.device)
+        pad = (-self.state.data_ptr()) % 256  # the library wants 256-byte alignment
+        self._state_ptr = self.state.data_ptr() + pad
+        self.A, self.Bmat, self.dtype, self.V, self.rank = A, Bmat, dtype, V, rank
+        self.handle = dspark_markov_t()
+        _check(lib().dspark_markov_prepare(ctypes.byref(self.handle), _p(A), _p(Bmat), V, rank, dtype,
+                                           self._state_ptr, nbytes, _stream(stream)))
+        self._ref = ctypes.byref(self.handle)
+
+    @property
+    def Bt(self):
+        """The prepared transposed factor [V, rank] (a view into the state)."""
+        import torch
+        off = self._state_ptr - self.state.data_ptr() + MARKOV_HEADER_BYTES
+        esz = 2 if self.dtype == DSPARK_BF16 else 4
+        raw = self.state[off:off + self.V * self.rank * esz]
+        return raw.view(torch.int16 if esz == 2 else torch.float32).view(self.V, self.rank)
 
 
-def dspark_chain(base, A, Bt, dtype: int, prev0, tokens, chained_logits=None, status=None, ws=None, stream=None):
+def dspark_markov_prepare(A, Bmat, dtype: int, stream=None) -> MarkovHead:
+    """Start-up preparation of the Markov head (see MarkovHead)."""
+    return MarkovHead(A, Bmat, dtype, stream)
+
+
+def dspark_set_chain_form(form: int):
+    """Stage 1's form for later calls: CHAIN_PRUNED (default) or CHAIN_DENSE."""
+    _check(lib().dspark_set_chain_form(form))
+
+
+def dspark_get_chain_form() -> int:
+    return int(lib().dspark_get_chain_form())
+
+
+def _shape(t, want, what):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{what} must be {list(want)}, got {list(t.shape)}")
+
+
+def _chain_checks(base, markov: MarkovHead, prev0, tokens, chained_logits, what):
+    if base.dim() != 3:
+        raise ValueError(f"{what}: base must be [R, K, V]")
     R, K, V = base.shape
-    rank = A.shape[1]
-    if tuple(A.shape) != (V, rank) or tuple(Bt.shape) != (V, rank) or tuple(prev0.shape) != (R,) \
-            or tuple(tokens.shape) != (R, K):
-        raise ValueError("dspark_chain: inconsistent shapes")
-    if chained_logits is not None and tuple(chained_logits.shape) != (R, K, V):
-        raise ValueError("dspark_chain: chained_logits must be [R, K, V]")
-    _contig(base, A, Bt, prev0, tokens, chained_logits)
-    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
-        _elem_ok(t, dtype, n)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().dspark_chain(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(tokens),
-                              _p(chained_logits), _p(status), _p(ws), wsb, _stream(stream)))
+    if V != markov.V:
+        raise ValueError(f"{what}: base has V={V}, the Markov head V={markov.V}")
+    _shape(prev0, (R,), f"{what}: prev0")
+    _shape(tokens, (R, K), f"{what}: tokens")
+    if chained_logits is not None:
+        _shape(chained_logits, (R, K, V), f"{what}: chained_logits")
+    _contig(base, prev0, tokens, chained_logits)
+    _elem_ok(base, markov.dtype, "base")
+    if prev0.element_size() != 4 or tokens.element_size() != 4:
+        raise ValueError(f"{what}: prev0 and tokens must be int32")
+    return R, K, V
 
 
-def dspark_chain_sample(base, A, Bt, dtype: int, prev0, temperature: float, seed: int, tokens, chained_logits=None,
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def dspark_chain(base, markov: MarkovHead, prev0, tokens, chained_logits=None, status=None, ws=None, stream=None):
+    R, K, V = _chain_checks(base, markov, prev0, tokens, chained_logits, "dspark_chain")
+    _check(lib().dspark_chain(_p(base), _p(markov.A), _p(markov.Bmat), markov.dtype, _p(prev0), R, K, V,
+                              markov.rank, markov._ref, _p(tokens), _p(chained_logits), _p(status), _p(ws),
+                              _ws_bytes(ws), _stream(stream)))
+
+
+def dspark_chain_sample(base, markov: MarkovHead, prev0, temperature: float, seed: int, tokens, chained_logits=None,
                         status=None, ws=None, stream=None):
     """Stage 1 with Gumbel-max sampling of softmax(x / temperature) (Philox4x32-10 keyed on seed)."""
-    R, K, V = base.shape
-    rank = A.shape[1]
-    if tuple(A.shape) != (V, rank) or tuple(Bt.shape) != (V, rank) or tuple(prev0.shape) != (R,) \
-            or tuple(tokens.shape) != (R, K):
-        raise ValueError("dspark_chain_sample: inconsistent shapes")
-    if chained_logits is not None and tuple(chained_logits.shape) != (R, K, V):
-        raise ValueError("dspark_chain_sample: chained_logits must be [R, K, V]")
-    _contig(base, A, Bt, prev0, tokens, chained_logits)
-    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
-        _elem_ok(t, dtype, n)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().dspark_chain_sample(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, float(temperature),
+    R, K, V = _chain_checks(base, markov, prev0, tokens, chained_logits, "dspark_chain_sample")
+    _check(lib().dspark_chain_sample(_p(base), _p(markov.A), _p(markov.Bmat), markov.dtype, _p(prev0), R, K, V,
+                                     markov.rank, markov._ref, float(temperature),
                                      int(seed) & 0xFFFFFFFFFFFFFFFF, _p(tokens), _p(chained_logits), _p(status),
-                                     _p(ws), wsb, _stream(stream)))
+                                     _p(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def dspark_survival(conf, surv, status=None, stream=None):
@@ -207,22 +271,43 @@ def dspark_allocate(order, b_star, R: int, K: int, prefix_len, offsets, ver_idx,
                                  _p(ver_idx), _p(ver_tokens), _stream(stream)))
 
 
-def dspark_step(base, A, Bt, dtype: int, prev0, conf, n_sampling: int, T: int, num_reqs: int, verify_cost,
+def _step_checks(base, markov: MarkovHead, prev0, conf, verify_cost, draft_cost, out: "StepBuffers", ws, status,
+                 what):
+    R, K, V = _chain_checks(base, markov, prev0, out.tokens, None, what)
+    _shape(conf, (R, K), f"{what}: conf")
+    for t, n in ((conf, "conf"), (verify_cost, "verify_cost"), (draft_cost, "draft_cost")):
+        if t.dtype != _torch().float32:
+            raise ValueError(f"{what}: {n} must be float32")
+    _contig(conf, verify_cost, draft_cost)
+    n = R * K
+    for t, want, name in ((out.order, n, "order"), (out.ver_idx, n, "ver_idx"), (out.ver_tokens, n, "ver_tokens"),
+                          (out.surv, n, "surv"), (out.sorted_surv, n, "sorted_surv"), (out.prefix_len, R, "prefix_len"),
+                          (out.offsets, R + 1, "offsets"), (out.b_star, 1, "b_star"), (out.best_obj, 1, "best_obj")):
+        if t.numel() < want:
+            raise ValueError(f"{what}: out.{name} holds {t.numel()} entries, {want} needed")
+    if status is not None and (status.numel() < 1 or status.element_size() != 4):
+        raise ValueError(f"{what}: status must hold one 32-bit word")
+    need = dspark_workspace_bytes(R, K, V, markov.rank, markov.dtype)
+    if _ws_bytes(ws) < need:
+        raise ValueError(f"{what}: workspace of {need} bytes needed, {_ws_bytes(ws)} given")
+    return R, K, V
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dspark_step(base, markov: MarkovHead, prev0, conf, n_sampling: int, T: int, num_reqs: int, verify_cost,
                 draft_cost, out: "StepBuffers", ws, status=None, stream=None):
     """The whole pass (chain + schedule) into the buffers of `out`."""
-    R, K, V = base.shape
-    rank = A.shape[1]
-    if tuple(conf.shape) != (R, K):
-        raise ValueError("dspark_step: conf must be [R, K]")
-    _contig(base, A, Bt, prev0, conf, verify_cost, draft_cost)
-    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
-        _elem_ok(t, dtype, n)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().dspark_step(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(conf), n_sampling, T,
-                             num_reqs, _p(verify_cost), verify_cost.numel(), _p(draft_cost), draft_cost.numel(),
-                             _p(out.tokens), _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
-                             _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
-                             _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+    R, K, V = _step_checks(base, markov, prev0, conf, verify_cost, draft_cost, out, ws, status, "dspark_step")
+    _check(lib().dspark_step(_p(base), _p(markov.A), _p(markov.Bmat), markov.dtype, _p(prev0), R, K, V, markov.rank,
+                             markov._ref, _p(conf), n_sampling, T, num_reqs, _p(verify_cost), verify_cost.numel(),
+                             _p(draft_cost), draft_cost.numel(), _p(out.tokens), _p(out.surv), _p(out.order),
+                             _p(out.sorted_surv), _p(out.b_star), _p(out.best_obj), _p(out.prefix_len),
+                             _p(out.offsets), _p(out.ver_idx), _p(out.ver_tokens), _p(status), _p(ws),
+                             _ws_bytes(ws), _stream(stream)))
 
 
 def dspark_schedule(conf, n_sampling: int, T: int, num_reqs: int, verify_cost, draft_cost, out: "StepBuffers",
@@ -245,29 +330,79 @@ def dspark_schedule(conf, n_sampling: int, T: int, num_reqs: int, verify_cost, d
                                  _p(out.ver_tokens) if tokens is not None else None, _p(status), _stream(stream)))
 
 
-def dspark_step_sized(base, A, Bt, dtype: int, prev0, conf, size_conf, rule: int, n_sampling: int, T: int,
+def dspark_step_sized(base, markov: MarkovHead, prev0, conf, size_conf, rule: int, n_sampling: int, T: int,
                       num_reqs: int, verify_cost, draft_cost, out: "StepBuffers", ws, status=None, stream=None):
     """dspark_step with B sized from `size_conf` ([R', K], e.g. an older step's confidences, or
     None for the current ones) under admission rule `rule`."""
-    R, K, V = base.shape
-    rank = A.shape[1]
-    if tuple(conf.shape) != (R, K):
-        raise ValueError("dspark_step_sized: conf must be [R, K]")
+    R, K, V = _step_checks(base, markov, prev0, conf, verify_cost, draft_cost, out, ws, status, "dspark_step_sized")
     size_R = -1                      # -1: size from conf itself
     if size_conf is not None:
-        if size_conf.dim() != 2 or size_conf.shape[1] != K:
-            raise ValueError("dspark_step_sized: size_conf must be [R', K]")
+        if size_conf.dim() != 2 or size_conf.shape[1] != K or size_conf.dtype != _torch().float32:
+            raise ValueError("dspark_step_sized: size_conf must be float32 [R', K]")
         size_R = size_conf.shape[0]
-    _contig(base, A, Bt, prev0, conf, size_conf, verify_cost, draft_cost)
-    for t, n in ((base, "base"), (A, "A"), (Bt, "Bt")):
-        _elem_ok(t, dtype, n)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().dspark_step_sized(_p(base), _p(A), _p(Bt), dtype, _p(prev0), R, K, V, rank, _p(conf),
-                                   _p(size_conf), size_R, rule, n_sampling, T, num_reqs, _p(verify_cost),
-                                   verify_cost.numel(), _p(draft_cost), draft_cost.numel(), _p(out.tokens),
-                                   _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
-                                   _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
-                                   _p(out.ver_tokens), _p(status), _p(ws), wsb, _stream(stream)))
+    _contig(size_conf)
+    _check(lib().dspark_step_sized(_p(base), _p(markov.A), _p(markov.Bmat), markov.dtype, _p(prev0), R, K, V,
+                                   markov.rank, markov._ref, _p(conf), _p(size_conf), size_R, rule, n_sampling, T,
+                                   num_reqs, _p(verify_cost), verify_cost.numel(), _p(draft_cost),
+                                   draft_cost.numel(), _p(out.tokens), _p(out.surv), _p(out.order),
+                                   _p(out.sorted_surv), _p(out.b_star), _p(out.best_obj), _p(out.prefix_len),
+                                   _p(out.offsets), _p(out.ver_idx), _p(out.ver_tokens), _p(status), _p(ws),
+                                   _ws_bytes(ws), _stream(stream)))
+
+
+class StepPlan:
+    """dspark_step (or dspark_step_sized) with every argument that stays fixed across
+    steps -- the head, the scalars, the cost tables, the output buffers, the workspace,
+    the status word and the stream -- checked and marshalled once.  A call passes the
+    step's own inputs (base, prev0, conf and, when sized, size_conf) and makes one C
+    call after cheap shape checks."""
+
+    def __init__(self, markov: MarkovHead, R: int, K: int, n_sampling: int, T: int, num_reqs: int, verify_cost,
+                 draft_cost, out: "StepBuffers", ws, status=None, stream=None, rule: int = None):
+        torch = _torch()
+        dev = markov.A.device
+        base0 = torch.empty((R, K, markov.V), dtype=markov.A.dtype, device=dev)
+        prev0 = torch.empty(R, dtype=torch.int32, device=dev)
+        conf0 = torch.empty((R, K), dtype=torch.float32, device=dev)
+        _step_checks(base0, markov, prev0, conf0, verify_cost, draft_cost, out, ws, status, "StepPlan")
+        del base0, prev0, conf0
+        self.shape = (R, K, markov.V)
+        self.rule = rule
+        self.markov, self.verify_cost, self.draft_cost, self.out, self.ws, self.status = (
+            markov, verify_cost, draft_cost, out, ws, status)
+        vp = ctypes.c_void_p
+        tail = [vp(_p(out.tokens)), vp(_p(out.surv)), vp(_p(out.order)), vp(_p(out.sorted_surv)),
+                vp(_p(out.b_star)), vp(_p(out.best_obj)), vp(_p(out.prefix_len)), vp(_p(out.offsets)),
+                vp(_p(out.ver_idx)), vp(_p(out.ver_tokens)), vp(_p(status)), vp(_p(ws)),
+                ctypes.c_size_t(_ws_bytes(ws)), vp(_stream(stream))]
+        head = [None, vp(_p(markov.A)), vp(_p(markov.Bmat)), ctypes.c_int(markov.dtype), None, ctypes.c_int(R),
+                ctypes.c_int(K), ctypes.c_int(markov.V), ctypes.c_int(markov.rank), markov._ref, None]
+        scal = [ctypes.c_int(n_sampling), ctypes.c_int(T), ctypes.c_int(num_reqs), vp(_p(verify_cost)),
+                ctypes.c_int(verify_cost.numel()), vp(_p(draft_cost)), ctypes.c_int(draft_cost.numel())]
+        if rule is None:
+            self._fn = lib().dspark_step
+            self._args = head + scal + tail
+        else:
+            self._fn = lib().dspark_step_sized
+            self._args = head + [None, None, ctypes.c_int(rule)] + scal + tail
+
+    def __call__(self, base, prev0, conf, size_conf=None):
+        if tuple(base.shape) != self.shape or prev0.shape[0] != self.shape[0] or tuple(conf.shape) != self.shape[:2]:
+            raise ValueError("StepPlan: input shapes differ from the plan's")
+        args = self._args
+        args[0] = base.data_ptr()
+        args[4] = prev0.data_ptr()
+        args[10] = conf.data_ptr()
+        if self.rule is not None:
+            if size_conf is None:
+                args[11], args[12] = None, -1
+            else:
+                if size_conf.dim() != 2 or size_conf.shape[1] != self.shape[1]:
+                    raise ValueError("StepPlan: size_conf must be [R', K]")
+                args[11], args[12] = size_conf.data_ptr(), size_conf.shape[0]
+        rc = self._fn(*args)
+        if rc != 0:
+            _check(rc)
 
 
 def dspark_accept_greedy(ver_tokens, offsets, target, R: int, K: int, accept_len, next_prev0, out_tokens=None,

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspark.so")
-SOURCES = ["chain.hip", "sched.hip", "step.hip", "accept.hip", "api.hip"]
+SOURCES = ["chain.hip", "cand.hip", "sched.hip", "step.hip", "accept.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

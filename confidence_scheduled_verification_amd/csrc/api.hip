@@ -19,6 +19,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 std::atomic<int> g_launch_mode{DSPARK_LAUNCH_RESIDENT};
+std::atomic<int> g_chain_form{DSPARK_CHAIN_PRUNED};
 thread_local hipEvent_t g_ev_before_chain = nullptr;
 thread_local hipEvent_t g_ev_after_chain = nullptr;
 
@@ -53,6 +54,64 @@ int coop_launch() { return g_launch_mode.load(std::memory_order_relaxed) == DSPA
 
 size_t keys_bytes(int R, int K) { return dspark::ws_total_bytes(R, K); }
 
+// Workspace bytes a call of this shape needs: the dense paths' region, then for bf16 the
+// pruned chain's candidate buffers.
+size_t ws_need(int R, int K, int V, int dtype) {
+    return keys_bytes(R, K) + (dtype == DSPARK_BF16 ? dspark::ws_cand_bytes(R, K, V) : 0);
+}
+
+int check_markov(const dspark_markov_t* m, const void* A, const void* Bmat, int V, int rank, int dtype) {
+    if (!m) return fail(DSPARK_EINVAL, "markov: NULL handle (prepare the head with dspark_markov_prepare)");
+    if (m->magic != DSPARK_MARKOV_MAGIC || !m->state)
+        return fail(DSPARK_EINVAL, "markov: the handle was not prepared (dspark_markov_prepare)");
+    if (m->A != A || m->Bmat != Bmat)
+        return fail(DSPARK_EINVAL, "markov: the handle was prepared from other A / Bmat pointers");
+    if (m->V != V || m->rank != rank || m->dtype != dtype)
+        return fail(DSPARK_EINVAL, "markov: the handle was prepared for V=%d rank=%d dtype=%d, the call has V=%d "
+                                   "rank=%d dtype=%d", m->V, m->rank, m->dtype, V, rank, dtype);
+    return DSPARK_OK;
+}
+
+const void* markov_bt(const dspark_markov_t* m) { return (const char*)m->state + dspark::kMarkovHeaderBytes; }
+
+// The pruned chain applies to bf16 with K <= DSPARK_PRUNED_MAX_K and V <= DSPARK_PRUNED_MAX_V
+// when no chained logits are asked for and the pruned form is selected.
+bool use_pruned(int dtype, int R, int K, int V, const void* A, const float* chained_logits) {
+    // the per-row counters hold DSPARK_MAX_SLOTS rows; key rows are read 16 bytes at a time
+    return g_chain_form.load(std::memory_order_relaxed) == DSPARK_CHAIN_PRUNED && dtype == DSPARK_BF16 &&
+           chained_logits == nullptr && K <= DSPARK_PRUNED_MAX_K && V <= DSPARK_PRUNED_MAX_V &&
+           (long long)R * K <= DSPARK_MAX_SLOTS && ((uintptr_t)A & 15u) == 0;
+}
+
+dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int32_t* prev0, int R, int K, int V,
+                           int rank, int32_t* tokens, uint32_t* status, void* ws) {
+    char* w = (char*)ws;
+    uint32_t* ctr = (uint32_t*)(w + dspark::ws_sync_bytes());
+    char* tail = w + keys_bytes(R, K);
+    dspark::CandArgs a{};
+    a.base = (const uint16_t*)base;
+    a.A = (const uint16_t*)m->A;
+    a.Bt = (const uint16_t*)markov_bt(m);
+    a.hdr = m->state;
+    a.prev0 = prev0;
+    a.R = R;
+    a.K = K;
+    a.V = V;
+    a.rank = rank;
+    a.NC = dspark::cand_items_per_row(V);
+    a.tokens = tokens;
+    a.status = status;
+    a.rowkey = ctr;
+    a.rownan = ctr + dspark::kMaxSlotsWs;
+    a.done = ctr + 2 * dspark::kMaxSlotsWs;
+    a.next = ctr + 3 * dspark::kMaxSlotsWs;
+    a.exited = a.next + 1;
+    a.wave_cap = (uint32_t)dspark::cand_wave_cap(R, K, V);
+    a.dir = (uint64_t*)tail;
+    a.ent = (uint64_t*)(tail + dspark::ws_round((size_t)R * K * a.NC * 8));
+    return a;
+}
+
 int check_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
                 int V, int rank, const int32_t* tokens) {
     if (R < 0 || K < 0) return fail(DSPARK_EINVAL, "chain: negative R (%d) or K (%d)", R, K);
@@ -73,8 +132,8 @@ int check_chain(const void* base, const void* A, const void* Bt, int dtype, cons
     return DSPARK_OK;
 }
 
-int check_ws(void* ws, size_t ws_bytes, int R, int K) {
-    const size_t need = keys_bytes(R, K);
+int check_ws(void* ws, size_t ws_bytes, int R, int K, int V, int dtype) {
+    const size_t need = ws_need(R, K, V, dtype);
     if (!ws || ws_bytes < need)
         return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
                     ws ? "" : " (NULL)");
@@ -103,32 +162,61 @@ const char* dspark_last_error(void) { return g_err; }
 const char* dspark_version(void) { return "dspark-gfx950 0.1"; }
 
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype) {
-    (void)V;
     (void)rank;
-    (void)dtype;
     if (R <= 0 || K <= 0) return 0;
-    return keys_bytes(R, K);
+    return ws_need(R, K, V < 1 ? 1 : V, dtype);
 }
 
-int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt, void* stream) {
-    if (!Bmat || !Bt) return fail(DSPARK_EINVAL, "markov_prepare: NULL pointer");
+size_t dspark_markov_state_bytes(int V, int rank, int dtype) {
+    if (V < 1 || rank < 1) return 0;
+    return dspark::kMarkovHeaderBytes + (size_t)V * (size_t)rank * (dtype == DSPARK_BF16 ? 2 : 4);
+}
+
+int dspark_markov_prepare(dspark_markov_t* m, const void* A, const void* Bmat, int V, int rank, int dtype,
+                          void* state, size_t state_bytes, void* stream) {
+    if (!m || !A || !Bmat || !state) return fail(DSPARK_EINVAL, "markov_prepare: NULL pointer");
+    m->magic = 0;
     if (rank < 1 || V < 1) return fail(DSPARK_EINVAL, "markov_prepare: rank %d and V %d must be >= 1", rank, V);
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16)
         return fail(DSPARK_EINVAL, "markov_prepare: unknown dtype %d", dtype);
-    const hipError_t e = dspark::launch_transpose(Bmat, rank, V, dtype == DSPARK_BF16 ? 2 : 4, Bt,
-                                                  (hipStream_t)stream);
-    return e == hipSuccess ? DSPARK_OK : hip_fail(e, "markov_prepare");
+    if (((uintptr_t)state & 255u) != 0) return fail(DSPARK_EINVAL, "markov_prepare: state must be 256-byte aligned");
+    if (state_bytes < dspark_markov_state_bytes(V, rank, dtype))
+        return fail(DSPARK_EWORKSPACE, "markov_prepare: state of %zu bytes needed, %zu given",
+                    dspark_markov_state_bytes(V, rank, dtype), state_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    void* Bt = (char*)state + dspark::kMarkovHeaderBytes;
+    hipError_t e = dspark::launch_transpose(Bmat, rank, V, dtype == DSPARK_BF16 ? 2 : 4, Bt, s);
+    if (e == hipSuccess && dtype == DSPARK_BF16) e = dspark::launch_markov_bound(A, Bt, V, rank, state, s);
+    if (e != hipSuccess) return hip_fail(e, "markov_prepare");
+    *m = dspark_markov_t{DSPARK_MARKOV_MAGIC, A, Bmat, state, state_bytes, V, rank, dtype, 0};
+    return DSPARK_OK;
 }
 
-int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
-                 int V, int rank, int32_t* tokens, float* chained_logits, uint32_t* status, void* ws,
-                 size_t ws_bytes, void* stream) {
-    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+int dspark_set_chain_form(int form) {
+    if (form != DSPARK_CHAIN_PRUNED && form != DSPARK_CHAIN_DENSE)
+        return fail(DSPARK_EINVAL, "set_chain_form: unknown form %d", form);
+    g_chain_form.store(form, std::memory_order_relaxed);
+    return DSPARK_OK;
+}
+
+int dspark_get_chain_form(void) { return g_chain_form.load(std::memory_order_relaxed); }
+
+int dspark_chain(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0, int R, int K,
+                 int V, int rank, const dspark_markov_t* markov, int32_t* tokens, float* chained_logits,
+                 uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_chain(base, A, Bmat, dtype, prev0, R, K, V, rank, tokens);
     if (rc != DSPARK_OK) return rc;
     if (R == 0 || K == 0) return DSPARK_OK;
-    if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    if ((rc = check_markov(markov, A, Bmat, V, rank, dtype)) != DSPARK_OK) return rc;
+    if ((rc = check_ws(ws, ws_bytes, R, K, V, dtype)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
+    const void* Bt = markov_bt(markov);
+    if (use_pruned(dtype, R, K, V, A, chained_logits)) {
+        const hipError_t e = dspark::launch_cand(cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws),
+                                                 num_cu(), s);
+        return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain (pruned)");
+    }
+    char* chain_ws = (char*)ws + dspark::ws_chain_off();
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
                         V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
                         (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)), dspark::SampleArgs{},
@@ -141,19 +229,22 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain (finalize)");
 }
 
-int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R,
-                        int K, int V, int rank, float temperature, uint64_t seed, int32_t* tokens,
-                        float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+int dspark_chain_sample(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0, int R,
+                        int K, int V, int rank, const dspark_markov_t* markov, float temperature, uint64_t seed,
+                        int32_t* tokens, float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes,
+                        void* stream) {
+    int rc = check_chain(base, A, Bmat, dtype, prev0, R, K, V, rank, tokens);
     if (rc != DSPARK_OK) return rc;
     const float scale = 1.4426950408889634f / temperature;  // log2(e) / temperature
     if (!(temperature > 0.f) || !isfinite(temperature) || !isfinite(scale))
         return fail(DSPARK_ERANGE, "chain_sample: temperature %g must be positive, finite and invertible",
                     (double)temperature);
     if (R == 0 || K == 0) return DSPARK_OK;
-    if ((rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    if ((rc = check_markov(markov, A, Bmat, V, rank, dtype)) != DSPARK_OK) return rc;
+    if ((rc = check_ws(ws, ws_bytes, R, K, V, dtype)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
+    const void* Bt = markov_bt(markov);
+    char* chain_ws = (char*)ws + dspark::ws_chain_off();
     dspark::ChainArgs a{base,   A,  Bt,   dtype,          prev0,  R,           K,
                         V,      rank, tokens, chained_logits, status, (uint64_t*)chain_ws,
                         (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
@@ -217,14 +308,15 @@ int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, c
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "allocate");
 }
 
-int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R,
-                      int K, int V, int rank, const float* conf, const float* size_conf, int size_R, int rule,
+int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0, int R,
+                      int K, int V, int rank, const dspark_markov_t* markov, const float* conf,
+                      const float* size_conf, int size_R, int rule,
                       int n_sampling, int T, int num_reqs, const float* verify_cost, int verify_len,
                       const float* draft_cost, int draft_len, int32_t* tokens, float* surv, int32_t* order,
                       float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len, int32_t* offsets,
                       int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws, size_t ws_bytes,
                       void* stream) {
-    int rc = check_chain(base, A, Bt, dtype, prev0, R, K, V, rank, tokens);
+    int rc = check_chain(base, A, Bmat, dtype, prev0, R, K, V, rank, tokens);
     if (rc != DSPARK_OK) return rc;
     const long long n = (long long)R * K;
     if (n > DSPARK_MAX_SLOTS) return fail(DSPARK_EUNSUPPORTED, "step: %lld slots exceed %d", n, DSPARK_MAX_SLOTS);
@@ -240,18 +332,35 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
     if (stale && ns > 0 && !size_conf) return fail(DSPARK_EINVAL, "step: NULL size_conf with %d rows", size_R);
     rc = check_sched_scalars((int)n, n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len);
     if (rc != DSPARK_OK) return rc;
-    if (n > 0 && (rc = check_ws(ws, ws_bytes, R, K)) != DSPARK_OK) return rc;
+    if (n > 0 && (rc = check_markov(markov, A, Bmat, V, rank, dtype)) != DSPARK_OK) return rc;
+    if (n > 0 && (rc = check_ws(ws, ws_bytes, R, K, V, dtype)) != DSPARK_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
+    const void* Bt = n > 0 ? markov_bt(markov) : nullptr;
     const int bmax = std::min((int)n, verify_len - 1 - T);
     const dspark::SizingArgs sizing{stale ? 1 : 0, size_conf, stale ? size_R : R,
                                     std::min((int)ns, verify_len - 1 - T), rule};
     hipError_t e;
+    if (n > 0 && use_pruned(dtype, R, K, V, A, nullptr)) {
+        // the chain, then stages 2-5 over the confidences and the verified tokens
+        if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
+            return hip_fail(e, "step (timing event)");
+        e = dspark::launch_cand(cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws), num_cu(), s);
+        if (e != hipSuccess) return hip_fail(e, "step (pruned chain)");
+        if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
+            return hip_fail(e, "step (timing event)");
+        dspark::FusedSchedArgs sa{conf,   R,        K,          n_sampling, T,      num_reqs, verify_cost,
+                                  draft_cost, bmax, sizing,    surv,       order,  sorted_surv, b_star,
+                                  best_obj, prefix_len, offsets, ver_idx,   status, nullptr, 0,
+                                  tokens,   ver_tokens};
+        e = dspark::launch_sched_fused(sa, s);
+        return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (schedule)");
+    }
     if (n > 0) {
         // One launch for the whole step when its grid fits on the device at once (fp32
         // factors: small batches only).
         char* w = (char*)ws;
         dspark::StepArgs st{base, A, Bt, prev0, R, K, V, rank, tokens, status,
-                            (uint64_t*)(w + dspark::ws_sync_bytes()), (uint32_t*)w, conf,
+                            (uint64_t*)(w + dspark::ws_chain_off()), (uint32_t*)w, conf,
                             n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, sizing, surv, order,
                             sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens,
                             coop_launch()};
@@ -268,12 +377,12 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
     }
     dspark::FusedSchedArgs sa{conf, R, K, n_sampling, T, num_reqs, verify_cost, draft_cost, bmax, sizing, surv, order,
                               sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, status,
-                              (uint64_t*)((char*)ws + dspark::ws_sync_bytes()),
+                              (uint64_t*)((char*)ws + dspark::ws_chain_off()),
                               n > 0 ? (int)(dspark::ws_chain_bytes(R, K) / 8) : 0};
     e = dspark::launch_sched_fused(sa, s);
     if (e != hipSuccess) return hip_fail(e, "step (schedule)");
     if (n == 0) return DSPARK_OK;
-    char* chain_ws = (char*)ws + dspark::ws_sync_bytes();
+    char* chain_ws = (char*)ws + dspark::ws_chain_off();
     dspark::ChainArgs a{base,    A,      Bt,     dtype, prev0, R, K, V, rank, tokens, nullptr, status,
                         (uint64_t*)chain_ws, (uint32_t*)(chain_ws + dspark::ws_keys_bytes(R, K)),
                         dspark::SampleArgs{}, coop_launch()};
@@ -287,13 +396,14 @@ int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype
     return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (finalize)");
 }
 
-int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0, int R, int K,
-                int V, int rank, const float* conf, int n_sampling, int T, int num_reqs, const float* verify_cost,
+int dspark_step(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0, int R, int K,
+                int V, int rank, const dspark_markov_t* markov, const float* conf, int n_sampling, int T,
+                int num_reqs, const float* verify_cost,
                 int verify_len, const float* draft_cost, int draft_len, int32_t* tokens, float* surv,
                 int32_t* order, float* sorted_surv, int32_t* b_star, double* best_obj, int32_t* prefix_len,
                 int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens, uint32_t* status, void* ws,
                 size_t ws_bytes, void* stream) {
-    return dspark_step_sized(base, A, Bt, dtype, prev0, R, K, V, rank, conf, nullptr, -1, DSPARK_RULE_ARGMAX,
+    return dspark_step_sized(base, A, Bmat, dtype, prev0, R, K, V, rank, markov, conf, nullptr, -1, DSPARK_RULE_ARGMAX,
                              n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len, tokens, surv,
                              order, sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens, status,
                              ws, ws_bytes, stream);

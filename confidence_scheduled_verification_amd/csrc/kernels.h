@@ -30,7 +30,12 @@ inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
 // Keys and chain counters: what the stage-wise paths clear.
 inline size_t ws_chain_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
-inline size_t ws_total_bytes(int R, int K) { return ws_sync_bytes() + ws_chain_bytes(R, K); }
+// The pruned chain's counters at a fixed offset (so that calls of every shape find them
+// at zero): row maxima and NaN marks (one u32 per slot each), per-request item counts,
+// then the chunk counter and the count of waves done with the streaming.
+inline size_t ws_cand_ctr_bytes() { return ws_round((size_t)kMaxSlotsWs * 4 * 3 + 8); }
+inline size_t ws_chain_off() { return ws_sync_bytes() + ws_cand_ctr_bytes(); }
+inline size_t ws_total_bytes(int R, int K) { return ws_chain_off() + ws_chain_bytes(R, K); }
 
 // Probabilistic drafting: Gumbel-max sampling of softmax(x / temperature) with
 // Philox4x32-10 random numbers keyed on the 64-bit seed (k0 low word, k1 high word).
@@ -133,6 +138,54 @@ struct StepArgs {
     int coop;  // cooperative launch (1) or plain launch of a resident grid (0)
 };
 
+// Candidate-pruned chain (cand.hip).  Limits of that path: K <= kCandMaxK positions and
+// V <= kCandMaxItems * 4096 entries per row (its per-request directory lives in LDS).
+constexpr int kCandMaxK = 32;
+constexpr int kCandMaxItems = 64;
+constexpr int kCandItem = 4096;           // base entries per streaming item
+constexpr int kCandListCap = 2048;        // filtered candidates of one request in LDS
+constexpr int kCandWaveCap = 1024;        // least candidate-pool entries per streaming wave
+constexpr int kCandWaveStage = 256;       // candidates a wave stages in LDS between write-outs
+constexpr int kCandWaveItems = 256;       // items a wave stages between write-outs
+constexpr int kCandMaxGroups = 256;       // streaming workgroups a workspace is sized for
+constexpr int kCandWaves = kCandMaxGroups * 16;
+constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, then Bt
+
+inline int cand_items_per_row(int V) { return (V + kCandItem - 1) / kCandItem; }
+// Candidate-pool entries per streaming wave for this shape: kCandWaveCap, or 64 per
+// item of the wave's average share if that is more (items hold a few tens at most).
+inline size_t cand_wave_cap(int R, int K, int V) {
+    const size_t items = (size_t)R * K * cand_items_per_row(V);
+    const size_t per_wave = (items + kCandWaves - 1) / kCandWaves;
+    return per_wave * 64 > (size_t)kCandWaveCap ? per_wave * 64 : (size_t)kCandWaveCap;
+}
+// After ws_total_bytes(R, K), bf16 workspaces hold the pruned chain's item directory
+// [R*K*items] u64 and the wave buffers [kCandWaves][kCandWaveCap] u64, rewritten by
+// every launch.  (Its counters sit at ws_sync_bytes(), zero between launches: each
+// chain puts its request's back.)
+inline size_t ws_cand_bytes(int R, int K, int V) {
+    return ws_round((size_t)R * K * cand_items_per_row(V) * 8) + (size_t)kCandWaves * cand_wave_cap(R, K, V) * 8;
+}
+
+struct CandArgs {
+    const uint16_t* base;
+    const uint16_t* A;
+    const uint16_t* Bt;
+    const void* hdr;   // prepared bound scalars (device)
+    const int32_t* prev0;
+    int R, K, V, rank, NC;
+    int32_t* tokens;
+    uint32_t* status;
+    uint32_t* rowkey;  // [R*K] row maxima (order-preserving image)
+    uint32_t* rownan;  // [R*K] ~(first NaN index), 0 = none
+    uint32_t* done;    // [R] items streamed per request
+    uint32_t* next;    // [1] chunks handed out
+    uint32_t* exited;  // [1] waves done with the streaming
+    uint64_t* dir;     // [R*K*NC] per item: (first entry << 32) | count
+    uint64_t* ent;     // [waves * wave_cap] (index << 32) | value bits
+    uint32_t wave_cap; // candidate-pool entries per wave
+};
+
 int chain_tile_vocab();
 // Persistent kernels (the single-launch step, the single-launch chain) keep every
 // workgroup resident and synchronise them through counters in the workspace.  They are
@@ -153,6 +206,13 @@ hipError_t launch_chain_positions(const ChainArgs& a, int num_cu, hipStream_t s)
 hipError_t launch_chain_finalize(const uint64_t* keys, int32_t* tokens, int R, int K, const int32_t* ver_idx,
                                  const int32_t* b_star, int32_t* ver_tokens, hipStream_t s);
 hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes, void* dst, hipStream_t s);
+// Bound scalars of a prepared bf16 Markov head into hdr (kMarkovHeaderBytes): the largest
+// squared row norms of A and Bt, then 2 max|A| max|Bt| (1 + 2^-10) rounded up and a flag
+// that it is finite.
+hipError_t launch_markov_bound(const void* A, const void* Bt, int V, int rank, void* hdr, hipStream_t s);
+// The candidate-pruned chain, one 1024-thread workgroup per compute unit (at most
+// kCandMaxGroups of them).
+hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s);
 
 hipError_t launch_survival(const float* conf, int R, int K, float* surv, uint32_t* status, hipStream_t s);
 hipError_t launch_topb(const float* surv, int R, int K, int32_t* order, float* sorted_surv, int32_t* rank,

@@ -88,6 +88,12 @@ WORKLOADS = {
                       base_std=2.0, factor_std=0.05, conf_a=2.0, conf_b=0.35, conf_eps=0.3,
                       verify_len=16385, graph_max=4096, verify_base=2000.0, verify_slope=1.0,
                       jump_us=3000.0, noise=0.0, seed=4),
+    # one GPU's share of the headline chain under an 8-way vocabulary split (tensor
+    # parallelism 8, as the vLLM blog's "Results" deployment): V / 8 columns, every request
+    "shard": Workload("shard", R=256, R_all=256, n_sampling=256, K=7, V=16160, rank=256, dtype=BF16,
+                      T=0, base_std=2.0, factor_std=0.05, conf_a=1.5, conf_b=0.45, conf_eps=0.3,
+                      verify_len=8193, graph_max=4096, verify_base=2000.0, verify_slope=1.0,
+                      jump_us=3000.0, noise=0.03, seed=5),
     # scheduler-only sweep: 1024 requests x 15 positions, same confidence law and tables as "large"
     "sweep": Workload("sweep", R=1024, R_all=1024, n_sampling=1024, K=15, V=0, rank=0, dtype=BF16, T=512,
                       base_std=0.0, factor_std=0.0, conf_a=2.0, conf_b=0.35, conf_eps=0.3,

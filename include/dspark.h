@@ -91,36 +91,64 @@ const char* dspark_last_error(void);
 /* Library version string. */
 const char* dspark_version(void);
 
-/* Bytes of device workspace needed by dspark_chain / dspark_step / dspark_step_sized
- * for this shape (0 when R*K == 0).  Zero-fill a workspace once, before its first
- * use: the single-launch step keeps grid-barrier counters and a ready flag in it and
- * leaves them at zero when it ends, so later calls need no further clearing.  A
- * workspace sized for one shape serves any smaller R and K. */
+/* Bytes of device workspace needed by dspark_chain / dspark_chain_sample / dspark_step /
+ * dspark_step_sized for this shape (0 when R*K == 0).  Zero-fill a workspace once, before
+ * its first use: the kernels keep counters in it (grid-barrier counters and a ready flag
+ * of the dense single-launch step; per-row and per-request counters of the pruned chain)
+ * and put each back to zero before they end, so later calls need no clearing.  A call
+ * that ends with DSPARK_STATUS_SYNC_TIMEOUT may leave counters set: zero-fill the
+ * workspace again before its next use.  A workspace sized for one shape serves any
+ * smaller R and K (and any V and rank of the same dtype); bf16 workspaces include the
+ * pruned chain's candidate buffers (about 33 MB). */
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
 
 /*
- * Start-up layout change of the Markov head's second factor.  The head's bias
- * for previous token u and candidate v is W[u,v] = sum_k A[u,k] * Bmat[k,v]
- * with A [V,rank] and Bmat [rank,V] (a rank-r factorisation; DSpark summary,
- * "Draft better").  The chain kernels read Bmat transposed, Bt [V,rank]
- * (Bt[v,k] = Bmat[k,v]), so that every candidate token's rank-r vector is
- * contiguous.  This call writes Bt from Bmat; run it once when the weights are
- * loaded, not per step.  dtype gives the element type of both arrays.
+ * Prepared state of the Markov head (start-up).  The head's bias for previous token u
+ * and candidate v is W[u,v] = sum_k A[u,k] * Bmat[k,v] with A [V,rank] and Bmat
+ * [rank,V], a rank-r factorisation (DSpark summary "How DSpark Speeds Up LLM
+ * Inference", section "Draft better").  dspark_markov_prepare writes, into the caller's
+ * device buffer `state`:
+ *   - Bt [V,rank], Bmat transposed (Bt[v,k] = Bmat[k,v]), so that each candidate's
+ *     rank-r vector is contiguous for the kernels;
+ *   - for bf16, the bias bound of the pruned chain: 2 max_u |A[u,:]| max_v |Bmat[:,v]|
+ *     (Euclidean norms, summed in double), times (1 + 2^-10) and rounded up, and
+ *     whether it is finite;
+ * and fills the host struct *m, which records the pointers it was prepared from.  The
+ * chain and step calls take A and Bmat as the method states them plus `m`, and refuse
+ * (DSPARK_EINVAL) a handle that was not prepared, or was prepared from other pointers,
+ * sizes or dtype -- a transposed or stale factor cannot reach the kernels.  Run it once
+ * when the weights are loaded (again if they change), not per step; it enqueues on
+ * `stream` like every call.  The caller owns A, Bmat and state; they must stay valid
+ * while m is used.  state_bytes must be at least dspark_markov_state_bytes(V, rank,
+ * dtype); state must be 256-byte aligned.
  */
-int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt, void* stream);
+#define DSPARK_MARKOV_MAGIC 0x31766b6d6b707364ull /* set in m->magic once prepared */
+typedef struct dspark_markov {
+    uint64_t magic;
+    const void* A;      /* [V,rank] device, as prepared                        */
+    const void* Bmat;   /* [rank,V] device, as prepared                        */
+    void* state;        /* device: bound scalars (256 bytes), then Bt [V,rank] */
+    size_t state_bytes;
+    int32_t V, rank, dtype, reserved;
+} dspark_markov_t;
+
+size_t dspark_markov_state_bytes(int V, int rank, int dtype);
+int dspark_markov_prepare(dspark_markov_t* m, const void* A, const void* Bmat, int V, int rank, int dtype,
+                          void* state, size_t state_bytes, void* stream);
 
 /*
  * Stage 1, chain.  For every request r, with prev = prev0[r]:
  *   for i in 0..K-1:
- *     x[v] = base[r,i,v] + sum_k A[prev,k] * Bt[v,k]      (fp32 accumulation)
+ *     x[v] = base[r,i,v] + sum_k A[prev,k] * Bmat[k,v]    (fp32 accumulation)
  *     tokens[r,i] = argmax_v x[v];  prev = tokens[r,i]
- * (DSpark summary, "Draft better": a Markov head adjusts each word's odds using
- * only the word right before it; MAX worklog, "What DSpark is": a low-rank bias
- * keyed on the previous chosen token, then an argmax.)
+ * (DSpark summary, "Draft better": a small Markov head corrects each position's scores
+ * from the previous token alone; MAX worklog, "What DSpark is": a low-rank bias keyed
+ * on the previous chosen token, then an argmax.)
  *
  *   base            [R,K,V]   backbone logits (dtype)
  *   A               [V,rank]  first factor, row u = key vector of previous token u (dtype)
- *   Bt              [V,rank]  second factor, transposed (see dspark_markov_prepare) (dtype)
+ *   Bmat            [rank,V]  second factor (dtype)
+ *   markov          the head prepared from exactly this A and Bmat (dspark_markov_prepare)
  *   prev0           [R]       int32 token preceding position 0; values outside [0,V)
  *                             are clamped and flagged with DSPARK_STATUS_PREV_CLAMPED
  *   tokens          [R,K]     int32 output
@@ -129,22 +157,44 @@ int dspark_markov_prepare(const void* Bmat, int rank, int V, int dtype, void* Bt
  *
  * argmax: the largest value wins; NaN counts as larger than every number; among
  * equal values the lowest index wins.  The returned index is always in [0,V).
- * bf16: products are exact and summed in fp32 by the matrix cores; fp32: fused
- * multiply-add in increasing k.  R == 0 or K == 0 enqueues nothing (data pointers
- * may then be NULL).
+ * How it is computed (dspark_set_chain_form): bf16 without chained_logits, K <=
+ * DSPARK_PRUNED_MAX_K and V <= DSPARK_PRUNED_MAX_V runs the pruned chain by default:
+ * one streaming pass over base keeps each row's entries within the bias bound of its
+ * maximum (the only ones that can win), then every request's chain scores those
+ * candidates alone (fp32 fused multiply-adds in increasing k within 32-entry slices,
+ * slices summed pairwise).  Rows the bound cannot prune (a non-finite bound, more
+ * candidates than the buffers hold) are scored over the whole vocabulary, so the
+ * tokens never depend on how well the bound prunes.  Otherwise (and in the dense form)
+ * bf16 products are summed in fp32 by the matrix cores over the whole vocabulary;
+ * fp32: fused multiply-add in increasing k.  Forms may differ only where two logits are
+ * within float32 rounding of each other.  R == 0 or K == 0 enqueues nothing (data
+ * pointers may then be NULL).
  * Limits: V >= 1; bf16 needs rank % 32 == 0, rank <= DSPARK_MAX_RANK_BF16 and
  * K*V <= DSPARK_MAX_KV_BF16 and V*rank <= DSPARK_MAX_VR_BF16;
  * fp32 needs 1 <= rank <= DSPARK_MAX_RANK_F32.
  */
-int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
-                 int R, int K, int V, int rank, int32_t* tokens, float* chained_logits,
-                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+int dspark_chain(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0,
+                 int R, int K, int V, int rank, const dspark_markov_t* markov, int32_t* tokens,
+                 float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Which form computes stage 1 (process-wide, for calls made after it):
+ *   DSPARK_CHAIN_PRUNED (default): the pruned chain where it applies (see dspark_chain);
+ *   DSPARK_CHAIN_DENSE: the matrix-core chain over the whole vocabulary everywhere.
+ * Returns DSPARK_EINVAL for an unknown form.
+ */
+#define DSPARK_CHAIN_PRUNED 0
+#define DSPARK_CHAIN_DENSE 1
+#define DSPARK_PRUNED_MAX_K 32
+#define DSPARK_PRUNED_MAX_V 262144
+int dspark_set_chain_form(int form);
+int dspark_get_chain_form(void);
 
 /*
  * Stage 1 with probabilistic drafting: as dspark_chain, but each position's token is
  * a SAMPLE of softmax(x / temperature) over the chained logits x instead of their
  * argmax (the vLLM blog's benchmark drafts at temperature 1.0, "Results"), drawn by
- * the Gumbel-max rule:
+ * the Gumbel-max rule (over the whole vocabulary, matrix-core form):
  *   tokens[r,i] = argmax_v  x[v] * (1 / temperature) + g(seed, r, i, v)
  *   g = -log(-log u),  u = (2 b + 1) / 2^24,  b = top 23 bits of word v % 4 of
  *       Philox4x32-10 (Salmon et al., SC 2011) at counter (v / 4, i, r, 0) under the
@@ -159,9 +209,10 @@ int dspark_chain(const void* base, const void* A, const void* Bt, int dtype, con
  * arguments, limits and the workspace are those of dspark_chain.  The tokens can be
  * scheduled with the stage calls (survival, top-B, budget, allocate with tokens).
  */
-int dspark_chain_sample(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
-                        int R, int K, int V, int rank, float temperature, uint64_t seed, int32_t* tokens,
-                        float* chained_logits, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+int dspark_chain_sample(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0,
+                        int R, int K, int V, int rank, const dspark_markov_t* markov, float temperature,
+                        uint64_t seed, int32_t* tokens, float* chained_logits, uint32_t* status, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * Stage 2, survival (vLLM blog, "Scheduling the budget"): for every request r,
@@ -234,20 +285,25 @@ int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, c
                     void* stream);
 
 /*
- * The whole pass on one stream: stages 2-5 (survival, top-B, budget, the
- * allocation) and stage 1 (chain), then the verified tokens are gathered.  The
- * stages share no host round trip.  Arguments are those of the stage calls;
- * `surv`, `order`, `sorted_surv`, `prefix_len`, `offsets`, `ver_idx`, `ver_tokens`
- * and `best_obj` are outputs (surv, order, sorted_surv may be NULL).
- * conf holds R rows (the drafting requests), R*K <= DSPARK_MAX_SLOTS.
- * It runs as ONE kernel launch when the grid fits on the device at once (one
- * workgroup per 512 vocabulary entries plus one scheduling workgroup): bf16 with
- * R <= 256, and fp32 with R <= 64 and rank <= 64 (with the whole vocabulary in one
- * workgroup, V <= 2048 and rank <= 16, positions need no device-wide barrier);
- * otherwise as the stage-wise launches.  Results are the same either way.
+ * The whole pass on one stream: stage 1 (chain) and stages 2-5 (survival, top-B,
+ * budget, the allocation), then the verified tokens are gathered.  The stages share
+ * no host round trip.  Arguments are those of the stage calls; `surv`, `order`,
+ * `sorted_surv`, `prefix_len`, `offsets`, `ver_idx`, `ver_tokens` and `best_obj` are
+ * outputs (surv, order, sorted_surv may be NULL).  conf holds R rows (the drafting
+ * requests), R*K <= DSPARK_MAX_SLOTS.
+ * Order.  Where the pruned chain applies (see dspark_chain), the chain runs first and
+ * stages 2-5 start once it has ended, in a second launch: in the method the
+ * confidences score the drafted tokens, so the schedule follows the chain (DSpark
+ * summary, Figure 1).  Otherwise (and in the dense form) it is ONE launch when the grid
+ * fits on the device at once -- one workgroup per 512 vocabulary entries plus one
+ * scheduling workgroup that runs stages 2-5 beside the chain, bf16 with R <= 256, and
+ * fp32 with R <= 64 and rank <= 64 (with the whole vocabulary in one workgroup, V <=
+ * 2048 and rank <= 16, positions need no device-wide barrier) -- else the stage-wise
+ * launches.  Results are the same in every form (tokens up to float32 near-ties, see
+ * dspark_chain).
  */
-int dspark_step(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
-                int R, int K, int V, int rank,
+int dspark_step(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0,
+                int R, int K, int V, int rank, const dspark_markov_t* markov,
                 const float* conf, int n_sampling, int T, int num_reqs,
                 const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
                 int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
@@ -294,8 +350,8 @@ int dspark_schedule(const float* conf, int R, int K, const float* size_conf, int
  * dspark_step is this call with size_R = -1 and DSPARK_RULE_ARGMAX.  size_conf is
  * read before the chain finishes; it must not alias an output.
  */
-int dspark_step_sized(const void* base, const void* A, const void* Bt, int dtype, const int32_t* prev0,
-                      int R, int K, int V, int rank,
+int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0,
+                      int R, int K, int V, int rank, const dspark_markov_t* markov,
                       const float* conf, const float* size_conf, int size_R, int rule,
                       int n_sampling, int T, int num_reqs,
                       const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
@@ -360,9 +416,10 @@ int dspark_get_launch_mode(void);
 
 /*
  * Measurement hook.  When set (non-NULL hipEvent_t handles), every later
- * dspark_step call on this thread records `before_chain` on its stream after the
- * schedule kernels and before the first chain kernel, and `after_chain` after the
- * last chain kernel, so a caller can time the phases with hipEventElapsedTime.
+ * dspark_step call on this thread records `before_chain` on its stream right before
+ * the first chain kernel, and `after_chain` right after the last chain kernel (for a
+ * single-launch step, around that launch), so a caller can time the chain with
+ * hipEventElapsedTime.
  * Pass NULLs to turn it off (the default).  Recording an event enqueues a marker
  * only; no synchronisation happens.
  */

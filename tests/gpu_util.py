@@ -13,6 +13,7 @@ through the C ABI, and compare with the oracle under the parity rules:
 """
 from __future__ import annotations
 
+import contextlib
 import os
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -43,7 +44,7 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 
 class Chain:
-    """Device copies of one chain problem (A, Bt prepared from Bmat on the GPU)."""
+    """Device copies of one chain problem and its prepared Markov head."""
 
     def __init__(self, base, A, Bmat, dtype, prev0):
         self.R, self.K, self.V = base.shape
@@ -51,10 +52,8 @@ class Chain:
         self.dtype = dtype
         self.base = to_dev(base)
         self.A = to_dev(A)
-        Bm = to_dev(Bmat)
-        self.Bt = torch.empty((self.V, self.rank), dtype=Bm.dtype, device=DEV)
-        B.dspark_markov_prepare(Bm, dtype, self.Bt)
-        del Bm
+        self.Bmat = to_dev(Bmat)
+        self.markov = B.MarkovHead(self.A, self.Bmat, dtype)
         self.prev0 = to_dev(np.asarray(prev0, dtype=np.int32))
         self.ws = B.workspace(self.R, self.K, self.V, self.rank, dtype)
 
@@ -62,7 +61,7 @@ class Chain:
         tokens = torch.full((self.R, self.K), -7, dtype=torch.int32, device=DEV)
         logits = torch.empty((self.R, self.K, self.V), dtype=torch.float32, device=DEV) if want_logits else None
         status = torch.zeros(1, dtype=torch.int32, device=DEV)
-        B.dspark_chain(self.base, self.A, self.Bt, self.dtype, self.prev0, tokens, logits, status, self.ws)
+        B.dspark_chain(self.base, self.markov, self.prev0, tokens, logits, status, self.ws)
         torch.cuda.synchronize()
         return tokens, logits, int(status.item())
 
@@ -142,6 +141,30 @@ def assert_chain_parity(gpu_tokens, gpu_logits, base, A, Bmat, dtype, prev0, row
         return sum(ex.map(work, chunks))
 
 
+def assert_tokens_agree(tok_a, tok_b, base, A, Bmat, dtype, prev0):
+    """tok_a has passed the oracle parity; tok_b (another chain form on the same inputs) may
+    differ only in rows that pass it too (a float32 near-tie taken the other way changes that
+    row's later positions).  Returns the number of differing rows."""
+    rows = np.nonzero((np.asarray(tok_a) != np.asarray(tok_b)).any(axis=1))[0]
+    if len(rows):
+        assert_chain_parity(np.asarray(tok_b), None, base, A, Bmat, dtype, prev0, rows=rows)
+    return len(rows)
+
+
+@contextlib.contextmanager
+def chain_form(form):
+    """Run the enclosed calls with stage 1 in `form` (B.CHAIN_PRUNED or B.CHAIN_DENSE)."""
+    old = B.dspark_get_chain_form()
+    B.dspark_set_chain_form(form)
+    try:
+        yield form
+    finally:
+        B.dspark_set_chain_form(old)
+
+
+FORMS = {"pruned": B.CHAIN_PRUNED, "dense": B.CHAIN_DENSE}
+
+
 def sched_oracle(conf, n_sampling, T, num_reqs, vc, dc, tokens=None):
     return sched.schedule(conf, n_sampling, T, num_reqs, vc, dc, tokens=tokens)
 
@@ -177,8 +200,7 @@ def run_step(ch: Chain, conf, n_sampling, T, num_reqs, vc, dc, out=None):
     conf_d = to_dev(np.asarray(conf, dtype=np.float32))
     vc_d, dc_d = to_dev(np.asarray(vc, dtype=np.float32)), to_dev(np.asarray(dc, dtype=np.float32))
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    B.dspark_step(ch.base, ch.A, ch.Bt, ch.dtype, ch.prev0, conf_d, n_sampling, T, num_reqs, vc_d, dc_d, out,
-                  ch.ws, status)
+    B.dspark_step(ch.base, ch.markov, ch.prev0, conf_d, n_sampling, T, num_reqs, vc_d, dc_d, out, ch.ws, status)
     torch.cuda.synchronize()
     return step_numpy(out), int(status.item()), out
 
@@ -198,7 +220,7 @@ def run_step_sized(ch: Chain, conf, size_conf, rule, n_sampling, T, num_reqs, vc
     size_d = None if size_conf is None else to_dev(np.asarray(size_conf, dtype=np.float32).reshape(-1, ch.K))
     vc_d, dc_d = to_dev(np.asarray(vc, dtype=np.float32)), to_dev(np.asarray(dc, dtype=np.float32))
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    B.dspark_step_sized(ch.base, ch.A, ch.Bt, ch.dtype, ch.prev0, conf_d, size_d, rule, n_sampling, T, num_reqs,
-                        vc_d, dc_d, out, ch.ws, status)
+    B.dspark_step_sized(ch.base, ch.markov, ch.prev0, conf_d, size_d, rule, n_sampling, T, num_reqs, vc_d, dc_d,
+                        out, ch.ws, status)
     torch.cuda.synchronize()
     return step_numpy(out), int(status.item()), out

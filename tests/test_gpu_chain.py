@@ -9,6 +9,14 @@ from confidence_scheduled_verification_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=["pruned", "dense"])
+def form(request):
+    """Every chain test runs in both forms of stage 1 (the fp32 tests take the same fp32
+    kernels in both)."""
+    with gu.chain_form(gu.FORMS[request.param]):
+        yield request.param
+
+
 def _case(seed, R, K, V, rank, dtype, **kw):
     return inputs.random_case(seed, R=R, K=K, V=V, rank=rank, dtype=dtype, **kw)
 

@@ -17,7 +17,7 @@ def _sample(ch, temperature, seed, want_logits=False):
     tokens = torch.full((ch.R, ch.K), -7, dtype=torch.int32, device=gu.DEV)
     logits = torch.empty((ch.R, ch.K, ch.V), dtype=torch.float32, device=gu.DEV) if want_logits else None
     status = torch.zeros(1, dtype=torch.int32, device=gu.DEV)
-    B.dspark_chain_sample(ch.base, ch.A, ch.Bt, ch.dtype, ch.prev0, temperature, seed, tokens, logits, status, ch.ws)
+    B.dspark_chain_sample(ch.base, ch.markov, ch.prev0, temperature, seed, tokens, logits, status, ch.ws)
     torch.cuda.synchronize()
     return tokens.cpu().numpy(), (None if logits is None else logits.cpu().numpy()), int(status.item())
 

@@ -21,9 +21,15 @@ LOGIT_ROWS = {"tiny": None, "small": None, "mid": [0, 37, 111], "headline": [0, 
               "large": [0, 63]}
 
 
+@pytest.mark.parametrize("form", ["pruned", "dense"])
 @pytest.mark.parametrize("name", ["tiny", "small", "mid", "headline", "large"])
-def test_full_size_step_parity(name):
+def test_full_size_step_parity(name, form):
     w = inputs.WORKLOADS[name]
+    with gu.chain_form(gu.FORMS[form]):
+        _full_size_step_parity(w, name)
+
+
+def _full_size_step_parity(w, name):
     gu.say(f"step {name}: generating R={w.R} K={w.K} V={w.V}")
     ins = inputs.generate(w)
     vc, dc = gu.forced_tables(w, ins)
@@ -38,10 +44,11 @@ def test_full_size_step_parity(name):
     want = sched.schedule(ins.conf, w.n_sampling, w.T, w.R_all, vc, dc, tokens=got["tokens"])
     gu.assert_sched_parity(got, want, w.R, w.K)
     # the chained logits of the sampled rows, from the stage-1 entry point on the same inputs
+    # (the dense form: asking for logits selects it); its tokens agree up to near-ties
     tok, lg, _ = ch.run(want_logits=True)
-    np.testing.assert_array_equal(tok.cpu().numpy(), got["tokens"])
+    gu.assert_tokens_agree(got["tokens"], tok.cpu().numpy(), ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
     sel = np.arange(w.R) if rows is None else np.array(rows)
-    gu.assert_chain_parity(got["tokens"], lg[torch.as_tensor(sel, device=gu.DEV)].cpu().numpy(), ins.base, ins.A,
+    gu.assert_chain_parity(tok.cpu().numpy(), lg[torch.as_tensor(sel, device=gu.DEV)].cpu().numpy(), ins.base, ins.A,
                            ins.Bmat, w.dtype, ins.prev0, rows=sel)
 
 
@@ -133,9 +140,14 @@ def test_single_launch_step_at_the_slot_limit():
 
 @pytest.mark.parametrize("name", ["small", "headline", "large"])
 def test_launch_modes_give_identical_results(name):
-    # The persistent kernels run as a plain launch of a resident grid (default) or as a
-    # cooperative launch; the work is the same, so every output must match bit for bit.
-    # Large runs the two-tile chain beside a separate schedule launch.
+    # The dense form's persistent kernels run as a plain launch of a resident grid
+    # (default) or as a cooperative launch; the work is the same, so every output must
+    # match bit for bit.  Large runs the two-tile chain beside a separate schedule launch.
+    with gu.chain_form(B.CHAIN_DENSE):
+        _launch_modes(name)
+
+
+def _launch_modes(name):
     w = inputs.WORKLOADS[name]
     ins = inputs.generate(w)
     vc, dc = gu.forced_tables(w, ins)
@@ -156,8 +168,14 @@ def test_launch_modes_give_identical_results(name):
     np.testing.assert_array_equal(tok_r.cpu().numpy(), res["tokens"])
 
 
+@pytest.mark.parametrize("form", ["pruned", "dense"])
 @pytest.mark.parametrize("R", [1, 17, 33, 64, 65])
-def test_ring_depth_boundaries(R):
+def test_ring_depth_boundaries(R, form):
+    with gu.chain_form(gu.FORMS[form]):
+        _ring_depth(R)
+
+
+def _ring_depth(R):
     # Up to 64 requests at the full rank the chain sweeps 2-block base rings (one group);
     # from 65 on, 4-block rings in two groups.  Both must give the oracle's tokens, the same
     # tokens through the step and the chain entry point, and the oracle's schedule.
@@ -182,13 +200,19 @@ def test_ring_depth_boundaries(R):
 # tiles, the schedule launch and the single-launch chain; 257 tiles with R <= 64, the
 # two-tile chain; 514 tiles, one chain launch per position.  Every form must give the
 # oracle's tokens and schedule.
+@pytest.mark.parametrize("form", ["pruned", "dense"])
 @pytest.mark.parametrize("R,K,V,rank", [
     (16, 3, 255 * 512, 256),
     (16, 3, 255 * 512 + 8, 256),
     (16, 3, 256 * 512 + 8, 256),
     (8, 2, 514 * 512 - 40, 64),
 ])
-def test_step_launch_form_boundaries(R, K, V, rank):
+def test_step_launch_form_boundaries(R, K, V, rank, form):
+    with gu.chain_form(gu.FORMS[form]):
+        _launch_form_boundary(R, K, V, rank)
+
+
+def _launch_form_boundary(R, K, V, rank):
     c = inputs.random_case(700 + V % 97, R=R, K=K, V=V, rank=rank, dtype=inputs.BF16)
     w = dataclasses.replace(inputs.WORKLOADS["small"], R=R, R_all=R, K=K, V=V, rank=rank, n_sampling=R)
     vc = sched.force_monotone(inputs.raw_verify_cost(w, None))

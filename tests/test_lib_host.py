@@ -45,6 +45,8 @@ def test_version_and_workspace_size():
     assert binding.dspark_workspace_bytes(0, 7, 100, 256, 1) == 0
     n = binding.dspark_workspace_bytes(256, 7, 129280, 256, 1)
     assert n >= 256 * 7 * 8 and n % 256 == 0
+    # bf16 workspaces carry the pruned chain's candidate buffers; fp32 ones do not
+    assert n > (32 << 20) > binding.dspark_workspace_bytes(256, 7, 129280, 256, 0)
 
 
 def test_force_monotone_matches_running_max():
@@ -67,39 +69,90 @@ def test_force_monotone_rejects_non_finite_and_leaves_table():
     assert L.dspark_force_monotone(None, 3) == -1
 
 
+_KEEP = []
+
+
 def _fake(n=64):
     # host buffers standing in for device pointers: every call below fails its checks first
-    return ctypes.c_void_p(ctypes.addressof((ctypes.c_char * n)()))
+    buf = (ctypes.c_char * n)()
+    _KEEP.append(buf)
+    return ctypes.c_void_p(ctypes.addressof(buf))
+
+
+def _handle(A, Bmat, V=1024, rank=256, dtype=1):
+    """A head handle as dspark_markov_prepare would fill it (host-only: no kernel runs)."""
+    m = binding.dspark_markov_t(binding.MARKOV_MAGIC, A.value, Bmat.value, _fake().value, 1 << 20, V, rank, dtype, 0)
+    _KEEP.append(m)
+    return ctypes.byref(m)
 
 
 def test_chain_argument_checks_return_before_launch():
     L = binding.lib()
-    p = _fake()
+    p, A, Bm = _fake(), _fake(), _fake()
+    m = _handle(A, Bm)
+    big = 1 << 26
     # NULL base
-    assert L.dspark_chain(None, p, p, 1, p, 4, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
-    assert L.dspark_chain(None, None, None, 1, None, 0, 7, 1024, 256, None, None, None, None, 0, None) == 0
+    assert L.dspark_chain(None, A, Bm, 1, p, 4, 7, 1024, 256, m, p, None, None, p, big, None) == -1
+    assert L.dspark_chain(None, None, None, 1, None, 0, 7, 1024, 256, None, None, None, None, None, 0, None) == 0
     # unknown dtype
-    assert L.dspark_chain(p, p, p, 7, p, 4, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_chain(p, A, Bm, 7, p, 4, 7, 1024, 256, m, p, None, None, p, big, None) == -1
     # bf16 rank not a multiple of 32
-    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 48, p, None, None, p, 1 << 20, None) == -3
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 48, m, p, None, None, p, big, None) == -3
     assert b"multiple of 32" in L.dspark_last_error()
     # bf16 rank too large
-    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 512, p, None, None, p, 1 << 20, None) == -3
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 512, m, p, None, None, p, big, None) == -3
     # bf16 K*V beyond the 32-bit per-lane base offsets
-    assert L.dspark_chain(p, p, p, 1, p, 4, 16, 1 << 24, 256, p, None, None, p, 1 << 40, None) == -3
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 16, 1 << 24, 256, m, p, None, None, p, 1 << 40, None) == -3
     # workspace too small / missing
-    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, p, 8, None) == -4
-    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 1024, 256, p, None, None, None, 0, None) == -4
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, None, None, p, 8, None) == -4
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, None, None, None, 0, None) == -4
     # negative sizes
-    assert L.dspark_chain(p, p, p, 1, p, -1, 7, 1024, 256, p, None, None, p, 1 << 20, None) == -1
-    assert L.dspark_chain(p, p, p, 1, p, 4, 7, 0, 256, p, None, None, p, 1 << 20, None) == -1
-    # R == 0 is a valid empty call that enqueues nothing
-    assert L.dspark_chain(p, p, p, 1, p, 0, 7, 1024, 256, p, None, None, None, 0, None) == 0
+    assert L.dspark_chain(p, A, Bm, 1, p, -1, 7, 1024, 256, m, p, None, None, p, big, None) == -1
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 0, 256, m, p, None, None, p, big, None) == -1
+    # R == 0 is a valid empty call that enqueues nothing (no head needed)
+    assert L.dspark_chain(p, A, Bm, 1, p, 0, 7, 1024, 256, None, p, None, None, None, 0, None) == 0
+
+
+def test_markov_handle_is_checked_before_launch():
+    # A head prepared from other pointers, sizes or dtype -- or not prepared at all, or a
+    # transposed factor passed as Bmat -- is refused before anything is enqueued.
+    L = binding.lib()
+    p, A, Bm, Bt = _fake(), _fake(), _fake(), _fake()
+    big = 1 << 26
+    m = _handle(A, Bm)
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 256, None, p, None, None, p, big, None) == -1
+    assert b"NULL handle" in L.dspark_last_error()
+    raw = binding.dspark_markov_t()
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 256, ctypes.byref(raw), p, None, None, p, big, None) == -1
+    assert b"not prepared" in L.dspark_last_error()
+    assert L.dspark_chain(p, A, Bt, 1, p, 4, 7, 1024, 256, m, p, None, None, p, big, None) == -1
+    assert b"other A / Bmat" in L.dspark_last_error()
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 2048, 256, m, p, None, None, p, big, None) == -1
+    assert b"prepared for V=1024" in L.dspark_last_error()
+    m32 = _handle(A, Bm, rank=256, dtype=0)
+    assert L.dspark_chain(p, A, Bm, 1, p, 4, 7, 1024, 256, m32, p, None, None, p, big, None) == -1
+    # the state must be large enough and aligned
+    state = _fake(4096)
+    h = binding.dspark_markov_t()
+    assert L.dspark_markov_prepare(ctypes.byref(h), A, Bm, 1024, 256, 1, state, 4096, None) in (-1, -4)
+    assert L.dspark_markov_state_bytes(1024, 256, 1) == 256 + 1024 * 256 * 2
+    assert L.dspark_markov_state_bytes(1024, 256, 0) == 256 + 1024 * 256 * 4
+    assert h.magic != binding.MARKOV_MAGIC
+
+
+def test_chain_form_switch():
+    L = binding.lib()
+    assert L.dspark_get_chain_form() == binding.CHAIN_PRUNED
+    assert L.dspark_set_chain_form(5) == -1 and L.dspark_get_chain_form() == binding.CHAIN_PRUNED
+    assert L.dspark_set_chain_form(binding.CHAIN_DENSE) == 0 and L.dspark_get_chain_form() == binding.CHAIN_DENSE
+    assert L.dspark_set_chain_form(binding.CHAIN_PRUNED) == 0
 
 
 def test_schedule_argument_checks_return_before_launch():
     L = binding.lib()
-    p = _fake()
+    p, A, Bm = _fake(), _fake(), _fake()
+    m = _handle(A, Bm)
+    big = 1 << 26
     # T outside [0, verify_len)
     assert L.dspark_choose_budget(p, 10, 4, 65, 4, p, 65, p, 257, 0, p, p, None, None, None) == -2
     # num_reqs outside the draft table
@@ -115,25 +168,28 @@ def test_schedule_argument_checks_return_before_launch():
     # NULL tables
     assert L.dspark_choose_budget(p, 10, 4, 0, 4, None, 65, p, 257, 0, p, p, None, None, None) == -1
     # the fused step checks both halves
-    assert L.dspark_step(p, p, p, 1, p, 2048, 9, 1024, 256, p, 4, 0, 4, p, 65, p, 257,
-                         p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
-    assert L.dspark_step(p, p, p, 1, p, 4, 7, 1024, 256, p, 4, 70, 4, p, 65, p, 257,
-                         p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -2
+    assert L.dspark_step(p, A, Bm, 1, p, 2048, 9, 1024, 256, m, p, 4, 0, 4, p, 65, p, 257,
+                         p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -3
+    assert L.dspark_step(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, 4, 70, 4, p, 65, p, 257,
+                         p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -2
     # unknown admission rule
     assert L.dspark_choose_budget(p, 10, 4, 0, 4, p, 65, p, 257, 2, p, p, None, None, None) == -1
-    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, None, -1, 7, 4, 0, 4, p, 65, p, 257,
-                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
+    assert L.dspark_step_sized(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, None, -1, 7, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -1
     # sizing array: rows below -1, NULL with rows, too many slots
-    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, -2, 0, 4, 0, 4, p, 65, p, 257,
-                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
-    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, None, 3, 0, 4, 0, 4, p, 65, p, 257,
-                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -1
-    assert L.dspark_step_sized(p, p, p, 1, p, 4, 7, 1024, 256, p, p, 2341, 0, 4, 0, 4, p, 65, p, 257,
-                               p, None, None, None, p, p, p, p, p, None, None, p, 1 << 20, None) == -3
+    assert L.dspark_step_sized(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, p, -2, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -1
+    assert L.dspark_step_sized(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, None, 3, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -1
+    assert L.dspark_step_sized(p, A, Bm, 1, p, 4, 7, 1024, 256, m, p, p, 2341, 0, 4, 0, 4, p, 65, p, 257,
+                               p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -3
+    # the step refuses a head prepared from another second factor
+    assert L.dspark_step(p, A, p, 1, p, 4, 7, 1024, 256, m, p, 4, 0, 4, p, 65, p, 257,
+                         p, None, None, None, p, p, p, p, p, None, None, p, big, None) == -1
     # sampling: temperature must be positive, finite and invertible
     for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
-        assert L.dspark_chain_sample(p, p, p, 1, p, 4, 7, 1024, 256, t, 1, p, None, None, p, 1 << 20, None) == -2
-    assert L.dspark_chain_sample(p, p, p, 1, p, 0, 7, 1024, 256, 1.0, 1, p, None, None, None, 0, None) == 0
+        assert L.dspark_chain_sample(p, A, Bm, 1, p, 4, 7, 1024, 256, m, t, 1, p, None, None, p, big, None) == -2
+    assert L.dspark_chain_sample(p, A, Bm, 1, p, 0, 7, 1024, 256, None, 1.0, 1, p, None, None, None, 0, None) == 0
     # the fused schedule: too many slots, ver_tokens without tokens, unknown rule
     assert L.dspark_schedule(p, 2000, 9, None, -1, 0, 4, 0, 4, p, 65, p, 257, None, None, None, None, p, p, p, p, p,
                              None, None, None) == -3
