@@ -11,12 +11,9 @@
 // once by dspark_markov_prepare).  With M = max_v base[v], the winner w has
 // x[w] >= x[argmax base] >= M - a b, hence base[w] >= M - 2 a b.  Only the entries with
 // base[v] >= M - 2ab (the candidates) can win, and which entries these are does not
-// depend on the previous token.  So a request splits into
-//   1. one streaming pass over its base logits -- all of the stage's HBM traffic, with no
-//      dependence between positions -- that keeps, per (request, position) row, its
-//      maximum and its candidates (index and value), and
-//   2. the chain over the candidates alone: the bias is evaluated for a few tens of
-//      entries per position instead of V.
+// depend on the previous token.  So a row needs one streaming pass over its base logits
+// (all of the stage's HBM traffic) that keeps its maximum and its candidates (index and
+// value), and then the bias of a few tens of candidates instead of V entries.
 // The bound is applied with a margin (2ab(1 + 2^-10), plus 2^-20 |M| for the rounding of
 // the subtraction), so the candidate set always contains the exact (real-number, and
 // hence the double-precision) argmax.  Among the candidates the kernel takes the float32
@@ -26,25 +23,25 @@
 // where base is); a row of -inf gives 0; a row whose candidates overflow a buffer, or
 // weights whose bound is not finite, are scored densely.
 //
-// One workgroup per compute unit; workgroup g takes requests g, g + G, ... whole, so a
-// request's candidates never leave the compute unit's LDS.
+// One workgroup per compute unit takes requests g, g + G, ... whole, so a request's
+// candidates never leave the compute unit's LDS.  Its nine waves split the work:
 //
-// Streaming.  A request's K*V base entries are items of 4096 entries (a row is
-// ceil(V/4096) items), streamed in rounds: in round t wave w takes item 16t + w, with the
-// next round's loads in flight.  Each wave folds its item's maximum into the row's
-// maximum in LDS; after a barrier every wave keeps the entries of its item that clear
-// the floor of the row's maximum so far (a lower bound of the final one, so nothing that
-// can win is dropped; the 16 items of a round already give a floor close to the final).
-// Candidates and one directory word per item stay in the wave's part of the LDS.
+// Streaming (waves 0-7).  The request's K*V base entries are items of 4096 entries (a row
+// is ceil(V/4096) items); wave w takes items w, w + 8, ..., with the next two items'
+// loads always in flight, and never waits for the other waves.  For each item it folds
+// the item's maximum into the row's maximum in LDS and keeps the entries that clear the
+// floor of the row's maximum seen so far (a lower bound of the final one, so nothing that
+// can win is dropped), with one directory word for the item, in its part of the LDS; then
+// it counts the item into its row.
 //
-// Chain.  Once the request is streamed its 1024 threads (a) read the rows' maxima and
-// NaN marks, (b) keep the candidates that clear each row's final floor, in one LDS list,
-// (c) put each listed candidate's Bt row in registers or LDS (8 threads per candidate,
-// 32 rank entries each) and the key rows each position most likely needs: prev0 for
-// position 0 and, for position i > 0, row i-1's largest base entry (its token unless the
-// bias reorders the top), (d) score every position with that key row, all at once, and
-// (e) walk the positions: where the previous token is the one guessed, the scored token
-// stands; otherwise that position is scored again with the right key row.
+// Chain (wave 8), concurrently.  Position by position it waits for the row's count to
+// reach its item count, lists the kept entries that clear the row's final floor, loads
+// their Bt rows (one 8-byte slice per lane) and scores them with the key row of the
+// previous token (x = value + the lanes' partial dot products summed over the wave).
+// The key row of the next position is prefetched for the row's largest entry -- the
+// token unless the bias reorders the top -- while the row is scored, and loaded again
+// only when that guess misses.  So the chain keeps up with the streaming, and only the
+// last row's scoring is left once the last item arrives.
 #include "common.h"
 #include "kernels.h"
 
@@ -52,19 +49,20 @@ namespace dspark {
 
 namespace {
 
-constexpr int kQT = 1024;               // threads per workgroup
-constexpr int kQW = kQT / 64;           // waves per workgroup
-constexpr int kQItem = kCandItem;       // base entries per item: 64 lanes x 8 loads x 8 entries
-constexpr int kQStage = kCandWaveStage; // candidates a wave keeps for its items of one request
-constexpr int kQRegCands = kQT / 8;     // listed candidates whose Bt slices sit in registers (one per 8 threads)
-constexpr int kQLdsCands = 128;         // the next ones, whose Bt rows are staged in LDS
+constexpr int kQS = 7;                   // streaming waves (with the chain wave, two waves per SIMD)
+constexpr int kQT = (kQS + 1) * 64;      // threads per workgroup: the streaming waves and the chain wave
+constexpr int kQItem = kCandItem;        // base entries per item: 64 lanes x 8 loads x 8 entries
+constexpr int kQStage = kCandWaveStage;  // entries a streaming wave keeps for its items of one request
+constexpr int kQList = 256;              // candidates the chain wave lists at once
 constexpr uint32_t kQOverflow = 0xFFFFFFFFu;
 constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
+constexpr long kQSpinLimit = 1L << 26;   // polls (with a short sleep each) before the chain wave gives up
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 static_assert(kCandMaxK * kCandMaxItems <= 2048, "a request's directory fits the LDS array");
-static_assert(kQW * kQStage < (1 << 16), "LDS slots fit the directory word");
+static_assert(kQS * kQStage < (1 << 16), "LDS slots fit the directory word");
 
 // Order-preserving image of a float in the unsigned integers (NaN above every number,
 // -0 equal to +0); never 0.
@@ -141,30 +139,23 @@ __device__ __forceinline__ HeaderView header_view(const void* hdr) {
 
 // LDS of one request.
 struct QLds {
-    uint64_t stage[kQW * kQStage];   // candidates, wave w's in [w kQStage, (w + 1) kQStage): (index << 32) | value bits
-    uint64_t dir[kCandMaxK * kCandMaxItems];  // per item: (first slot << 32) | count (kQOverflow: no room);
-                                     // from (b) on (first slot << 32) | the row's prefix
-    uint64_t flat[kCandListCap];     // the rows' candidate lists, concatenated
-    uint16_t btrow[kQLdsCands][256]; // Bt rows of listed candidates kQRegCands ..
-    uint16_t arow[kCandMaxK][256];   // key rows (bf16): the one guessed for each position
-    uint16_t fix[256];               // key row of a re-scored position
-    uint64_t best[kCandMaxK];        // per-position argmax key (LDS atomic max)
-    uint64_t dbest;                  // a whole-row scoring's key
-    uint32_t rowmax[kCandMaxK];      // the rows' maxima so far (order-preserving image; 0 = none yet)
-    uint32_t rownan[kCandMaxK];      // ~(first NaN index), 0 = none
-    int32_t rowstart[kCandMaxK];     // listed candidates of row i: flat[rowstart[i] ..] (rowcnt[i] of them)
-    int32_t rowcnt[kCandMaxK];
-    int32_t npool[kCandMaxK];        // the row's kept entries before the final floor
-    int32_t kind[kCandMaxK];         // 0 listed candidates, 1 first NaN, 2 all -inf, 3 dense, 4 candidates
-                                     // scored from the kept entries (more than the list holds)
-    int32_t nanidx[kCandMaxK];
-    float floor_[kCandMaxK];
-    int32_t top[kCandMaxK];          // the row's largest candidate (lowest index among equals)
-    int32_t guess[kCandMaxK];        // key token row i was scored with
-    int32_t tok[kCandMaxK];
-    uint8_t frow[kCandListCap];      // row of each listed candidate
-    int32_t ntot;
+    uint64_t stage[kQS * kQStage];           // kept entries, wave w's in [w kQStage, (w + 1) kQStage): (index << 32) | value bits
+    uint64_t dir[kCandMaxK * kCandMaxItems]; // per item: (first slot << 32) | count (kQOverflow: no room)
+    uint32_t pfx[kCandMaxK * kCandMaxItems]; // per item: prefix of its row's counts (written by the chain wave)
+    uint64_t clist[kQList];                  // the chain wave's listed candidates
+    uint16_t akey[256];                      // key row of a densely scored row
+    uint32_t rowmax[kCandMaxK];              // the rows' maxima so far (order-preserving image; 0 = none yet)
+    uint32_t rownan[kCandMaxK];              // ~(first NaN index), 0 = none
+    uint32_t rowdone[kCandMaxK];             // items of the row kept so far
 };
+
+// LDS writes of this wave complete, and not moved past this point by the compiler.  (A
+// release fence at workgroup scope would also wait for the wave's global loads in
+// flight.)
+__device__ __forceinline__ void lds_writes_done() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------------
 // Streaming
@@ -179,14 +170,32 @@ __device__ __forceinline__ void load_item(u32x4 (&buf)[8], const uint16_t* __res
     for (int q = 0; q < 8; ++q) {
         const int e = v0 + q * 512 + lane * 8;
         if (VEC) {
-            buf[q] = e < V ? __builtin_nontemporal_load((const u32x4*)(p + e))
-                           : u32x4{kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair};
+            // every load is issued (past the row, at the row's start), so that the number of
+            // loads in flight is the same on every path and the waits for one buffer never
+            // wait for the buffers loaded after it
+            const u32x4 x = __builtin_nontemporal_load((const u32x4*)(p + (e < V ? e : 0)));
+            buf[q] = e < V ? x : u32x4{kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair};
         } else {
             uint32_t h[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) h[t] = e + t < V ? (uint32_t)p[e + t] : 0xFF80u;
             buf[q] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
+    }
+}
+
+// The maxima of an item's eight 8-entry groups (per lane).
+__device__ __forceinline__ void group_maxima(const u32x4 (&cur)[8], float (&gm)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        float g = -__builtin_huge_valf();
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t x = cur[q][d];
+            g = __builtin_elementwise_maximum(
+                g, __builtin_elementwise_maximum(__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u)));
+        }
+        gm[q] = g;
     }
 }
 
@@ -199,417 +208,332 @@ __device__ __forceinline__ float entry_of(const u32x4& word4, int t) {
     return __uint_as_float((t & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
-// Streams request r (see the file comment): the rows' maxima and NaN marks, and each
-// item's candidates with its directory word, into L.
-template <bool VEC>
-__device__ __forceinline__ void stream_request(const CandArgs& a, QLds& L, int r, float ab2) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int K = a.K, NC = a.NC, V = a.V;
-    const int per_req = K * NC;
-    const int n_rounds = (per_req + kQW - 1) / kQW;
-    const uint16_t* rbase = a.base + (size_t)r * (size_t)K * (size_t)V;
+// One item of a streaming wave (see the file comment): the item's maximum into its row's
+// (or its first NaN into the row's mark), its entries that clear the floor of the row's
+// maximum so far -- in entry order, from slot w kQStage + used -- and its directory
+// word; then the item is counted into its row.  -inf never wins unless the whole row is
+// -inf, which is handled apart, so it is never kept.
+__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j, int i, int v0, uint32_t& used,
+                                          float ab2) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     constexpr float kNegInf = -__builtin_huge_valf();
-    if (tid < K) {
-        L.rowmax[tid] = 0u;
-        L.rownan[tid] = 0u;
-    }
-    __syncthreads();
-    uint32_t used = 0;  // candidates this wave keeps so far
-    u32x4 cur[8], nxt[8];
-    if (w < per_req) load_item<VEC>(nxt, rbase + (size_t)(w / NC) * V, (w % NC) * kQItem, V);
-    for (int t = 0; t < n_rounds; ++t) {
-        const int jl = t * kQW + w;  // the item of the request this wave takes
-        const bool valid = jl < per_req;
-        const int i = valid ? jl / NC : 0;
-        const int v0 = valid ? (jl - i * NC) * kQItem : 0;
+    float gm[8];
+    group_maxima(cur, gm);
+    float m = gm[0];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
-        const int jn = jl + kQW;
-        if (jn < per_req) load_item<VEC>(nxt, rbase + (size_t)(jn / NC) * V, (jn % NC) * kQItem, V);
-        // the item's 8-entry group maxima and its maximum; a NaN marks the row at once
-        float gm[8];
-        bool nan_item = false;
-        if (valid) {
+    for (int q = 1; q < 8; ++q) m = __builtin_elementwise_maximum(m, gm[q]);
+    const float mw = wave_max(m);
+    uint32_t count = 0;
+    const uint32_t first_slot = (uint32_t)(w * kQStage) + used;
+    if (mw != mw) {
+        // the row's token is its first NaN, whatever the bias
+        uint32_t first = 0xFFFFFFFFu;
+#pragma unroll
+        for (int q = 7; q >= 0; --q) {
+            if (gm[q] != gm[q]) {
+#pragma unroll
+                for (int s = 7; s >= 0; --s) {
+                    const float x = entry_of(cur[q], s);
+                    if (x != x) first = (uint32_t)(v0 + q * 512 + lane * 8 + s);
+                }
+            }
+        }
+        first = wave_min_u32(first);
+        if (lane == 0) atomicMax(&L.rownan[i], ~first);
+    } else {
+        uint32_t seen = 0u;
+        if (lane == 0) seen = atomicMax(&L.rowmax[i], ord32(mw));
+        seen = __builtin_amdgcn_readfirstlane(seen);
+        const uint32_t now = seen > ord32(mw) ? seen : ord32(mw);
+        const float fl = cand_floor(unord32(now), ab2);
+        bool any = false;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) any |= gm[q] >= fl && gm[q] > kNegInf;
+        if (__ballot(any) != 0ull) {
+            uint32_t c = 0;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                float g = kNegInf;
+                if (gm[q] >= fl && gm[q] > kNegInf) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t x = cur[q][d];
-                    g = __builtin_elementwise_maximum(
-                        g, __builtin_elementwise_maximum(__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u)));
+                    for (int s = 0; s < 8; ++s) {
+                        const float x = entry_of(cur[q], s);
+                        c += (x >= fl && x > kNegInf) ? 1u : 0u;
+                    }
                 }
-                gm[q] = g;
             }
-            float m = gm[0];
+            uint32_t total = 0;
+            uint32_t slot = first_slot + wave_excl_scan(c, &total);
+            if (used + total <= (uint32_t)kQStage) {
 #pragma unroll
-            for (int q = 1; q < 8; ++q) m = __builtin_elementwise_maximum(m, gm[q]);
-            const float mw = wave_max(m);
-            if (mw != mw) {
-                // the row's token is its first NaN, whatever the bias
-                nan_item = true;
-                uint32_t first = 0xFFFFFFFFu;
+                for (int q = 0; q < 8; ++q) {
+                    if (gm[q] >= fl && gm[q] > kNegInf) {
 #pragma unroll
-                for (int q = 7; q >= 0; --q) {
-                    if (gm[q] != gm[q]) {
-#pragma unroll
-                        for (int s = 7; s >= 0; --s) {
+                        for (int s = 0; s < 8; ++s) {
                             const float x = entry_of(cur[q], s);
-                            if (x != x) first = (uint32_t)(v0 + q * 512 + lane * 8 + s);
-                        }
-                    }
-                }
-                first = wave_min_u32(first);
-                if (lane == 0) atomicMax(&L.rownan[i], ~first);
-            } else if (lane == 0) {
-                atomicMax(&L.rowmax[i], ord32(mw));
-            }
-        }
-        __syncthreads();  // the round's maxima are in
-        if (valid) {
-            uint32_t count = 0;
-            const uint32_t first_slot = (uint32_t)(w * kQStage) + used;
-            if (!nan_item) {
-                const float fl = cand_floor(unord32(L.rowmax[i]), ab2);
-                // -inf never wins unless the whole row is -inf, which the chain handles apart
-                bool any = false;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) any |= gm[q] >= fl && gm[q] > kNegInf;
-                if (__ballot(any) != 0ull) {
-                    uint32_t c = 0;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        if (gm[q] >= fl && gm[q] > kNegInf) {
-#pragma unroll
-                            for (int s = 0; s < 8; ++s) {
-                                const float x = entry_of(cur[q], s);
-                                c += (x >= fl && x > kNegInf) ? 1u : 0u;
+                            if (x >= fl && x > kNegInf) {
+                                const uint32_t v = (uint32_t)(v0 + q * 512 + lane * 8 + s);
+                                L.stage[slot++] = ((uint64_t)v << 32) | __float_as_uint(x);
                             }
                         }
                     }
-                    uint32_t total = 0;
-                    uint32_t slot = first_slot + wave_excl_scan(c, &total);
-                    if (used + total <= (uint32_t)kQStage) {
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            if (gm[q] >= fl && gm[q] > kNegInf) {
-#pragma unroll
-                                for (int s = 0; s < 8; ++s) {
-                                    const float x = entry_of(cur[q], s);
-                                    if (x >= fl && x > kNegInf) {
-                                        const uint32_t v = (uint32_t)(v0 + q * 512 + lane * 8 + s);
-                                        L.stage[slot++] = ((uint64_t)v << 32) | __float_as_uint(x);
-                                    }
-                                }
-                            }
-                        }
-                        count = total;
-                        used += total;
-                    } else {
-                        count = kQOverflow;  // no room: the row is scored densely
-                    }
                 }
+                count = total;
+                used += total;
+            } else {
+                count = kQOverflow;  // no room: the row is scored densely
             }
-            if (lane == 0) L.dir[jl] = ((uint64_t)first_slot << 32) | count;
         }
     }
-    __syncthreads();
+    if (lane == 0) L.dir[j] = ((uint64_t)first_slot << 32) | count;
+    lds_writes_done();
+    if (lane == 0) __hip_atomic_fetch_add(&L.rowdone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// A streaming wave's items of one request: w, w + kQS, ..., each loaded two items ahead
+// (three buffers in turn, so no item waits for another's loads; one ahead with
+// element-wise loads).  An item past the request loads nothing (v0 = V: every entry
+// reads as -inf).
+template <bool VEC>
+__device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int per_req, int NC, int V, float ab2) {
+    const int w = threadIdx.x >> 6;
+    uint32_t used = 0;
+    auto issue = [&](u32x4 (&buf)[8], int j) {
+        const bool ok = j < per_req;
+        load_item<VEC>(buf, rbase + (size_t)(ok ? j / NC : 0) * V, ok ? (j % NC) * kQItem : V, V);
+    };
+    auto take = [&](const u32x4 (&buf)[8], int j) {
+        if (j < per_req) {
+            const int i = j / NC;
+            keep_item(L, buf, j, i, (j - i * NC) * kQItem, used, ab2);
+        }
+    };
+    if (VEC) {
+        u32x4 b0[8], b1[8], b2[8];
+        issue(b0, w);
+        issue(b1, w + kQS);
+        for (int j = w; j < per_req; j += 3 * kQS) {
+            issue(b2, j + 2 * kQS);
+            take(b0, j);
+            issue(b0, j + 3 * kQS);
+            take(b1, j + kQS);
+            issue(b1, j + 4 * kQS);
+            take(b2, j + 2 * kQS);
+        }
+    } else {
+        // element-wise loads take more registers: one item ahead
+        u32x4 b0[8], b1[8];
+        issue(b0, w);
+        for (int j = w; j < per_req; j += 2 * kQS) {
+            issue(b1, j + kQS);
+            take(b0, j);
+            issue(b0, j + 2 * kQS);
+            take(b1, j + kQS);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------
 // Chain
 
-// x for a candidate scored with key row `arow` (LDS, bf16): the 8 threads of a candidate
-// each take 32 rank entries (slice s = lane % 8, held in `bt`), fused multiply-adds in
-// increasing k, then a butterfly over the 8 threads (every one ends with the same sum);
-// x = fl32(value + dot).
-__device__ __forceinline__ float cand_x(const u32x4 (&bt)[4], const uint16_t* arow, int rank, float value) {
-    const int s = threadIdx.x & 7;
-    float acc = 0.f;
-    if (32 * s < rank) {
-        const u32x4* ap = (const u32x4*)(arow + 32 * s);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const u32x4 av = ap[g];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                acc = __builtin_fmaf(__uint_as_float(av[d] << 16), __uint_as_float(bt[g][d] << 16), acc);
-                acc = __builtin_fmaf(__uint_as_float(av[d] & 0xFFFF0000u), __uint_as_float(bt[g][d] & 0xFFFF0000u),
-                                     acc);
-            }
-        }
-    }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    return value + acc;
+// This lane's four entries of a key row (A row u) or of a Bt row: entries [4 lane, 4 lane + 4).
+__device__ __forceinline__ u32x2 row_quad(const uint16_t* __restrict__ M, int u, int rank) {
+    const int lane = threadIdx.x & 63;
+    return 4 * lane < rank ? *(const u32x2*)(M + (size_t)u * rank + 4 * lane) : u32x2{0u, 0u};
 }
 
-__device__ __forceinline__ void load_bt_slice(u32x4 (&bt)[4], const uint16_t* __restrict__ Bt, int c, int rank) {
-    const int s = threadIdx.x & 7;
-    if (32 * s < rank) {
-        const u32x4* p = (const u32x4*)(Bt + (size_t)c * rank + 32 * s);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bt[g] = p[g];
-    } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bt[g] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// A key row into LDS (threads [t0, t0 + rank/8) load 16 bytes each).
-__device__ __forceinline__ void key_row_to_lds(uint16_t* dst, const uint16_t* __restrict__ A, int u, int rank, int t0) {
-    const int t = (int)threadIdx.x - t0;
-    if (t >= 0 && t < rank / 8) ((u32x4*)dst)[t] = ((const u32x4*)(A + (size_t)u * rank))[t];
-}
-
-// Entry e of row i's kept entries, through the row's (first slot, prefix) directory: the
-// item holding it is the last with prefix <= e.
+// Kept entry e (< the row's count) of row i: the item holding it is the last whose
+// prefix is <= e.
 __device__ __forceinline__ uint64_t kept_entry(const QLds& L, int i, int NC, uint32_t e) {
     int lo = 0, hi = NC - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((uint32_t)L.dir[i * NC + mid] <= e) lo = mid;
+        if (L.pfx[i * NC + mid] <= e) lo = mid;
         else hi = mid - 1;
     }
-    const uint64_t d = L.dir[i * NC + lo];
-    return L.stage[(uint32_t)(d >> 32) + (e - (uint32_t)d)];
+    const uint32_t slot = (uint32_t)(L.dir[i * NC + lo] >> 32) + (e - L.pfx[i * NC + lo]);
+    return L.stage[slot < (uint32_t)(kQS * kQStage) ? slot : 0u];
 }
 
-// Row `row` scored over the whole vocabulary with key row L.fix: the exact argmax (every
-// entry) for rows the bound does not prune.
-__device__ __forceinline__ int dense_row(const CandArgs& a, QLds& L, long row) {
-    const uint16_t* bp = a.base + (size_t)row * (size_t)a.V;
-    if (threadIdx.x == 0) L.dbest = 0ull;
-    __syncthreads();
-    uint64_t best = 0ull;
-    for (int v0 = 0; v0 < a.V; v0 += kQT / 8) {
-        const int v = v0 + (int)(threadIdx.x >> 3);
-        u32x4 bt[4];
-        load_bt_slice(bt, a.Bt, v < a.V ? v : 0, a.rank);
-        const float value = __uint_as_float((uint32_t)bp[v < a.V ? v : 0] << 16);
-        const float x = cand_x(bt, L.fix, a.rank, value);
-        if (v < a.V && (threadIdx.x & 7) == 0) best = umax64(best, argmax_key(x, (uint32_t)v));
-    }
-    best = wave_max_u64(best);
-    if ((threadIdx.x & 63) == 0) atomicMax((unsigned long long*)&L.dbest, (unsigned long long)best);
-    __syncthreads();
-    const int tok = key_index(L.dbest);
-    __syncthreads();
-    return tok;
-}
+// Candidates are scored two lanes each: lane pair (2c, 2c+1) takes candidate c, the even
+// lane rank entries [0, rank/2), the odd lane the rest.  kQHalf = the 16-byte groups a
+// lane holds (rank <= 256).
+constexpr int kQHalf = 16;
 
-// Row i's kept entries that clear its floor (rows with more candidates than the list
-// holds), scored with key row `arow`, into L.best[i].
-__device__ __forceinline__ void score_row_kept(const CandArgs& a, QLds& L, int i, int NC, const uint16_t* arow) {
-    const int n = L.npool[i];
-    const float fl = L.floor_[i];
-    for (int j0 = 0; j0 < n; j0 += kQT / 8) {
-        const int j = j0 + (int)(threadIdx.x >> 3);
-        const uint64_t e = j < n ? kept_entry(L, i, NC, (uint32_t)j) : 0ull;
-        const float value = __uint_as_float((uint32_t)e);
-        u32x4 b[4];
-        load_bt_slice(b, a.Bt, (int)(e >> 32), a.rank);
-        const float x = cand_x(b, arow, a.rank, value);
-        if (j < n && value >= fl && (threadIdx.x & 7) == 0)
-            atomicMax((unsigned long long*)&L.best[i], (unsigned long long)argmax_key(x, (uint32_t)(e >> 32)));
-    }
-}
-
-// Scores listed candidates with key rows from LDS and raises each row's key in L.best.
-// only < 0: every listed candidate, with its own row's guessed key row; only = i: the
-// candidates of row i alone, with L.fix.  Candidate j's Bt slice comes from this
-// thread's registers (j < kQRegCands: `bt`), from LDS (the next kQLdsCands) or from
-// global memory (the rest).
-__device__ __forceinline__ void score_pass(const CandArgs& a, QLds& L, const u32x4 (&bt)[4], int N, int only) {
-    const int tid = threadIdx.x, g = tid >> 3, s = tid & 7;
-    auto score = [&](const u32x4 (&b)[4], int j) {
-        const bool in = j < N;
-        const int i = in ? L.frow[j] : 0;
-        const uint64_t e = in ? L.flat[j] : 0ull;
-        const bool live = in && (only < 0 || i == only);
-        const float x = cand_x(b, only < 0 ? L.arow[i] : L.fix, a.rank, __uint_as_float((uint32_t)e));
-        if (live && s == 0)
-            atomicMax((unsigned long long*)&L.best[i], (unsigned long long)argmax_key(x, (uint32_t)(e >> 32)));
-    };
-    score(bt, g);
-    if (kQRegCands < N) {
-        const int j = kQRegCands + g;  // kQLdsCands == kQT / 8: one LDS candidate per 8 threads
-        u32x4 b[4];
+// This lane's half of Bt row v (rank/16 16-byte groups).
+__device__ __forceinline__ void load_bt_half(u32x4 (&bt)[kQHalf], const uint16_t* __restrict__ Bt, int v, int rank) {
+    const int half = threadIdx.x & 1, ng = rank / 16;
+    const u32x4* b = (const u32x4*)(Bt + (size_t)v * rank) + half * ng;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) b[q] = ((const u32x4*)(L.btrow[g] + 32 * s))[q];
-        score(b, j);
+    for (int g = 0; g < kQHalf; ++g) bt[g] = g < ng ? b[g] : u32x4{0u, 0u, 0u, 0u};
+}
+
+// x for this lane pair's entry: fl32(value + the dot product of the key row in L.akey and
+// the Bt row, each half by fused multiply-adds in increasing k, then the two halves
+// added).  Both lanes of the pair end with the same value.
+__device__ __forceinline__ float pair_x(const QLds& L, const u32x4 (&bt)[kQHalf], int rank, float value) {
+    const int half = threadIdx.x & 1, ng = rank / 16;
+    const u32x4* k = (const u32x4*)L.akey + half * ng;
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < kQHalf; ++g) {
+        if (g < ng) {
+            const u32x4 kv = k[g], bv = bt[g];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                acc = __builtin_fmaf(__uint_as_float(kv[d] << 16), __uint_as_float(bv[d] << 16), acc);
+                acc = __builtin_fmaf(__uint_as_float(kv[d] & 0xFFFF0000u), __uint_as_float(bv[d] & 0xFFFF0000u), acc);
+            }
+        }
     }
-    for (int j0 = kQRegCands + kQLdsCands; j0 < N; j0 += kQT / 8) {
-        const int j = j0 + g;
-        u32x4 b[4];
-        load_bt_slice(b, a.Bt, j < N ? (int)(L.flat[j] >> 32) : 0, a.rank);
-        score(b, j);
+    const float other = __shfl_xor(acc, 1, 64);
+    return value + (half ? other + acc : acc + other);
+}
+
+// Row `row` scored over the whole vocabulary with the key row in L.akey, 32 entries at a
+// time.  Returns the argmax key (every lane alike).
+__device__ __forceinline__ uint64_t dense_row(const QLds& L, const uint16_t* __restrict__ bp, int V,
+                                              const uint16_t* __restrict__ Bt, int rank) {
+    const int pair = (threadIdx.x & 63) >> 1;
+    uint64_t best = 0ull;
+    for (int v0 = 0; v0 < V; v0 += 32) {
+        const int v = v0 + pair < V ? v0 + pair : V - 1;
+        u32x4 bt[kQHalf];
+        load_bt_half(bt, Bt, v, rank);
+        const float x = pair_x(L, bt, rank, __uint_as_float((uint32_t)bp[v] << 16));
+        if (v0 + pair < V) best = umax64(best, argmax_key(x, (uint32_t)v));
+    }
+    return wave_max_u64(best);
+}
+
+// Scores L.clist[0, n) with the key row in L.akey into best, 64 candidates at a time
+// (lane pair p takes candidates p and p + 32; all their Bt loads are in flight together).
+__device__ __forceinline__ void score_list(const QLds& L, uint32_t n, const uint16_t* __restrict__ Bt, int rank,
+                                           uint64_t& best) {
+    const uint32_t pair = (threadIdx.x & 63) >> 1;
+    for (uint32_t c0 = 0; c0 < n; c0 += 64) {
+        const uint32_t c = c0 + pair, c2 = c + 32;
+        const uint64_t e = c < n ? L.clist[c] : L.clist[c0];
+        const uint64_t e2 = c2 < n ? L.clist[c2] : L.clist[c0];
+        u32x4 bt[kQHalf], bt2[kQHalf];
+        load_bt_half(bt, Bt, (int)(e >> 32), rank);
+        if (c0 + 32 < n) load_bt_half(bt2, Bt, (int)(e2 >> 32), rank);
+        const float x = pair_x(L, bt, rank, __uint_as_float((uint32_t)e));
+        if (c < n) best = umax64(best, argmax_key(x, (uint32_t)(e >> 32)));
+        if (c0 + 32 < n) {
+            const float x2 = pair_x(L, bt2, rank, __uint_as_float((uint32_t)e2));
+            if (c2 < n) best = umax64(best, argmax_key(x2, (uint32_t)(e2 >> 32)));
+        }
     }
 }
 
-// The chain of request r, streamed into L (see the file comment).
-__device__ __forceinline__ void chain_request(const CandArgs& a, QLds& L, int r, float ab2, bool bound_ok) {
-    const int K = a.K, NC = a.NC, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// The chain wave's work on request r (see the file comment).
+__device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, float ab2, bool bound_ok) {
+    const int lane = threadIdx.x & 63;
+    const int K = a.K, NC = a.NC, V = a.V, rank = a.rank;
     const long row0 = (long)r * K;
-    // (a) the rows' kinds and final floors
-    if (tid < K) {
-        const uint32_t nk = L.rownan[tid];
-        const float M = unord32(L.rowmax[tid]);
-        L.nanidx[tid] = (int)~nk;
-        L.kind[tid] = nk ? 1 : (M == -__builtin_huge_valf() ? 2 : (bound_ok ? 0 : 3));
-        L.floor_[tid] = cand_floor(M, ab2);
-        L.best[tid] = 0ull;
+    constexpr float kNegInf = -__builtin_huge_valf();
+    int prev = a.prev0[r];
+    if (prev < 0 || prev >= V) {
+        if (lane == 0) raise_status(a.status, kStatusPrevClamped);
+        prev = prev < 0 ? 0 : V - 1;
     }
-    if (tid == 0) {
-        int p = a.prev0[r];
-        if (p < 0 || p >= a.V) {
-            raise_status(a.status, kStatusPrevClamped);
-            p = p < 0 ? 0 : a.V - 1;
+    u32x2 key = row_quad(a.A, prev, rank);  // key row of the current position
+    for (int i = 0; i < K; ++i) {
+        // the row's items are all kept
+        long n_polls = 0;
+        while (__hip_atomic_load(&L.rowdone[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)NC) {
+            if (++n_polls > kQSpinLimit) {
+                if (lane == 0) raise_status(a.status, kStatusSyncTimeout);
+                return;  // the rest of the request's tokens are left unwritten (the status says so)
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-        L.guess[0] = p;
-    }
-    __syncthreads();
-    // (b) per row (one wave each): the items' counts and their prefix, then the kept
-    // entries that clear the row's final floor: how many, and the largest (lowest index
-    // among equals)
-    for (int i = w; i < K; i += kQW) {
-        uint32_t cnt = 0, start = 0;
-        bool over = false;
+        asm volatile("" ::: "memory");
+        // the row's directory: counts, their prefix, overflow
+        uint32_t cnt = 0;
+        bool ov = false;
         if (lane < NC) {
-            const uint64_t d = L.dir[i * NC + lane];
-            cnt = (uint32_t)d;
-            start = (uint32_t)(d >> 32);
-            over = cnt == kQOverflow;
+            cnt = (uint32_t)L.dir[i * NC + lane];
+            ov = cnt == kQOverflow;
         }
-        const bool any_over = __ballot(over) != 0ull;
-        if (any_over) cnt = 0;
+        const bool over = __ballot(ov) != 0ull;
+        if (over) cnt = 0;
         uint32_t total = 0;
         const uint32_t pre = wave_excl_scan(cnt, &total);
-        if (lane < NC) L.dir[i * NC + lane] = ((uint64_t)start << 32) | pre;
+        if (lane < NC) L.pfx[i * NC + lane] = pre;
         wave_lds_sync();
-        const bool use = L.kind[i] == 0 && !any_over;
-        const float fl = L.floor_[i];
-        uint32_t kept = 0, best_u = 0, best_v = 0xFFFFFFFFu;
-        for (uint32_t e0 = 0; use && e0 < total; e0 += 64) {
-            const uint32_t e = e0 + lane;
-            const uint64_t ent = e < total ? kept_entry(L, i, NC, e) : 0ull;
-            const bool ok = e < total && __uint_as_float((uint32_t)ent) >= fl;
-            if (ok) {
-                const uint32_t u = ord32(__uint_as_float((uint32_t)ent)), v = (uint32_t)(ent >> 32);
-                if (u > best_u || (u == best_u && v < best_v)) {
-                    best_u = u;
-                    best_v = v;
-                }
-            }
-            kept += (uint32_t)__builtin_popcountll(__ballot(ok));
-        }
-        uint64_t k = best_u ? (((uint64_t)best_u << 32) | (uint64_t)(~best_v)) : 0ull;
-        k = wave_max_u64(k);
-        if (lane == 0) {
-            // overflowed buffers mean lost candidates: the row is scored densely
-            if (L.kind[i] == 0 && any_over) L.kind[i] = 3;
-            if (L.kind[i] == 0 && kept == 0) L.kind[i] = 3;  // cannot occur: its maximum clears the floor
-            L.rowcnt[i] = L.kind[i] == 0 ? (int)kept : 0;
-            L.npool[i] = L.kind[i] == 0 ? (int)total : 0;
-            // the token row i most likely gets: its largest candidate, its first NaN, or 0
-            L.top[i] = L.kind[i] == 1 ? L.nanidx[i] : (L.kind[i] == 0 ? key_index(k) : 0);
-        }
-    }
-    __syncthreads();
-    // the rows' lists in one LDS list (a row that does not fit is scored from its kept
-    // entries), and the key rows guessed for each position
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < K; ++i) {
-            if (L.kind[i] == 0 && acc + L.rowcnt[i] > kCandListCap) L.kind[i] = 4;
-            L.rowstart[i] = acc;
-            if (L.kind[i] == 0) acc += L.rowcnt[i];
-        }
-        L.ntot = acc;
-    }
-    if (tid > 0 && tid < K) L.guess[tid] = L.top[tid - 1];
-    __syncthreads();
-    for (int i = w; i < K; i += kQW) {
-        if (L.kind[i] != 0) continue;
-        const uint32_t n_kept = (uint32_t)L.npool[i];
-        const float fl = L.floor_[i];
-        uint32_t placed = (uint32_t)L.rowstart[i];
-        for (uint32_t e0 = 0; e0 < n_kept; e0 += 64) {
-            const uint32_t e = e0 + lane;
-            const uint64_t ent = e < n_kept ? kept_entry(L, i, NC, e) : 0ull;
-            const bool ok = e < n_kept && __uint_as_float((uint32_t)ent) >= fl;
-            const uint64_t bal = __ballot(ok);
-            if (ok) {
-                const uint32_t at = placed + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-                L.flat[at] = ent;
-                L.frow[at] = (uint8_t)i;
-            }
-            placed += (uint32_t)__builtin_popcountll(bal);
-        }
-    }
-    __syncthreads();
-    const int N = L.ntot;
-    // (c) the listed candidates' Bt slices (registers, then LDS) and the guessed key rows
-    u32x4 bt[4];
-    load_bt_slice(bt, a.Bt, (tid >> 3) < N ? (int)(L.flat[tid >> 3] >> 32) : 0, a.rank);
-    {
-        const int j = kQRegCands + (tid >> 3);
-        if (j < N && j < kQRegCands + kQLdsCands) {
-            u32x4 b1[4];
-            load_bt_slice(b1, a.Bt, (int)(L.flat[j] >> 32), a.rank);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ((u32x4*)(L.btrow[j - kQRegCands] + 32 * (tid & 7)))[q] = b1[q];
-        }
-    }
-    for (int i = 0; i < K; ++i) key_row_to_lds(L.arow[i], a.A, L.guess[i], a.rank, i * 32);
-    __syncthreads();
-    // (d) every position scored with its guessed key row
-    score_pass(a, L, bt, N, -1);
-    for (int i = 0; i < K; ++i)
-        if (L.kind[i] == 4) score_row_kept(a, L, i, NC, L.arow[i]);
-    __syncthreads();
-    // (e) the walk
-    int prev = L.guess[0];
-    for (int i = 0; i < K; ++i) {
-        const int kind = L.kind[i];
+        if (4 * lane < rank) *(u32x2*)(L.akey + 4 * lane) = key;  // this position's key row, for every lane
+        wave_lds_sync();
+        const uint32_t nk = L.rownan[i];
+        const float M = unord32(L.rowmax[i]);
+        // (a row of candidates always keeps its maximum; an empty one is scored densely all the same)
+        const int kind = nk ? 1 : (M == kNegInf ? 2 : ((!bound_ok || over || total == 0) ? 3 : 0));
         int tok;
+        u32x2 next_key{0u, 0u};
+        bool have_next = false;
         if (kind == 1) {
-            tok = L.nanidx[i];
+            tok = (int)~nk;
         } else if (kind == 2) {
             tok = 0;
-        } else if ((kind == 0 || kind == 4) && prev == L.guess[i]) {
-            tok = key_index(L.best[i]);
+        } else if (kind == 3) {
+            tok = key_index(dense_row(L, a.base + (size_t)(row0 + i) * (size_t)V, V, a.Bt, rank));
         } else {
-            // the guess missed, or the row is scored densely: row i with prev's key row
-            key_row_to_lds(L.fix, a.A, prev, a.rank, 0);
-            if (tid == 0) L.best[i] = 0ull;
-            __syncthreads();
-            if (kind == 3) {
-                tok = dense_row(a, L, row0 + i);
-            } else {
-                if (kind == 0) score_pass(a, L, bt, N, i);
-                else score_row_kept(a, L, i, NC, L.fix);
-                __syncthreads();
-                tok = key_index(L.best[i]);
+            // list the kept entries that clear the final floor, score them in lists of
+            // at most kQList; note the largest (the likely token)
+            const float fl = cand_floor(M, ab2);
+            uint64_t best = 0ull, top = 0ull;
+            uint32_t n = 0;
+            bool prefetched = false;
+            for (uint32_t e0 = 0; e0 < total; e0 += 64) {
+                const uint32_t e = e0 + lane;
+                const uint64_t ent = e < total ? kept_entry(L, i, NC, e) : 0ull;
+                const bool ok = e < total && __uint_as_float((uint32_t)ent) >= fl;
+                const uint64_t bal = __ballot(ok);
+                if (ok) {
+                    L.clist[n + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] = ent;
+                    top = umax64(top, argmax_key(__uint_as_float((uint32_t)ent), (uint32_t)(ent >> 32)));
+                }
+                n += (uint32_t)__builtin_popcountll(bal);
+                const bool last = e0 + 64 >= total;
+                if (last && !prefetched && i + 1 < K) {
+                    // the next position's key row, for the likely token, while this row is scored
+                    top = wave_max_u64(top);
+                    next_key = row_quad(a.A, key_index(top), rank);
+                    prefetched = true;
+                }
+                if (n > (uint32_t)(kQList - 64) || last) {
+                    wave_lds_sync();
+                    score_list(L, n, a.Bt, rank, best);
+                    wave_lds_sync();
+                    n = 0;
+                }
             }
-            __syncthreads();  // L.fix and L.best[i] are read before the next re-score
+            tok = key_index(wave_max_u64(best));
+            have_next = prefetched && key_index(top) == tok;
         }
-        if (tid == 0) L.tok[i] = tok;
-        prev = tok;
+        wave_lds_sync();  // L.akey is read before the next position's key row is written
+        if (lane == 0) a.tokens[row0 + i] = tok;
+        if (i + 1 < K) key = have_next ? next_key : row_quad(a.A, tok, rank);
     }
-    __syncthreads();
-    if (tid < K) a.tokens[row0 + tid] = L.tok[tid];
 }
 
-// Stage 1 in one launch: workgroup g streams and chains requests g, g + G, ...
+// Stage 1 in one launch: workgroup g takes requests g, g + G, ...
 template <bool VEC>
 __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
     __shared__ QLds S;
     const HeaderView hv = header_view(a.hdr);
+    const int per_req = a.K * a.NC;
     for (int r = blockIdx.x; r < a.R; r += (int)gridDim.x) {
-        stream_request<VEC>(a, S, r, hv.ab2);
-        chain_request(a, S, r, hv.ab2, hv.ok);
+        if ((int)threadIdx.x < a.K) {
+            S.rowmax[threadIdx.x] = 0u;
+            S.rownan[threadIdx.x] = 0u;
+            S.rowdone[threadIdx.x] = 0u;
+        }
+        __syncthreads();
+        if ((int)(threadIdx.x >> 6) < kQS)
+            stream_items<VEC>(S, a.base + (size_t)r * (size_t)a.K * (size_t)a.V, per_req, a.NC, a.V, hv.ab2);
+        else
+            chain_wave(a, S, r, hv.ab2, hv.ok);
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
     }
 }

@@ -145,7 +145,7 @@ constexpr int kCandMaxItems = 64;
 constexpr int kCandItem = 4096;           // base entries per streaming item
 constexpr int kCandListCap = 2048;        // filtered candidates of one request in LDS
 constexpr int kCandWaveCap = 1024;        // least candidate-pool entries per streaming wave
-constexpr int kCandWaveStage = 256;       // candidates a wave stages in LDS between write-outs
+constexpr int kCandWaveStage = 1024;      // entries a streaming wave of the pruned chain keeps in LDS for one request
 constexpr int kCandWaveItems = 256;       // items a wave stages between write-outs
 constexpr int kCandMaxGroups = 256;       // streaming workgroups a workspace is sized for
 constexpr int kCandWaves = kCandMaxGroups * 16;
