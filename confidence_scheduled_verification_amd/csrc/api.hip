@@ -57,7 +57,9 @@ size_t keys_bytes(int R, int K) { return dspark::ws_total_bytes(R, K); }
 // Workspace bytes a call of this shape needs: the dense paths' region, then for bf16 the
 // pruned chain's candidate buffers.
 size_t ws_need(int R, int K, int V, int dtype) {
-    return keys_bytes(R, K) + (dtype == DSPARK_BF16 ? dspark::ws_cand_bytes(R, K, V) : 0);
+    (void)V;
+    (void)dtype;
+    return keys_bytes(R, K);
 }
 
 int check_markov(const dspark_markov_t* m, const void* A, const void* Bmat, int V, int rank, int dtype) {
@@ -85,9 +87,6 @@ bool use_pruned(int dtype, int R, int K, int V, const void* A, const float* chai
 
 dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int32_t* prev0, int R, int K, int V,
                            int rank, int32_t* tokens, uint32_t* status, void* ws) {
-    char* w = (char*)ws;
-    uint32_t* ctr = (uint32_t*)(w + dspark::ws_sync_bytes());
-    char* tail = w + keys_bytes(R, K);
     dspark::CandArgs a{};
     a.base = (const uint16_t*)base;
     a.A = (const uint16_t*)m->A;
@@ -101,14 +100,7 @@ dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int
     a.NC = dspark::cand_items_per_row(V);
     a.tokens = tokens;
     a.status = status;
-    a.rowkey = ctr;
-    a.rownan = ctr + dspark::kMaxSlotsWs;
-    a.done = ctr + 2 * dspark::kMaxSlotsWs;
-    a.next = ctr + 3 * dspark::kMaxSlotsWs;
-    a.exited = a.next + 1;
-    a.wave_cap = (uint32_t)dspark::cand_wave_cap(R, K, V);
-    a.dir = (uint64_t*)tail;
-    a.ent = (uint64_t*)(tail + dspark::ws_round((size_t)R * K * a.NC * 8));
+    (void)ws;
     return a;
 }
 
@@ -341,7 +333,8 @@ int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dty
                                     std::min((int)ns, verify_len - 1 - T), rule};
     hipError_t e;
     if (n > 0 && use_pruned(dtype, R, K, V, A, nullptr)) {
-        // the chain, then stages 2-5 over the confidences and the verified tokens
+        // the chain, then stages 2-5 over the confidences and the verified tokens (in the
+        // method the confidences score the drafted tokens, so the schedule follows)
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
         e = dspark::launch_cand(cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws), num_cu(), s);

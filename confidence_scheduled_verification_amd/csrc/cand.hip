@@ -24,24 +24,26 @@
 // weights whose bound is not finite, are scored densely.
 //
 // One workgroup per compute unit takes requests g, g + G, ... whole, so a request's
-// candidates never leave the compute unit's LDS.  Its nine waves split the work:
+// candidates never leave the compute unit's LDS.  Its eight waves (two per SIMD) split
+// the work:
 //
-// Streaming (waves 0-7).  The request's K*V base entries are items of 4096 entries (a row
-// is ceil(V/4096) items); wave w takes items w, w + 8, ..., with the next two items'
-// loads always in flight, and never waits for the other waves.  For each item it folds
-// the item's maximum into the row's maximum in LDS and keeps the entries that clear the
-// floor of the row's maximum seen so far (a lower bound of the final one, so nothing that
-// can win is dropped), with one directory word for the item, in its part of the LDS; then
-// it counts the item into its row.
+// Streaming (waves 0-6).  The request's K*V base entries are items of 4096 entries (a row
+// is ceil(V/4096) items); a wave takes the next item from an LDS counter whenever it
+// starts a load, keeps the next two items' loads in flight, and never waits for the
+// other waves.  For each item it folds the item's maximum into the row's maximum in LDS
+// and keeps the entries that clear the floor of the row's maximum seen so far (a lower
+// bound of the final one, so nothing that can win is dropped), with one directory word
+// for the item, in its part of the LDS; then it counts the item into its row.
 //
-// Chain (wave 8), concurrently.  Position by position it waits for the row's count to
-// reach its item count, lists the kept entries that clear the row's final floor, loads
-// their Bt rows (one 8-byte slice per lane) and scores them with the key row of the
-// previous token (x = value + the lanes' partial dot products summed over the wave).
-// The key row of the next position is prefetched for the row's largest entry -- the
-// token unless the bias reorders the top -- while the row is scored, and loaded again
-// only when that guess misses.  So the chain keeps up with the streaming, and only the
-// last row's scoring is left once the last item arrives.
+// Chain (wave 7), concurrently.  Position by position it waits for the row's count to
+// reach its item count, lists the kept entries that clear the row's final floor, and
+// scores them with the key row of the previous token, two lanes per candidate with the
+// whole Bt rows of up to 64 candidates in flight at once (x = value + the dot product,
+// each lane's half by fused multiply-adds in increasing k, then the halves added).  The
+// key row of the next position is prefetched for the row's largest entry -- the token
+// unless the bias reorders the top -- while the row is scored, and loaded again only
+// when that guess misses.  So the chain keeps up with the streaming, and only the last
+// row's scoring is left once the last item arrives.
 #include "common.h"
 #include "kernels.h"
 
@@ -147,6 +149,7 @@ struct QLds {
     uint32_t rowmax[kCandMaxK];              // the rows' maxima so far (order-preserving image; 0 = none yet)
     uint32_t rownan[kCandMaxK];              // ~(first NaN index), 0 = none
     uint32_t rowdone[kCandMaxK];             // items of the row kept so far
+    uint32_t next;                           // the next item to hand to a streaming wave
 };
 
 // LDS writes of this wave complete, and not moved past this point by the compiler.  (A
@@ -289,14 +292,20 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
     if (lane == 0) __hip_atomic_fetch_add(&L.rowdone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// A streaming wave's items of one request: w, w + kQS, ..., each loaded two items ahead
-// (three buffers in turn, so no item waits for another's loads; one ahead with
-// element-wise loads).  An item past the request loads nothing (v0 = V: every entry
-// reads as -inf).
+// A streaming wave's items of one request: it takes the next item from the workgroup's
+// counter whenever it starts loading one, so that waves which happen to be served faster
+// take more, and items are taken in order (rows complete in order).  Each item is loaded
+// two items ahead (three buffers in turn, so no item waits for another's loads; one
+// ahead with element-wise loads).  An item past the request loads nothing (v0 = V: every
+// entry reads as -inf).
 template <bool VEC>
 __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int per_req, int NC, int V, float ab2) {
-    const int w = threadIdx.x >> 6;
     uint32_t used = 0;
+    auto claim = [&]() -> int {
+        uint32_t j = 0u;
+        if ((threadIdx.x & 63) == 0) j = atomicAdd(&L.next, 1u);
+        return (int)__builtin_amdgcn_readfirstlane(j);
+    };
     auto issue = [&](u32x4 (&buf)[8], int j) {
         const bool ok = j < per_req;
         load_item<VEC>(buf, rbase + (size_t)(ok ? j / NC : 0) * V, ok ? (j % NC) * kQItem : V, V);
@@ -309,25 +318,32 @@ __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int
     };
     if (VEC) {
         u32x4 b0[8], b1[8], b2[8];
-        issue(b0, w);
-        issue(b1, w + kQS);
-        for (int j = w; j < per_req; j += 3 * kQS) {
-            issue(b2, j + 2 * kQS);
-            take(b0, j);
-            issue(b0, j + 3 * kQS);
-            take(b1, j + kQS);
-            issue(b1, j + 4 * kQS);
-            take(b2, j + 2 * kQS);
+        int j0 = claim(), j1 = claim(), j2;
+        issue(b0, j0);
+        issue(b1, j1);
+        while (j0 < per_req) {
+            j2 = claim();
+            issue(b2, j2);
+            take(b0, j0);
+            j0 = claim();
+            issue(b0, j0);
+            take(b1, j1);
+            j1 = claim();
+            issue(b1, j1);
+            take(b2, j2);
         }
     } else {
         // element-wise loads take more registers: one item ahead
         u32x4 b0[8], b1[8];
-        issue(b0, w);
-        for (int j = w; j < per_req; j += 2 * kQS) {
-            issue(b1, j + kQS);
-            take(b0, j);
-            issue(b0, j + 2 * kQS);
-            take(b1, j + kQS);
+        int j0 = claim(), j1;
+        issue(b0, j0);
+        while (j0 < per_req) {
+            j1 = claim();
+            issue(b1, j1);
+            take(b0, j0);
+            j0 = claim();
+            issue(b0, j0);
+            take(b1, j1);
         }
     }
 }
@@ -529,6 +545,7 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
             S.rownan[threadIdx.x] = 0u;
             S.rowdone[threadIdx.x] = 0u;
         }
+        if (threadIdx.x == 0) S.next = 0u;
         __syncthreads();
         if ((int)(threadIdx.x >> 6) < kQS)
             stream_items<VEC>(S, a.base + (size_t)r * (size_t)a.K * (size_t)a.V, per_req, a.NC, a.V, hv.ab2);

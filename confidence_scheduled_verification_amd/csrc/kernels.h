@@ -30,11 +30,7 @@ inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
 // Keys and chain counters: what the stage-wise paths clear.
 inline size_t ws_chain_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
-// The pruned chain's counters at a fixed offset (so that calls of every shape find them
-// at zero): row maxima and NaN marks (one u32 per slot each), per-request item counts,
-// then the chunk counter and the count of waves done with the streaming.
-inline size_t ws_cand_ctr_bytes() { return ws_round((size_t)kMaxSlotsWs * 4 * 3 + 8); }
-inline size_t ws_chain_off() { return ws_sync_bytes() + ws_cand_ctr_bytes(); }
+inline size_t ws_chain_off() { return ws_sync_bytes(); }
 inline size_t ws_total_bytes(int R, int K) { return ws_chain_off() + ws_chain_bytes(R, K); }
 
 // Probabilistic drafting: Gumbel-max sampling of softmax(x / temperature) with
@@ -143,29 +139,11 @@ struct StepArgs {
 constexpr int kCandMaxK = 32;
 constexpr int kCandMaxItems = 64;
 constexpr int kCandItem = 4096;           // base entries per streaming item
-constexpr int kCandListCap = 2048;        // filtered candidates of one request in LDS
-constexpr int kCandWaveCap = 1024;        // least candidate-pool entries per streaming wave
-constexpr int kCandWaveStage = 1024;      // entries a streaming wave of the pruned chain keeps in LDS for one request
-constexpr int kCandWaveItems = 256;       // items a wave stages between write-outs
-constexpr int kCandMaxGroups = 256;       // streaming workgroups a workspace is sized for
-constexpr int kCandWaves = kCandMaxGroups * 16;
+constexpr int kCandWaveStage = 1024;      // entries a streaming wave keeps in LDS for one request
+constexpr int kCandMaxGroups = 256;       // workgroups of one launch at most
 constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, then Bt
 
 inline int cand_items_per_row(int V) { return (V + kCandItem - 1) / kCandItem; }
-// Candidate-pool entries per streaming wave for this shape: kCandWaveCap, or 64 per
-// item of the wave's average share if that is more (items hold a few tens at most).
-inline size_t cand_wave_cap(int R, int K, int V) {
-    const size_t items = (size_t)R * K * cand_items_per_row(V);
-    const size_t per_wave = (items + kCandWaves - 1) / kCandWaves;
-    return per_wave * 64 > (size_t)kCandWaveCap ? per_wave * 64 : (size_t)kCandWaveCap;
-}
-// After ws_total_bytes(R, K), bf16 workspaces hold the pruned chain's item directory
-// [R*K*items] u64 and the wave buffers [kCandWaves][kCandWaveCap] u64, rewritten by
-// every launch.  (Its counters sit at ws_sync_bytes(), zero between launches: each
-// chain puts its request's back.)
-inline size_t ws_cand_bytes(int R, int K, int V) {
-    return ws_round((size_t)R * K * cand_items_per_row(V) * 8) + (size_t)kCandWaves * cand_wave_cap(R, K, V) * 8;
-}
 
 struct CandArgs {
     const uint16_t* base;
@@ -176,14 +154,6 @@ struct CandArgs {
     int R, K, V, rank, NC;
     int32_t* tokens;
     uint32_t* status;
-    uint32_t* rowkey;  // [R*K] row maxima (order-preserving image)
-    uint32_t* rownan;  // [R*K] ~(first NaN index), 0 = none
-    uint32_t* done;    // [R] items streamed per request
-    uint32_t* next;    // [1] chunks handed out
-    uint32_t* exited;  // [1] waves done with the streaming
-    uint64_t* dir;     // [R*K*NC] per item: (first entry << 32) | count
-    uint64_t* ent;     // [waves * wave_cap] (index << 32) | value bits
-    uint32_t wave_cap; // candidate-pool entries per wave
 };
 
 int chain_tile_vocab();

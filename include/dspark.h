@@ -94,12 +94,12 @@ const char* dspark_version(void);
 /* Bytes of device workspace needed by dspark_chain / dspark_chain_sample / dspark_step /
  * dspark_step_sized for this shape (0 when R*K == 0).  Zero-fill a workspace once, before
  * its first use: the kernels keep counters in it (grid-barrier counters and a ready flag
- * of the dense single-launch step; per-row and per-request counters of the pruned chain)
- * and put each back to zero before they end, so later calls need no clearing.  A call
- * that ends with DSPARK_STATUS_SYNC_TIMEOUT may leave counters set: zero-fill the
+ * of the dense single-launch step) and put each back to zero before they end, so later
+ * calls need no clearing.  A
+ * call that ends with DSPARK_STATUS_SYNC_TIMEOUT may leave counters set: zero-fill the
  * workspace again before its next use.  A workspace sized for one shape serves any
- * smaller R and K (and any V and rank of the same dtype); bf16 workspaces include the
- * pruned chain's candidate buffers (about 33 MB). */
+ * smaller R and K and any V, rank and dtype (the pruned chain keeps its candidates in
+ * LDS). */
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
 
 /*
