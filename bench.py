@@ -719,6 +719,9 @@ def main():
         "step_bytes": sb["total"],
         "step_hbm_frac": round(sb["total"] / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "step_us_loop_events": round(loop_ms * 1e3 / K, 2),
+        # the step in the method's order: the chain, then stages 2-5 over the confidences
+        # (the reported value is this serial step; no part of the schedule overlaps the chain)
+        "serial_step_us": round(ms_per_step * 1e3, 2) if pruned else None,
         "event_pass": {"steps": KE, "step_us": round(float(step_ms.mean()) * 1e3, 2),
                        "before_chain_us": round(float(pre_ms.mean()) * 1e3, 2),
                        "chain_us": round(float(chain_ms.mean()) * 1e3, 2),

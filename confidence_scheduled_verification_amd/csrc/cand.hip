@@ -87,10 +87,50 @@ __device__ __forceinline__ float cand_floor(float M, float ab2) {
     return (M - ab2) - __builtin_fabsf(M) * 0x1p-20f;
 }
 
+// DPP lane moves within rows of 16 lanes (no LDS round trip, unlike a shuffle).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16
+
+__device__ __forceinline__ float dpp_f32(float x, int ctrl) {
+    switch (ctrl) {  // the control must be a constant of the builtin
+        case kDppXor1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor1, 0xF, 0xF, false));
+        case kDppXor2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor2, 0xF, 0xF, false));
+        case kDppHalfMirror:
+            return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppHalfMirror, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppMirror, 0xF, 0xF, false));
+    }
+}
+
+// The maximum over the wave (NaN if any lane holds one), the same in every lane: within
+// rows of 16 by lane moves, then the four rows' values read out.
 __device__ __forceinline__ float wave_max(float x) {
+    x = __builtin_elementwise_maximum(x, dpp_f32(x, kDppXor1));
+    x = __builtin_elementwise_maximum(x, dpp_f32(x, kDppXor2));
+    x = __builtin_elementwise_maximum(x, dpp_f32(x, kDppHalfMirror));
+    x = __builtin_elementwise_maximum(x, dpp_f32(x, kDppMirror));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(r0, r1), __builtin_elementwise_maximum(r2, r3));
+}
+
+// Exclusive prefix sum over the wave of values below 128, from one ballot per bit (no
+// LDS round trip); *total receives the sum.
+__device__ __forceinline__ uint32_t wave_excl_scan_small(uint32_t v, uint32_t* total) {
+    uint32_t pre = 0u, tot = 0u;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, o, 64));
-    return x;
+    for (int b = 0; b < 7; ++b) {
+        const uint64_t m = __ballot((v >> b) & 1u);
+        const uint32_t below =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        pre += below << b;
+        tot += (uint32_t)__builtin_popcountll(m) << b;
+    }
+    *total = tot;
+    return pre;
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
@@ -202,6 +242,26 @@ __device__ __forceinline__ void group_maxima(const u32x4 (&cur)[8], float (&gm)[
     }
 }
 
+// Word d (0..3, not a constant) of a 16-byte group, by selects.
+__device__ __forceinline__ uint32_t pick_word(const u32x4& g, int d) {
+    const uint32_t lo = (d & 1) ? g[1] : g[0];
+    const uint32_t hi = (d & 1) ? g[3] : g[2];
+    return (d & 2) ? hi : lo;
+}
+
+// Bit t of the result: entry t (0..7) of 16-byte group `g` is >= fl and above -inf.
+__device__ __forceinline__ uint32_t pass_mask(const u32x4& g, float fl) {
+    constexpr float kNegInf = -__builtin_huge_valf();
+    uint32_t mk = 0u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const float lo = __uint_as_float(g[d] << 16), hi = __uint_as_float(g[d] & 0xFFFF0000u);
+        mk |= (lo >= fl && lo > kNegInf) ? (1u << (2 * d)) : 0u;
+        mk |= (hi >= fl && hi > kNegInf) ? (2u << (2 * d)) : 0u;
+    }
+    return mk;
+}
+
 // Entry t (0..7) of 16-byte group `word4` as a float.  The word goes through an empty asm
 // statement first, so the compiler recomputes the unpacking where it is used instead of
 // keeping all 64 unpacked entries of an item live across the passes over it.
@@ -249,35 +309,38 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
         seen = __builtin_amdgcn_readfirstlane(seen);
         const uint32_t now = seen > ord32(mw) ? seen : ord32(mw);
         const float fl = cand_floor(unord32(now), ab2);
-        bool any = false;
+        // per 8-entry group, a mask of this lane's entries that clear the floor; groups
+        // no lane needs are skipped by the whole wave
+        uint32_t gmask[8];
+        uint32_t c = 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) any |= gm[q] >= fl && gm[q] > kNegInf;
-        if (__ballot(any) != 0ull) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (gm[q] >= fl && gm[q] > kNegInf) {
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const float x = entry_of(cur[q], s);
-                        c += (x >= fl && x > kNegInf) ? 1u : 0u;
-                    }
-                }
+        for (int q = 0; q < 8; ++q) {
+            const bool need = gm[q] >= fl && gm[q] > kNegInf;
+            uint32_t mk = 0u;
+            if (need) {
+                // (a branch, not a select: a group that no lane needs is skipped by the wave)
+                asm volatile("");
+                mk = pass_mask(cur[q], fl);
             }
-            uint32_t total = 0;
-            uint32_t slot = first_slot + wave_excl_scan(c, &total);
+            gmask[q] = mk;
+            c += (uint32_t)__builtin_popcount(mk);
+        }
+        uint32_t total = 0;
+        const uint32_t before = wave_excl_scan_small(c, &total);
+        if (total != 0u) {
             if (used + total <= (uint32_t)kQStage) {
+                uint32_t slot = first_slot + before;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    if (gm[q] >= fl && gm[q] > kNegInf) {
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) {
-                            const float x = entry_of(cur[q], s);
-                            if (x >= fl && x > kNegInf) {
-                                const uint32_t v = (uint32_t)(v0 + q * 512 + lane * 8 + s);
-                                L.stage[slot++] = ((uint64_t)v << 32) | __float_as_uint(x);
-                            }
-                        }
+                    if (__ballot(gmask[q] != 0u) == 0ull) continue;
+                    uint32_t mk = gmask[q];
+                    while (mk != 0u) {
+                        const int t = __builtin_ctz(mk);
+                        mk &= mk - 1u;
+                        const uint32_t word = pick_word(cur[q], t >> 1);
+                        const uint32_t bits = (t & 1) ? (word & 0xFFFF0000u) : (word << 16);
+                        const uint32_t v = (uint32_t)(v0 + q * 512 + lane * 8 + t);
+                        L.stage[slot++] = ((uint64_t)v << 32) | bits;
                     }
                 }
                 count = total;
