@@ -48,10 +48,10 @@ __global__ __launch_bounds__(kST, 1) void topb_kernel(const float* __restrict__ 
                                                      int32_t* __restrict__ order, float* __restrict__ sorted_surv,
                                                      int32_t* __restrict__ rank) {
     __shared__ SchedShared<kST> sh;
-    const int n = R * K, n_pad = pad_slots<kST>(n);
-    surv_global_to_lds<kST>(sh, surv, n, n_pad);
-    sort_slots<kST>(sh, n_pad);
-    write_ranking<kST>(sh, n, order, sorted_surv, rank);
+    const int n = R * K;
+    surv_global_to_lds<kST>(sh, surv, n);
+    const uint64_t* rk = merge_sort_slots<kST>(sh, n, 1);  // the survivals may come in any order
+    write_ranking<kST>(rk, n, order, sorted_surv, rank);
 }
 
 __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict__ sorted_surv, int n, int n_sampling,
@@ -61,18 +61,14 @@ __global__ __launch_bounds__(kST, 1) void budget_kernel(const float* __restrict_
                                                        double* __restrict__ obj, uint32_t* status) {
     __shared__ SchedShared<kST> sh;
     const int n_pad = pad_slots<kST>(n);
-    CostPrefetch<kST> cp;
+    CostPrefetch cp;
     prefetch_costs<kST>(cp, vc, dc, T, num_reqs, bmax, n_pad);
-    for (int j = threadIdx.x; j < n_pad; j += kST) {
-        uint32_t key = kOne;  // value 0 for pads (never summed: j >= n)
-        if (j < n) {
-            bool bad = false;
-            key = kOne - __float_as_uint(sanitize_conf(sorted_surv[j], bad));
-        }
-        sh.key[j] = key;
+    for (int j = threadIdx.x; j < n; j += kST) {
+        bool bad = false;
+        sh.item[j] = slot_word(kOne - __float_as_uint(sanitize_conf(sorted_surv[j], bad)), 0);
     }
     __syncthreads();
-    choose_budget_lds<kST>(sh, cp, n, n_pad, n_sampling, bmax, rule, b_star, best_obj, obj, status);
+    choose_budget_lds<kST>(sh, sh.item, cp, vc + T, n, n_pad, n_sampling, bmax, rule, b_star, best_obj, obj, status);
 }
 
 __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restrict__ order,

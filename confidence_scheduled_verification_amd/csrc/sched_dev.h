@@ -9,12 +9,15 @@
 //                 Inference", section "Verify smarter")
 //   allocation    per-request prefix lengths, offsets and the compacted slot list
 //
-//   * Ranking is a stable LSD radix sort of 32-bit keys (0x3F800000 - bits(s):
-//     non-negative floats order like their bit patterns) over slots laid out in
-//     flat-id order, so equal survivals keep (request, position) order.  Each
-//     8-bit pass ranks a wave's 64 items per round by wavefront ballots (match of
-//     the digit bits), keeps per-wave digit counters in LDS, and scatters through
-//     one block-wide scan of the 256 x waves counters.
+//   * Ranking sorts one 64-bit word per slot, (0x3F800000 - bits(s)) << 16 | flat id:
+//     non-negative floats order like their bit patterns, so ascending words are
+//     (s descending, request ascending, position ascending) and every word is
+//     distinct.  The sort is a bottom-up merge over runs that are adjacent in flat
+//     order: each level moves a slot to its own index in its run plus the number of
+//     smaller words in the partner run (a binary search in LDS), so a level is one
+//     parallel step with no counters or scans.  A request's survivals never rise
+//     along its positions (each factor is at most 1 and rounding is monotone), so
+//     the first runs are whole requests and R requests take ceil(log2 R) levels.
 //   * S_B is summed EXACTLY: each float32 survival is an integer multiple of
 //     2^-149, held as a 192-bit integer, scanned in any order with the same
 //     result; N + S_B is rounded to double once (round to nearest even) and the
@@ -32,7 +35,6 @@ namespace {
 
 constexpr int kMaxN = 16384;           // slots
 constexpr uint32_t kOne = 0x3F800000u; // bits of 1.0f
-constexpr uint32_t kPadKey = 0xFFFFFFFFu;
 constexpr int kRuleArgmax = 0;
 constexpr int kRuleFirstDrop = 1;
 
@@ -41,14 +43,20 @@ struct U192 {
 };
 
 __device__ __forceinline__ U192 add192(U192 x, U192 y) {
+    unsigned long long c0, c1, c2;
     U192 r;
-    r.a = x.a + y.a;
-    const uint64_t c0 = r.a < x.a;
-    const uint64_t t = x.b + y.b;
-    uint64_t c1 = t < x.b;
-    r.b = t + c0;
-    c1 |= (r.b < t);
-    r.c = x.c + y.c + c1;
+    r.a = __builtin_addcll(x.a, y.a, 0ull, &c0);
+    r.b = __builtin_addcll(x.b, y.b, c0, &c1);
+    r.c = __builtin_addcll(x.c, y.c, c1, &c2);
+    return r;
+}
+
+__device__ __forceinline__ U192 sub192(U192 x, U192 y) {
+    unsigned long long b0, b1, b2;
+    U192 r;
+    r.a = __builtin_subcll(x.a, y.a, 0ull, &b0);
+    r.b = __builtin_subcll(x.b, y.b, b0, &b1);
+    r.c = __builtin_subcll(x.c, y.c, b1, &b2);
     return r;
 }
 
@@ -71,92 +79,131 @@ __device__ __forceinline__ U192 fixed_from_bits(uint32_t bits) {
     return r;
 }
 
-__device__ __forceinline__ bool bit192(const U192& x, int i) {
-    const uint64_t w = i < 64 ? x.a : (i < 128 ? x.b : x.c);
-    return (w >> (i & 63)) & 1ull;
-}
-
-// Any bit strictly below position i (0 <= i <= 191)?
-__device__ __forceinline__ bool any_below192(const U192& x, int i) {
-    if (i <= 0) return false;
-    if (i < 64) return (x.a & ((1ull << i) - 1ull)) != 0ull;
-    if (x.a) return true;
-    if (i == 64) return false;
-    if (i < 128) return (x.b & ((1ull << (i - 64)) - 1ull)) != 0ull;
-    if (x.b) return true;
-    if (i == 128) return false;
-    return (x.c & ((1ull << (i - 128)) - 1ull)) != 0ull;
-}
-
-// Low 64 bits of x >> s, 1 <= s <= 191.
-__device__ __forceinline__ uint64_t shr192_lo(const U192& x, int s) {
-    if (s < 64) return (x.a >> s) | (x.b << (64 - s));
-    if (s == 64) return x.b;
-    if (s < 128) return (x.b >> (s - 64)) | (x.c << (128 - s));
-    if (s == 128) return x.c;
-    return x.c >> (s - 128);
-}
-
-// x * 2^-149 rounded to the nearest double, ties to even.
+// x * 2^-149 rounded to the nearest double, ties to even: the 64 bits from x's leading
+// one down, with every lower bit ORed into their last bit (that bit lies below the
+// rounding position of a 53-bit significand, so it only breaks ties the way the exact
+// value does), converted once.
 __device__ __forceinline__ double fixed_to_double(const U192& x) {
-    int p;
-    if (x.c) p = 128 + 63 - __clzll(x.c);
-    else if (x.b) p = 64 + 63 - __clzll(x.b);
-    else if (x.a) p = 63 - __clzll(x.a);
-    else return 0.0;
-    if (p <= 52) return ldexp((double)x.a, -149);
-    int sh = p - 52;
-    uint64_t mant = shr192_lo(x, sh);
-    const bool guard = bit192(x, sh - 1);
-    const bool sticky = any_below192(x, sh - 1);
-    if (guard && (sticky || (mant & 1ull))) {
-        mant += 1ull;
-        if (mant == (1ull << 53)) {
-            mant >>= 1;
-            sh += 1;
-        }
-    }
-    return ldexp((double)mant, sh - 149);
+    const bool c_nz = x.c != 0ull, b_nz = x.b != 0ull;
+    const uint64_t h = c_nz ? x.c : (b_nz ? x.b : x.a);      // limb of the leading one
+    const uint64_t m = c_nz ? x.b : (b_nz ? x.a : 0ull);     // the limb below it
+    const bool low = c_nz && x.a != 0ull;                    // anything further below
+    const int base = c_nz ? 128 : (b_nz ? 64 : 0);
+    if (h == 0ull) return 0.0;
+    const int z = __clzll(h);
+    const uint64_t top = z ? (h << z) | (m >> (64 - z)) : h;
+    const uint64_t rest = z ? (m << z) : m;
+    const double d = (double)(top | (uint64_t)(rest != 0ull || low));
+    return ldexp(d, base - z - 149);
 }
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
-    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-    lo = __shfl_up(lo, d, 64);
-    hi = __shfl_up(hi, d, 64);
-    return ((uint64_t)hi << 32) | lo;
+// Wavefront data movement (DPP) for the scans and reductions below: lanes whose source
+// lies outside the pattern (or rows outside row_mask) receive 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
 }
 
-__device__ __forceinline__ U192 shfl_up_192(U192 x, int d) {
-    return U192{shfl_up_u64(x.a, d), shfl_up_u64(x.b, d), shfl_up_u64(x.c, d)};
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    return ((uint64_t)dpp_u32<CTRL, ROW_MASK>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL, ROW_MASK>((uint32_t)x);
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double x, int m) {
-    return __longlong_as_double((long long)shfl_xor_u64((uint64_t)__double_as_longlong(x), m));
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ U192 dpp192(const U192& x) {
+    return U192{dpp_u64<CTRL, ROW_MASK>(x.a), dpp_u64<CTRL, ROW_MASK>(x.b), dpp_u64<CTRL, ROW_MASK>(x.c)};
 }
 
-// Digit counters are stored digit-major with a stride of (waves + 1) words, so that
-// both the per-wave ranking (one digit per lane) and the block scan (consecutive
-// (digit, wave) entries per thread) touch distinct LDS banks.
-template <int NT>
-__device__ __forceinline__ int hist_at(int d, int w) { return d * (NT / 64 + 1) + w; }
+// Inclusive wavefront scans: shifts by 1, 2, 4, 8 within each row of 16 lanes, then lane
+// 15 into row 1, lane 47 into row 3, and lane 31 into rows 2 and 3.
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+// Reductions: partner lanes at xor 1 and xor 2 within quads, then the mirrored lane of the
+// half row and of the row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += dpp_u32<kDppShr1, 0xF>(x);
+    x += dpp_u32<kDppShr2, 0xF>(x);
+    x += dpp_u32<kDppShr4, 0xF>(x);
+    x += dpp_u32<kDppShr8, 0xF>(x);
+    x += dpp_u32<kDppBcast15, 0xA>(x);
+    x += dpp_u32<kDppBcast31, 0xC>(x);
+    return x;
+}
+
+__device__ __forceinline__ U192 wave_incl_scan192(U192 x) {
+    x = add192(x, dpp192<kDppShr1, 0xF>(x));
+    x = add192(x, dpp192<kDppShr2, 0xF>(x));
+    x = add192(x, dpp192<kDppShr4, 0xF>(x));
+    x = add192(x, dpp192<kDppShr8, 0xF>(x));
+    x = add192(x, dpp192<kDppBcast15, 0xA>(x));
+    x = add192(x, dpp192<kDppBcast31, 0xC>(x));
+    return x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_max_step_f64(double v) {
+    const double w = __longlong_as_double((long long)dpp_u64<CTRL, 0xF>((uint64_t)__double_as_longlong(v)));
+    return w > v ? w : v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Wavefront maximum of a double (no NaN) and minimum of an int, the same in every lane.
+// The patterns have no lane outside them, so the 0 fill never enters.
+__device__ __forceinline__ double wave_max_f64(double x) {
+    x = dpp_max_step_f64<kDppXor1>(x);
+    x = dpp_max_step_f64<kDppXor2>(x);
+    x = dpp_max_step_f64<kDppHalfMirror>(x);
+    x = dpp_max_step_f64<kDppMirror>(x);
+    const double a = readlane_f64(x, 0), b = readlane_f64(x, 16), c = readlane_f64(x, 32), d = readlane_f64(x, 48);
+    const double ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_min_step_i32(int v) {
+    const int w = (int)dpp_u32<CTRL, 0xF>((uint32_t)v);
+    return w < v ? w : v;
+}
+
+__device__ __forceinline__ int wave_min_i32(int x) {
+    x = dpp_min_step_i32<kDppXor1>(x);
+    x = dpp_min_step_i32<kDppXor2>(x);
+    x = dpp_min_step_i32<kDppHalfMirror>(x);
+    x = dpp_min_step_i32<kDppMirror>(x);
+    const int a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const int c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    return min(min(a, b), min(c, d));
+}
 
 // LDS of the scheduling workgroup (NT threads).
 template <int NT>
 struct SchedShared {
     static constexpr int SW = NT / 64;
-    uint32_t key[kMaxN];                 // sort keys; after sorting: keys in rank order
-    uint16_t id[kMaxN];                  // flat slot ids travelling with the keys
-    uint32_t hist[256 * (SW + 1)];       // per-(digit, wave) counters / offsets
+    // slot words (see slot_word); with n <= kMaxN / 2 the two halves are the merge's
+    // source and destination in turn, above that it merges in place
+    uint64_t item[kMaxN];
     // per-thread partial sums; reused as the selection map (one byte per slot)
     static constexpr int kPart = NT > (kMaxN + 23) / 24 ? NT : (kMaxN + 23) / 24;
     U192 part[kPart];
     uint32_t wsum[SW];
     U192 wsum192[SW];
-    double wbest_f[SW];
-    double wbest_v[SW];
-    int32_t wbest_b[SW];
+    double wbest_f[SW];   // per wave: largest objective, the smallest B that reaches it, and
+    int32_t wbest_b[SW];  // the smallest first-drop candidate
+    int32_t wdrop[SW];
     int32_t b_star;
 };
+
+__device__ __forceinline__ uint64_t slot_word(uint32_t key, int f) { return ((uint64_t)key << 16) | (uint32_t)f; }
+__device__ __forceinline__ uint32_t word_key(uint64_t x) { return (uint32_t)(x >> 16); }
+__device__ __forceinline__ int word_slot(uint64_t x) { return (int)(x & 0xFFFFull); }
 
 // Exclusive scan of one uint32 per thread over the block.  TRAIL: end with a barrier so
 // that the next call may reuse sh.wsum at once (callers with barriers of their own in
@@ -164,12 +211,7 @@ struct SchedShared {
 template <int NT, bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_scan(SchedShared<NT>& sh, uint32_t v, uint32_t* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan_u32(v);
     if (lane == 63) sh.wsum[w] = x;
     __syncthreads();
     uint32_t off = 0, tot = 0;
@@ -183,36 +225,17 @@ __device__ __forceinline__ uint32_t block_excl_scan(SchedShared<NT>& sh, uint32_
     return off + x - v;
 }
 
-// Exclusive scan of one 192-bit integer per thread.
+// Exclusive scan of one 192-bit integer per thread.  sh.wsum192 may be written again
+// once every thread has passed a later barrier.
 template <int NT>
 __device__ __forceinline__ U192 block_excl_scan192(SchedShared<NT>& sh, U192 v) {
-    constexpr int kSW = NT / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    U192 x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const U192 y = shfl_up_192(x, o);
-        if (lane >= o) x = add192(x, y);
-    }
-    U192 excl = shfl_up_192(x, 1);
-    if (lane == 0) excl = U192{0ull, 0ull, 0ull};
+    const U192 x = wave_incl_scan192(v);
     if (lane == 63) sh.wsum192[w] = x;
     __syncthreads();
-    if (w == 0) {  // exclusive scan of the wave totals, in the first lanes of wave 0
-        U192 t = lane < kSW ? sh.wsum192[lane] : U192{0ull, 0ull, 0ull};
-#pragma unroll
-        for (int o = 1; o < kSW; o <<= 1) {
-            const U192 y = shfl_up_192(t, o);
-            if (lane >= o) t = add192(t, y);
-        }
-        U192 te = shfl_up_192(t, 1);
-        if (lane == 0) te = U192{0ull, 0ull, 0ull};
-        if (lane < kSW) sh.part[lane] = te;
-    }
-    __syncthreads();
-    const U192 off = sh.part[w];
-    __syncthreads();
-    return add192(off, excl);
+    U192 off = {0ull, 0ull, 0ull};
+    for (int q = 0; q < w; ++q) off = add192(off, sh.wsum192[q]);
+    return sub192(add192(off, x), v);
 }
 
 template <int NT>
@@ -233,27 +256,30 @@ __device__ __forceinline__ float sanitize_conf(float c, bool& bad) {
     return c == 0.f ? 0.f : c;  // -0 -> +0
 }
 
-// Stage 2 for all requests; keys/ids in flat order, pads after n.  The confidences
-// are first read coalesced into LDS (one memory round trip for the whole block),
-// then each thread runs the sequential product of its request from LDS.
+// Stage 2 for all requests; slot words in flat order.  Each thread runs the sequential
+// product of its request, its confidences requested eight at a time (one memory round
+// trip for up to eight positions).
 template <int NT>
-__device__ __forceinline__ void survival_to_lds(SchedShared<NT>& sh, const float* __restrict__ conf, int R, int K, int n_pad,
+__device__ __forceinline__ void survival_to_lds(SchedShared<NT>& sh, const float* __restrict__ conf, int R, int K,
                                                 float* __restrict__ surv_out, uint32_t* status) {
-    const int n = R * K;
-    for (int f = threadIdx.x; f < n_pad; f += NT) {
-        sh.key[f] = f < n ? __float_as_uint(conf[f]) : kPadKey;
-        sh.id[f] = (uint16_t)f;
-    }
-    __syncthreads();
     bool bad = false;
     for (int r = threadIdx.x; r < R; r += NT) {
+        const int f0 = r * K;
         float s = 0.f;
-        for (int i = 0; i < K; ++i) {
-            const int f = r * K + i;
-            const float c = sanitize_conf(__uint_as_float(sh.key[f]), bad);
-            s = (i == 0) ? c : s * c;
-            sh.key[f] = kOne - __float_as_uint(s);
-            if (surv_out) surv_out[f] = s;
+        for (int i0 = 0; i0 < K; i0 += 8) {
+            float c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = i0 + u < K ? conf[f0 + i0 + u] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u;
+                if (i < K) {
+                    const float cu = sanitize_conf(c[u], bad);
+                    s = (i == 0) ? cu : s * cu;
+                    sh.item[f0 + i] = slot_word(kOne - __float_as_uint(s), f0 + i);
+                    if (surv_out) surv_out[f0 + i] = s;
+                }
+            }
         }
     }
     if (bad) raise_status(status, kStatusConfSanitized);
@@ -262,150 +288,196 @@ __device__ __forceinline__ void survival_to_lds(SchedShared<NT>& sh, const float
 
 // Survivals given in global memory (topb-only entry point); values outside [0,1] are clamped.
 template <int NT>
-__device__ __forceinline__ void surv_global_to_lds(SchedShared<NT>& sh, const float* __restrict__ surv, int n, int n_pad) {
-    for (int f = threadIdx.x; f < n_pad; f += NT) {
-        if (f < n) {
-            bool bad = false;
-            const float s = sanitize_conf(surv[f], bad);
-            sh.key[f] = kOne - __float_as_uint(s);
-        } else {
-            sh.key[f] = kPadKey;
-        }
-        sh.id[f] = (uint16_t)f;
+__device__ __forceinline__ void surv_global_to_lds(SchedShared<NT>& sh, const float* __restrict__ surv, int n) {
+    for (int f = threadIdx.x; f < n; f += NT) {
+        bool bad = false;
+        const float s = sanitize_conf(surv[f], bad);
+        sh.item[f] = slot_word(kOne - __float_as_uint(s), f);
     }
     __syncthreads();
 }
 
-// One stable counting pass over the 8-bit digit at `shift`.  Wave w owns items
-// [w*S, (w+1)*S) of the current order, 64 per round; an item's rank among equal
-// digits of its wave comes from a ballot match of the digit bits and a running
-// per-(digit, wave) counter.  Entered after a barrier that follows the last writes of
-// the keys (the previous pass's scatter, or the survival stage).  A wave's counter
-// column is written and read by that wave alone until the barrier before the offset
-// scan, so clearing it needs no barrier of its own; the scan's scratch is not written
-// again before this pass's later barriers, so it needs no trailing one either.
-template <int NT>
-__device__ __forceinline__ void radix_pass(SchedShared<NT>& sh, int n_pad, int shift) {
-    constexpr int kSW = NT / 64, JM = kMaxN / NT;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int S = n_pad / kSW;  // items per wave, a multiple of 64
-    const int J = S / 64;       // rounds, <= JM
-    uint32_t k[JM];
-    uint32_t il[JM];  // flat id (low 16 bits) and rank among equal digits of the wave (high 16 bits)
-    for (int d = lane; d < 256; d += 64) sh.hist[hist_at<NT>(d, w)] = 0u;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        if (j < J) {
-            const int p = w * S + j * 64 + lane;
-            k[j] = sh.key[p];
-            il[j] = sh.id[p];
+// One merge level for the word at index p of src (see merge_sort_slots), W = run0 << lvl:
+// its partner run [plo, plo + len) and where it goes when c words of that run are below
+// it (base + c).  With no partner run, len = 0 and plo = 1 (reads stay at src[0]).
+struct MergeSlot {
+    int plo, len, base;
+};
+
+__device__ __forceinline__ MergeSlot merge_slot(int n, int p, int run0, float inv_run0, int lvl, int W) {
+    // p / run0, exact for p < 2^24 after the correction
+    int q = (int)((float)p * inv_run0);
+    if (q * run0 > p) --q;
+    else if ((q + 1) * run0 <= p) ++q;
+    const int j = q >> lvl;
+    const int own = j * W;
+    MergeSlot m;
+    if (j & 1) {
+        m.plo = own - W;
+        m.len = W;
+        m.base = p - W;  // (own - W) + (p - own)
+    } else {
+        m.plo = own + W;
+        m.len = (own + 2 * W < n ? own + 2 * W : n) - m.plo;
+        m.base = p;
+        if (m.len <= 0) {
+            m.plo = 1;
+            m.len = 0;
         }
     }
-    const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        if (j < J) {
-            const uint32_t d = (k[j] >> shift) & 0xFFu;
-            uint64_t peers = ~0ull;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bool on = (d >> b) & 1u;
-                const uint64_t m = __ballot(on);
-                peers &= on ? m : ~m;
-            }
-            const uint32_t before = (uint32_t)__popcll(peers & lt);
-            const uint32_t h = sh.hist[hist_at<NT>(d, w)];
-            il[j] |= (h + before) << 16;
-            if (before == 0u) sh.hist[hist_at<NT>(d, w)] = h + (uint32_t)__popcll(peers);
-        }
-    }
-    __syncthreads();
-    // Offsets in (digit, wave) order: entries e = 4*tid .. 4*tid+3 (256 digits x kSW
-    // waves = 4 per thread), digit e / kSW, wave e % kSW.
-    uint32_t c[4], s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = 4 * tid + q;
-        c[q] = sh.hist[hist_at<NT>(e / kSW, e % kSW)];
-        s += c[q];
-    }
-    uint32_t ex = block_excl_scan<NT, false>(sh, s, nullptr);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = 4 * tid + q;
-        sh.hist[hist_at<NT>(e / kSW, e % kSW)] = ex;
-        ex += c[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        if (j < J) {
-            const uint32_t d = (k[j] >> shift) & 0xFFu;
-            const uint32_t dest = sh.hist[hist_at<NT>(d, w)] + (il[j] >> 16);
-            sh.key[dest] = k[j];
-            sh.id[dest] = (uint16_t)(il[j] & 0xFFFFu);
-        }
-    }
-    __syncthreads();
+    return m;
 }
 
-template <int NT>
-__device__ __forceinline__ void sort_slots(SchedShared<NT>& sh, int n_pad) {
+// Binary search step t (>= 1) reads the partner run's word t - 1, or its last word when
+// t > len: the test "word < v" then answers as it does at t = len, so the predicate stays
+// monotone in t and the count found, clamped to len at the end, is exact.  Every read is
+// in [0, n).
+__device__ __forceinline__ int merge_probe(const MergeSlot& m, int t) { return m.plo + (t < m.len ? t : m.len) - 1; }
+
+// Where the word v at index p of src goes: words of the partner run below v counted by
+// a binary search of top, top / 2, ..., 1 (top: the largest power of two <= W, so the
+// steps reach any count up to W).
+__device__ __forceinline__ int merge_dest(const uint64_t* src, int n, int p, uint64_t v, int run0, float inv_run0,
+                                          int lvl, int W, int top) {
+    const MergeSlot m = merge_slot(n, p, run0, inv_run0, lvl, W);
+    int c = 0;
 #pragma unroll 1
-    for (int shift = 0; shift < 32; shift += 8) radix_pass<NT>(sh, n_pad, shift);
+    for (int st = top; st > 0; st >>= 1) {
+        const int t = c + st;
+        c = src[merge_probe(m, t)] < v ? t : c;
+    }
+    return m.base + (c < m.len ? c : m.len);
+}
+
+// The same for two words at once (indices p0 and p1 of src), their searches interleaved
+// so that each step's two LDS reads are in flight together.
+__device__ __forceinline__ void merge_dest2(const uint64_t* src, int n, int p0, uint64_t v0, int p1, uint64_t v1,
+                                            int run0, float inv_run0, int lvl, int W, int top, int& d0, int& d1) {
+    const MergeSlot m0 = merge_slot(n, p0, run0, inv_run0, lvl, W);
+    const MergeSlot m1 = merge_slot(n, p1, run0, inv_run0, lvl, W);
+    int c0 = 0, c1 = 0;
+#pragma unroll 1
+    for (int st = top; st > 0; st >>= 1) {
+        const int t0 = c0 + st, t1 = c1 + st;
+        const uint64_t x0 = src[merge_probe(m0, t0)];
+        const uint64_t x1 = src[merge_probe(m1, t1)];
+        c0 = x0 < v0 ? t0 : c0;
+        c1 = x1 < v1 ? t1 : c1;
+    }
+    d0 = m0.base + (c0 < m0.len ? c0 : m0.len);
+    d1 = m1.base + (c1 < m1.len ? c1 : m1.len);
+}
+
+// Sorts the n slot words in sh.item, whose runs [j*run0, (j+1)*run0) are each ascending
+// already (run0 = 1 for arbitrary words); returns where the sorted words are (sh.item or
+// its upper half).  Entered after a barrier that follows the last writes of the words.
+// Level l merges run pairs of width W = run0 << l: the word at index p of run j moves to
+// (start of the pair) + (p - j W) + (number of words of the partner run below it), so
+// runs that are adjacent in flat order stay adjacent and no two words share a place.
+template <int NT>
+__device__ __forceinline__ const uint64_t* merge_sort_slots(SchedShared<NT>& sh, int n, int run0) {
+    constexpr int JM = kMaxN / NT;
+    const int tid = threadIdx.x;
+    const bool pp = n <= kMaxN / 2;
+    uint64_t* src = sh.item;
+    uint64_t* dst = pp ? sh.item + kMaxN / 2 : sh.item;
+    const float inv_run0 = 1.0f / (float)run0;
+    int top = 1;
+    while (2 * top <= run0) top *= 2;
+    int lvl = 0;
+#pragma unroll 1
+    for (int W = run0; W < n; W *= 2, top *= 2, ++lvl) {
+        if (pp) {  // source and destination apart: each word moves as soon as its place is known
+#pragma unroll 1
+            for (int p0 = tid; p0 < n; p0 += 2 * NT) {
+                const int p1 = p0 + NT < n ? p0 + NT : p0;  // a lone word is searched twice
+                const uint64_t v0 = src[p0], v1 = src[p1];
+                int d0, d1;
+                merge_dest2(src, n, p0, v0, p1, v1, run0, inv_run0, lvl, W, top, d0, d1);
+                dst[d0] = v0;
+                dst[d1] = v1;
+            }
+            __syncthreads();
+            uint64_t* t = src;
+            src = dst;
+            dst = t;
+        } else {  // in place: every word of the level is read before any moves
+            int dest[JM];
+#pragma unroll
+            for (int k = 0; k < JM; ++k) {
+                const int p = tid + k * NT;
+                dest[k] = p < n ? merge_dest(src, n, p, src[p], run0, inv_run0, lvl, W, top) : -1;
+            }
+            uint64_t v[JM];
+#pragma unroll
+            for (int k = 0; k < JM; ++k) v[k] = dest[k] >= 0 ? src[tid + k * NT] : 0ull;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < JM; ++k)
+                if (dest[k] >= 0) src[dest[k]] = v[k];
+            __syncthreads();
+        }
+    }
+    return src;
 }
 
 template <int NT>
-__device__ __forceinline__ void write_ranking(const SchedShared<NT>& sh, int n, int32_t* __restrict__ order,
-                              float* __restrict__ sorted_surv, int32_t* __restrict__ rank) {
+__device__ __forceinline__ void write_ranking(const uint64_t* rk, int n, int32_t* __restrict__ order,
+                                              float* __restrict__ sorted_surv, int32_t* __restrict__ rank) {
     for (int j = threadIdx.x; j < n; j += NT) {
-        const int f = sh.id[j];
+        const uint64_t x = rk[j];
+        const int f = word_slot(x);
         if (order) order[j] = f;
-        if (sorted_surv) sorted_surv[j] = __uint_as_float(kOne - sh.key[j]);
+        if (sorted_surv) sorted_surv[j] = __uint_as_float(kOne - word_key(x));
         if (rank) rank[f] = j;
     }
 }
 
-// The cost-table entries one thread evaluates in stage 4 (B = tid*C + q, and
-// B = tid*C + C, the next thread's first candidate, which the first-drop rule compares
-// against and which is n_pad for the last thread), read at the start of the kernel so
-// that their memory latency overlaps the earlier stages.
-template <int NT>
+// The cost-table entries of the first kCostPre candidates one thread evaluates in stage
+// 4 (B = tid*C + q), of B = tid*C + C (the next thread's first candidate, which the
+// first-drop rule compares against, n_pad for the last thread) and the draft cost, read
+// at the start of the kernel so that their memory latency overlaps the earlier stages.
+// With more than kCostPre * NT slots the later candidates read theirs in stage 4.
+constexpr int kCostPre = 2;
 struct CostPrefetch {
-    float vc[kMaxN / NT];
+    float vc[kCostPre];
     float vc_next;
     float dc;
 };
 
 template <int NT>
-__device__ __forceinline__ void prefetch_costs(CostPrefetch<NT>& cp, const float* __restrict__ vc,
+__device__ __forceinline__ void prefetch_costs(CostPrefetch& cp, const float* __restrict__ vc,
                                                const float* __restrict__ dc, int T, int num_reqs, int bmax,
                                                int n_pad) {
     const int C = n_pad / NT;
     const int j0 = threadIdx.x * C;
 #pragma unroll
-    for (int q = 0; q < kMaxN / NT; ++q) cp.vc[q] = (q < C && j0 + q <= bmax) ? vc[T + j0 + q] : 0.f;
+    for (int q = 0; q < kCostPre; ++q) cp.vc[q] = (q < C && j0 + q <= bmax) ? vc[T + j0 + q] : 0.f;
     cp.vc_next = (j0 + C <= bmax) ? vc[T + j0 + C] : 0.f;
     cp.dc = dc[num_reqs];
 }
 
-// Stage 4 over the keys in sh.key (rank order).  Leaves the budget in sh.b_star.
-// rule kRuleArgmax: the smallest B with the largest f.  rule kRuleFirstDrop: the first
-// B whose successor does not raise f (f(B+1) <= f(B)), else bmax.  Every f(B) is the
-// same double in both rules, so where f rises to a single peak they agree.
+// Stage 4 over the slot words rk (rank order); returns the budget (the same in every
+// thread) and writes b_star and best_obj.  rule kRuleArgmax: the smallest B with the
+// largest f.  rule kRuleFirstDrop: the first B whose successor does not raise f
+// (f(B+1) <= f(B)), else bmax.  Every f(B) is the same double in both rules, so where f
+// rises to a single peak they agree.  vcT is the verify-cost table from B = 0 (its
+// entries beyond the prefetched ones are read here).
 template <int NT>
-__device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const CostPrefetch<NT>& cp, int n, int n_pad,
-                                                  int n_sampling, int bmax, int rule, int32_t* __restrict__ b_star,
-                                                  double* __restrict__ best_obj, double* __restrict__ obj,
-                                                  uint32_t* status) {
+__device__ __forceinline__ int choose_budget_lds(SchedShared<NT>& sh, const uint64_t* rk, const CostPrefetch& cp,
+                                                 const float* __restrict__ vcT, int n, int n_pad, int n_sampling,
+                                                 int bmax, int rule, int32_t* __restrict__ b_star,
+                                                 double* __restrict__ best_obj, double* __restrict__ obj,
+                                                 uint32_t* status) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    constexpr int kSW = NT / 64;
+    constexpr int kSW = NT / 64, QM = kMaxN / NT;
+    constexpr int kNone = 0x7FFFFFFF;
     const int C = n_pad / NT;
     const int j0 = tid * C;
     U192 local = {0ull, 0ull, 0ull};
     for (int q = 0; q < C; ++q) {
         const int j = j0 + q;
-        if (j < n) local = add192(local, fixed_from_bits(kOne - sh.key[j]));
+        if (j < n) local = add192(local, fixed_from_bits(kOne - word_key(rk[j])));
     }
     U192 S = block_excl_scan192<NT>(sh, local);
     const double dcost = (double)cp.dc;
@@ -421,9 +493,9 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const Cos
         return -INFINITY;
     };
     double bf = -INFINITY;   // argmax candidate of this thread: f and B
-    int bb = 0x7FFFFFFF;
+    int bb = kNone;
     double fprev = 0.0;      // f(B-1) of the previous candidate of this thread
-    int drop = 0x7FFFFFFF;   // first-drop candidate: B with f(B+1) <= f(B), and f(B)
+    int drop = kNone;        // first-drop candidate: B with f(B+1) <= f(B), and f(B)
     double fdrop = 0.0;
     auto take = [&](int B, double f, bool own) {
         if (own) {
@@ -432,7 +504,7 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const Cos
                 bf = f;
                 bb = B;
             }
-            if (B == bmax && drop == 0x7FFFFFFF) {  // no drop before bmax: admission ends there
+            if (B == bmax && drop == kNone) {  // no drop before bmax: admission ends there
                 drop = B;
                 fdrop = f;
             }
@@ -444,58 +516,50 @@ __device__ __forceinline__ void choose_budget_lds(SchedShared<NT>& sh, const Cos
         fprev = f;
     };
 #pragma unroll
-    for (int q = 0; q < kMaxN / NT; ++q) {
+    for (int q = 0; q < QM; ++q) {
         if (q < C) {
             const int B = j0 + q;
-            if (B <= bmax) take(B, eval(cp.vc[q]), true);
-            if (B < n) S = add192(S, fixed_from_bits(kOne - sh.key[B]));
+            if (B <= bmax) take(B, eval(q < kCostPre ? cp.vc[q < kCostPre ? q : 0] : vcT[B]), true);
+            if (B < n) S = add192(S, fixed_from_bits(kOne - word_key(rk[B])));
         }
     }
     // B = j0 + C: the next thread's first candidate (compared against f(j0 + C - 1)), or
     // B = n_pad for the last thread.
     if (j0 + C <= bmax) take(j0 + C, eval(cp.vc_next), tid == NT - 1);
     if (bad) raise_status(status, kStatusCostInvalid);
-    // Block reduction: argmax takes the larger f, then the smaller B; first drop takes
-    // the smaller B.  (kf, kb) is the key, vf the objective carried along.
-    double kf = bf, vf = bf;
-    int kb = bb;
-    if (rule == kRuleFirstDrop) {
-        kf = drop == 0x7FFFFFFF ? -INFINITY : 0.0;
-        kb = drop;
-        vf = fdrop;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const double of = shfl_xor_f64(kf, m);
-        const double ov = shfl_xor_f64(vf, m);
-        const int ob = __shfl_xor(kb, m, 64);
-        if (of > kf || (of == kf && ob < kb)) {
-            kf = of;
-            kb = ob;
-            vf = ov;
-        }
-    }
+    // Per wave: the largest f and the smallest B reaching it, and the smallest drop; then
+    // every thread combines the waves' (a drop, once found, belongs to one thread only).
+    const double fw = wave_max_f64(bf);
+    const int bw = wave_min_i32(bf == fw ? bb : kNone);
+    const int dw = wave_min_i32(drop);
     if (lane == 0) {
-        sh.wbest_f[w] = kf;
-        sh.wbest_v[w] = vf;
-        sh.wbest_b[w] = kb;
+        sh.wbest_f[w] = fw;
+        sh.wbest_b[w] = bw;
+        sh.wdrop[w] = dw;
     }
     __syncthreads();
-    if (tid == 0) {
-        double f = sh.wbest_f[0], v = sh.wbest_v[0];
-        int b = sh.wbest_b[0];
-        for (int q = 1; q < kSW; ++q) {
-            if (sh.wbest_f[q] > f || (sh.wbest_f[q] == f && sh.wbest_b[q] < b)) {
-                f = sh.wbest_f[q];
-                v = sh.wbest_v[q];
-                b = sh.wbest_b[q];
-            }
+    double F = sh.wbest_f[0];
+    int Bx = sh.wbest_b[0], D = sh.wdrop[0];
+    for (int q = 1; q < kSW; ++q) {
+        const double f = sh.wbest_f[q];
+        const int b = sh.wbest_b[q];
+        if (f > F || (f == F && b < Bx)) {
+            F = f;
+            Bx = b;
         }
-        sh.b_star = b;
-        if (b_star) *b_star = b;
-        if (best_obj) *best_obj = v;
+        D = min(D, sh.wdrop[q]);
     }
-    __syncthreads();
+    const int B = rule == kRuleFirstDrop ? D : Bx;
+    if (tid == 0 && b_star) *b_star = B;
+    if (best_obj) {
+        if (rule == kRuleFirstDrop) {
+            if (drop == D) *best_obj = fdrop;
+        } else if (tid == 0) {
+            *best_obj = F;
+        }
+    }
+    __syncthreads();  // sh.wbest_* and sh.wdrop are read before they are written again
+    return B;
 }
 
 // Stage 5.  sel must already mark the chosen slots (1 byte per flat id, n entries).
@@ -568,7 +632,7 @@ struct Sizing {
 // Stages 2-5 in sequence: survival (optionally written out), ranking (written out),
 // budget, selection and allocation.  Leaves B* in sh.b_star and the selection map in
 // LDS; every output pointer except the required ones may be null.  lds_rows (may be
-// null, may alias sh.key, which is free by then): each request's offset and prefix
+// null, may alias sh.item, which is free by then): each request's offset and prefix
 // length (see allocate_lds).  tokens and ver_tokens (may be null): the draft tokens and
 // the verified-token output of allocate_lds.
 // With a separate sizing array, B is chosen from its survivals first (same survival,
@@ -591,6 +655,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     // the current slots; otherwise one pass does both.
     const int passes = sz.separate ? 2 : 1;
     int B = 0;
+    const uint64_t* rk = sh.item;
 #pragma unroll 1
     for (int ps = 0; ps < passes; ++ps) {
         const bool sizing = ps == 0, last = ps == passes - 1;
@@ -598,34 +663,27 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
         const int rows = sz.separate && sizing ? sz.R : R;
         const int m = rows * K, m_pad = pad_slots<NT>(m);
         const int bm = sz.separate ? sz.bmax : bmax;
-        // The cost-table entries are requested before the ranking where the registers
-        // allow (up to 512 threads), so their memory round trip overlaps the confidences'
-        // and the sort; with more threads, after the sort (overlapping the write-out and
-        // the exact scan).
-        constexpr bool kEarly = NT <= 512;
-        CostPrefetch<NT> cp;
-        if (kEarly && sizing) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
-        survival_to_lds<NT>(sh, src, rows, K, m_pad, last ? surv_out : nullptr, status);
-        sort_slots<NT>(sh, m_pad);
+        // the cost-table entries are requested before the confidences, so that both
+        // memory round trips overlap (and the sort)
+        CostPrefetch cp;
+        if (sizing) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
+        survival_to_lds<NT>(sh, src, rows, K, last ? surv_out : nullptr, status);
+        rk = merge_sort_slots<NT>(sh, m, K);  // each request's row is a sorted run
         if (sizing) {
-            if (!kEarly) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
-            if (last) write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
-            choose_budget_lds<NT>(sh, cp, m, m_pad, n_sampling, bm, sz.rule, last ? b_star : nullptr, best_obj,
-                                  nullptr, status);
-            B = sh.b_star;  // every thread reads it before the next barrier
+            if (last) write_ranking<NT>(rk, n, order, sorted_surv, nullptr);
+            B = choose_budget_lds<NT>(sh, rk, cp, vc + T, m, m_pad, n_sampling, bm, sz.rule, last ? b_star : nullptr,
+                                      best_obj, nullptr, status);
         } else {
-            write_ranking<NT>(sh, n, order, sorted_surv, nullptr);
+            write_ranking<NT>(rk, n, order, sorted_surv, nullptr);
         }
     }
     if (sz.separate) {
         B = B < n ? B : n;
-        if (threadIdx.x == 0) {
-            sh.b_star = B;
-            if (b_star) *b_star = B;
-        }
+        if (threadIdx.x == 0 && b_star) *b_star = B;
     }
+    if (threadIdx.x == 0) sh.b_star = B;
     uint8_t* sel = selection_map<NT>(sh);
-    for (int j = threadIdx.x; j < n; j += NT) sel[sh.id[j]] = (uint8_t)(j < B);
+    for (int j = threadIdx.x; j < n; j += NT) sel[word_slot(rk[j])] = (uint8_t)(j < B);
     __syncthreads();
     allocate_lds<NT>(sh, sel, R, K, B, tokens, prefix_len, offsets, ver_idx, ver_tokens, lds_rows);
 }

@@ -58,7 +58,7 @@ __device__ __forceinline__ void step_schedule_wg(const StepArgs& a, unsigned cha
     __builtin_amdgcn_s_waitcnt(0);  // every exchange has returned
     __syncthreads();
     if (threadIdx.x == 0) set_agent_u32(ready, 1u);
-    int32_t* lds_rows = reinterpret_cast<int32_t*>(sh.key);  // per request: offset, prefix length
+    int32_t* lds_rows = reinterpret_cast<int32_t*>(sh.item);  // per request: offset, prefix length
     const Sizing sz{a.sizing.separate, a.sizing.conf, a.sizing.R, a.sizing.bmax, a.sizing.rule};
     sched_pass<kNT>(sh, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs, a.vc, a.dc, a.bmax, sz, a.surv, a.order,
                     a.sorted_surv, a.b_star, a.best_obj, a.prefix_len, a.offsets, a.ver_idx, a.status, lds_rows);
