@@ -65,17 +65,13 @@ __device__ __forceinline__ U192 fixed_from_bits(uint32_t bits) {
     const uint32_t E = bits >> 23, M = bits & 0x7FFFFFu;
     const uint64_t m = E ? (uint64_t)(M | 0x800000u) : (uint64_t)M;
     const int sh = E ? (int)E - 1 : 0;  // 0 .. 126
-    U192 r = {0ull, 0ull, 0ull};
-    if (sh < 64) {
-        r.a = m << sh;
-        r.b = sh ? (m >> (64 - sh)) : 0ull;
-    } else if (sh < 128) {
-        const int s2 = sh - 64;
-        r.b = m << s2;
-        r.c = s2 ? (m >> (64 - s2)) : 0ull;
-    } else {
-        r.c = m << (sh - 128);
-    }
+    const int li = sh >> 6, off = sh & 63;  // limb and offset of m's lowest bit
+    const uint64_t lo = m << off;
+    const uint64_t hi = off ? m >> (64 - off) : 0ull;
+    U192 r;
+    r.a = li == 0 ? lo : 0ull;
+    r.b = li == 0 ? hi : (li == 1 ? lo : 0ull);
+    r.c = li == 1 ? hi : (li == 2 ? lo : 0ull);
     return r;
 }
 
@@ -258,18 +254,26 @@ __device__ __forceinline__ float sanitize_conf(float c, bool& bad) {
 
 // Stage 2 for all requests; slot words in flat order.  Each thread runs the sequential
 // product of its request, its confidences requested eight at a time (one memory round
-// trip for up to eight positions).
+// trip for up to eight positions).  tok_lds (may be null): the request's draft tokens are
+// copied there too, read in the same round trip.
 template <int NT>
 __device__ __forceinline__ void survival_to_lds(SchedShared<NT>& sh, const float* __restrict__ conf, int R, int K,
-                                                float* __restrict__ surv_out, uint32_t* status) {
+                                                float* __restrict__ surv_out, uint32_t* status,
+                                                const int32_t* __restrict__ tokens = nullptr,
+                                                int32_t* tok_lds = nullptr) {
     bool bad = false;
     for (int r = threadIdx.x; r < R; r += NT) {
         const int f0 = r * K;
         float s = 0.f;
         for (int i0 = 0; i0 < K; i0 += 8) {
             float c[8];
+            int32_t tk[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) c[u] = i0 + u < K ? conf[f0 + i0 + u] : 0.f;
+            if (tok_lds) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) tk[u] = i0 + u < K ? tokens[f0 + i0 + u] : 0;
+            }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int i = i0 + u;
@@ -278,6 +282,7 @@ __device__ __forceinline__ void survival_to_lds(SchedShared<NT>& sh, const float
                     s = (i == 0) ? cu : s * cu;
                     sh.item[f0 + i] = slot_word(kOne - __float_as_uint(s), f0 + i);
                     if (surv_out) surv_out[f0 + i] = s;
+                    if (tok_lds) tok_lds[f0 + i] = tk[u];
                 }
             }
         }
@@ -304,26 +309,25 @@ struct MergeSlot {
     int plo, len, base;
 };
 
-__device__ __forceinline__ MergeSlot merge_slot(int n, int p, int run0, float inv_run0, int lvl, int W) {
-    // p / run0, exact for p < 2^24 after the correction
-    int q = (int)((float)p * inv_run0);
-    if (q * run0 > p) --q;
-    else if ((q + 1) * run0 <= p) ++q;
+// p / run0 for p, run0 <= 2^14 with magic = ceil(2^32 / run0) (run0 > 1): the product
+// overshoots p / run0 by less than p / 2^32 <= 2^-18, while p / run0 stays at least
+// 1 / run0 >= 2^-14 below the next integer, so the floor is exact.
+__device__ __forceinline__ int run_index(int p, int run0, uint32_t magic) {
+    return run0 == 1 ? p : (int)__umulhi((uint32_t)p, magic);
+}
+
+__device__ __forceinline__ MergeSlot merge_slot(int n, int p, int q, int lvl, int W) {
     const int j = q >> lvl;
-    const int own = j * W;
+    const int own = (int)__umul24((uint32_t)j, (uint32_t)W);  // < 2^24
+    const bool odd = j & 1;
     MergeSlot m;
-    if (j & 1) {
-        m.plo = own - W;
-        m.len = W;
-        m.base = p - W;  // (own - W) + (p - own)
-    } else {
-        m.plo = own + W;
-        m.len = (own + 2 * W < n ? own + 2 * W : n) - m.plo;
-        m.base = p;
-        if (m.len <= 0) {
-            m.plo = 1;
-            m.len = 0;
-        }
+    m.plo = odd ? own - W : own + W;
+    const int end = odd ? own : min(own + 2 * W, n);
+    m.len = end - m.plo;
+    m.base = odd ? p - W : p;  // the pair's start plus p's index in its own run
+    if (m.len <= 0) {
+        m.plo = 1;
+        m.len = 0;
     }
     return m;
 }
@@ -337,9 +341,9 @@ __device__ __forceinline__ int merge_probe(const MergeSlot& m, int t) { return m
 // Where the word v at index p of src goes: words of the partner run below v counted by
 // a binary search of top, top / 2, ..., 1 (top: the largest power of two <= W, so the
 // steps reach any count up to W).
-__device__ __forceinline__ int merge_dest(const uint64_t* src, int n, int p, uint64_t v, int run0, float inv_run0,
+__device__ __forceinline__ int merge_dest(const uint64_t* src, int n, int p, uint64_t v, int run0, uint32_t magic,
                                           int lvl, int W, int top) {
-    const MergeSlot m = merge_slot(n, p, run0, inv_run0, lvl, W);
+    const MergeSlot m = merge_slot(n, p, run_index(p, run0, magic), lvl, W);
     int c = 0;
 #pragma unroll 1
     for (int st = top; st > 0; st >>= 1) {
@@ -352,9 +356,9 @@ __device__ __forceinline__ int merge_dest(const uint64_t* src, int n, int p, uin
 // The same for two words at once (indices p0 and p1 of src), their searches interleaved
 // so that each step's two LDS reads are in flight together.
 __device__ __forceinline__ void merge_dest2(const uint64_t* src, int n, int p0, uint64_t v0, int p1, uint64_t v1,
-                                            int run0, float inv_run0, int lvl, int W, int top, int& d0, int& d1) {
-    const MergeSlot m0 = merge_slot(n, p0, run0, inv_run0, lvl, W);
-    const MergeSlot m1 = merge_slot(n, p1, run0, inv_run0, lvl, W);
+                                            int run0, uint32_t magic, int lvl, int W, int top, int& d0, int& d1) {
+    const MergeSlot m0 = merge_slot(n, p0, run_index(p0, run0, magic), lvl, W);
+    const MergeSlot m1 = merge_slot(n, p1, run_index(p1, run0, magic), lvl, W);
     int c0 = 0, c1 = 0;
 #pragma unroll 1
     for (int st = top; st > 0; st >>= 1) {
@@ -381,7 +385,7 @@ __device__ __forceinline__ const uint64_t* merge_sort_slots(SchedShared<NT>& sh,
     const bool pp = n <= kMaxN / 2;
     uint64_t* src = sh.item;
     uint64_t* dst = pp ? sh.item + kMaxN / 2 : sh.item;
-    const float inv_run0 = 1.0f / (float)run0;
+    const uint32_t magic = run0 > 1 ? (uint32_t)((0xFFFFFFFFull + (uint64_t)run0) / (uint64_t)run0) : 0u;
     int top = 1;
     while (2 * top <= run0) top *= 2;
     int lvl = 0;
@@ -390,12 +394,17 @@ __device__ __forceinline__ const uint64_t* merge_sort_slots(SchedShared<NT>& sh,
         if (pp) {  // source and destination apart: each word moves as soon as its place is known
 #pragma unroll 1
             for (int p0 = tid; p0 < n; p0 += 2 * NT) {
-                const int p1 = p0 + NT < n ? p0 + NT : p0;  // a lone word is searched twice
-                const uint64_t v0 = src[p0], v1 = src[p1];
-                int d0, d1;
-                merge_dest2(src, n, p0, v0, p1, v1, run0, inv_run0, lvl, W, top, d0, d1);
-                dst[d0] = v0;
-                dst[d1] = v1;
+                const int p1 = p0 + NT;
+                const uint64_t v0 = src[p0];
+                if (p1 < n) {
+                    const uint64_t v1 = src[p1];
+                    int d0, d1;
+                    merge_dest2(src, n, p0, v0, p1, v1, run0, magic, lvl, W, top, d0, d1);
+                    dst[d0] = v0;
+                    dst[d1] = v1;
+                } else {
+                    dst[merge_dest(src, n, p0, v0, run0, magic, lvl, W, top)] = v0;
+                }
             }
             __syncthreads();
             uint64_t* t = src;
@@ -406,7 +415,7 @@ __device__ __forceinline__ const uint64_t* merge_sort_slots(SchedShared<NT>& sh,
 #pragma unroll
             for (int k = 0; k < JM; ++k) {
                 const int p = tid + k * NT;
-                dest[k] = p < n ? merge_dest(src, n, p, src[p], run0, inv_run0, lvl, W, top) : -1;
+                dest[k] = p < n ? merge_dest(src, n, p, src[p], run0, magic, lvl, W, top) : -1;
             }
             uint64_t v[JM];
 #pragma unroll
@@ -538,17 +547,12 @@ __device__ __forceinline__ int choose_budget_lds(SchedShared<NT>& sh, const uint
         sh.wdrop[w] = dw;
     }
     __syncthreads();
-    double F = sh.wbest_f[0];
-    int Bx = sh.wbest_b[0], D = sh.wdrop[0];
-    for (int q = 1; q < kSW; ++q) {
-        const double f = sh.wbest_f[q];
-        const int b = sh.wbest_b[q];
-        if (f > F || (f == F && b < Bx)) {
-            F = f;
-            Bx = b;
-        }
-        D = min(D, sh.wdrop[q]);
-    }
+    static_assert(kSW <= 64, "one lane per wave's partials");
+    const double fq = lane < kSW ? sh.wbest_f[lane] : -INFINITY;
+    const int bq = lane < kSW ? sh.wbest_b[lane] : kNone;
+    const double F = wave_max_f64(fq);
+    const int Bx = wave_min_i32(fq == F ? bq : kNone);
+    const int D = wave_min_i32(lane < kSW ? sh.wdrop[lane] : kNone);
     const int B = rule == kRuleFirstDrop ? D : Bx;
     if (tid == 0 && b_star) *b_star = B;
     if (best_obj) {
@@ -564,12 +568,14 @@ __device__ __forceinline__ int choose_budget_lds(SchedShared<NT>& sh, const uint
 
 // Stage 5.  sel must already mark the chosen slots (1 byte per flat id, n entries).
 // lds_rows (may be null): per request r, lds_rows[2r] = its offset into ver_idx and
-// lds_rows[2r + 1] = its prefix length.
+// lds_rows[2r + 1] = its prefix length.  tok_lds (may be null): the draft tokens, already
+// in LDS.
 template <int NT>
 __device__ __forceinline__ void allocate_lds(SchedShared<NT>& sh, const uint8_t* sel, int R, int K, int B,
                              const int32_t* __restrict__ tokens, int32_t* __restrict__ prefix_len,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ ver_idx,
-                             int32_t* __restrict__ ver_tokens, int32_t* lds_rows = nullptr) {
+                             int32_t* __restrict__ ver_tokens, int32_t* lds_rows = nullptr,
+                             const int32_t* tok_lds = nullptr) {
     const int tid = threadIdx.x;
     const int n = R * K;
     const int CR = (R + NT - 1) / NT;
@@ -591,7 +597,7 @@ __device__ __forceinline__ void allocate_lds(SchedShared<NT>& sh, const uint8_t*
             const int f = r * K + i;
             if (sel[f]) {
                 ver_idx[o + L] = f;
-                if (ver_tokens) ver_tokens[o + L] = tokens[f];
+                if (ver_tokens) ver_tokens[o + L] = tok_lds ? tok_lds[f] : tokens[f];
                 ++L;
             }
         }
@@ -656,6 +662,10 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     const int passes = sz.separate ? 2 : 1;
     int B = 0;
     const uint64_t* rk = sh.item;
+    // The draft tokens (for ver_tokens) go to LDS with the confidences when they fit past
+    // the merge's upper half (n <= kMaxN / 3): words [kMaxN / 2 + n, kMaxN) are free.
+    int32_t* tok_lds = (tokens && ver_tokens && 3 * n <= kMaxN)
+                           ? reinterpret_cast<int32_t*>(sh.item + kMaxN / 2 + n) : nullptr;
 #pragma unroll 1
     for (int ps = 0; ps < passes; ++ps) {
         const bool sizing = ps == 0, last = ps == passes - 1;
@@ -667,7 +677,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
         // memory round trips overlap (and the sort)
         CostPrefetch cp;
         if (sizing) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
-        survival_to_lds<NT>(sh, src, rows, K, last ? surv_out : nullptr, status);
+        survival_to_lds<NT>(sh, src, rows, K, last ? surv_out : nullptr, status, tokens, last ? tok_lds : nullptr);
         rk = merge_sort_slots<NT>(sh, m, K);  // each request's row is a sorted run
         if (sizing) {
             if (last) write_ranking<NT>(rk, n, order, sorted_surv, nullptr);
@@ -685,7 +695,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     uint8_t* sel = selection_map<NT>(sh);
     for (int j = threadIdx.x; j < n; j += NT) sel[word_slot(rk[j])] = (uint8_t)(j < B);
     __syncthreads();
-    allocate_lds<NT>(sh, sel, R, K, B, tokens, prefix_len, offsets, ver_idx, ver_tokens, lds_rows);
+    allocate_lds<NT>(sh, sel, R, K, B, tokens, prefix_len, offsets, ver_idx, ver_tokens, lds_rows, tok_lds);
 }
 
 }  // namespace
