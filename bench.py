@@ -493,7 +493,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="headline", choices=["tiny", "small", "mid", "headline", "large", "sweep"])
+    ap.add_argument("--workload", default="headline", choices=["tiny", "small", "mid", "headline", "large", "shard", "sweep"])
     ap.add_argument("--pool", type=int, default=4, help="distinct per-step input sets cycled through")
     ap.add_argument("--cpu-rows", type=int, default=128, help="requests in the oracle's timed chain sample")
     ap.add_argument("--event-steps", type=int, default=200,

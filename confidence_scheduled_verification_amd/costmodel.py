@@ -1,10 +1,10 @@
 """Start-up cost tables measured on this GPU (vLLM blog "Adaptive Verification in
 vLLM", section "The cost model").
 
-The engine times dummy steps over the captured graph sizes plus a couple of sizes
-above the largest, takes the median of five runs per shape and builds two tables:
-verification cost by step token count and drafting cost by request count, each
-forced monotone.  Here the dummy step is a stand-in for the target model's forward
+At start-up, dummy steps are timed at every captured graph size and at a few sizes
+past the largest one; each shape's cost is the median over five timings, and the
+costs form two tables (verification indexed by the step's token count, drafting by
+the number of requests), each made non-decreasing.  Here the dummy step is a stand-in for the target model's forward
 pass -- `layers` bf16 GEMMs of shape [t, H] x [H, H] -- since no model runs in this
 package; the timing (dspark_profile_shapes) and the table construction
 (dspark_build_cost_table) are the library's.

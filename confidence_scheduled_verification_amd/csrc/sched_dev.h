@@ -624,8 +624,8 @@ __device__ __forceinline__ uint8_t* selection_map(SchedShared<NT>& sh) {
 
 // Where the budget is sized from: the current confidences (separate == 0), or another
 // array [R][K] such as the one of one or two steps earlier (vLLM blog, "Scheduling the
-// budget": B is sized from a one-step-old confidence buffer while the slots are handed
-// out with current values).  bmax is the largest B of that sizing, rule the admission
+// budget": the size of B may come from confidences a step old, the slots themselves
+// are then assigned by the current ones).  bmax is the largest B of that sizing, rule the admission
 // rule.
 struct Sizing {
     int separate;

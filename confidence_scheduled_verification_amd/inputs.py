@@ -105,7 +105,7 @@ WORKLOADS = {
 def pad_to_graph(t: int, graph_max: int) -> int:
     """Smallest captured graph size (a power of two) that holds t tokens.
 
-    A step of 121 tokens runs the 128-token graph (vLLM blog, "The cost model").
+    121 tokens are padded up to the 128-token graph (vLLM blog, "The cost model").
     pad(0) is the smallest graph, 1.  Sizes above graph_max are not padded.
     """
     if t > graph_max:

@@ -13,8 +13,8 @@
  *                   request (vLLM blog "Adaptive Verification in vLLM", section
  *                   "Scheduling the budget");
  *   3. top-B     -- all request x position slots ranked globally by survival;
- *                   every prefix of that ranking is a contiguous prefix of each
- *                   request's draft (same section);
+ *                   taking the ranking's first B slots takes, in each request,
+ *                   its first positions only (same section);
  *   4. budget    -- B chosen to maximise expected tokens per microsecond,
  *                   (N_sampling + sum of the B best survivals) divided by
  *                   verify_cost[T + B] + draft_cost[num_reqs] (same section, and
@@ -142,8 +142,8 @@ int dspark_markov_prepare(dspark_markov_t* m, const void* A, const void* Bmat, i
  *     x[v] = base[r,i,v] + sum_k A[prev,k] * Bmat[k,v]    (fp32 accumulation)
  *     tokens[r,i] = argmax_v x[v];  prev = tokens[r,i]
  * (DSpark summary, "Draft better": a small Markov head corrects each position's scores
- * from the previous token alone; MAX worklog, "What DSpark is": a low-rank bias keyed
- * on the previous chosen token, then an argmax.)
+ * from the previous token alone; MAX worklog, "What DSpark is": a rank-r additive term
+ * selected by the token chosen one position earlier, then an argmax.)
  *
  *   base            [R,K,V]   backbone logits (dtype)
  *   A               [V,rank]  first factor, row u = key vector of previous token u (dtype)
@@ -459,7 +459,7 @@ int dspark_profile_shapes(dspark_shape_fn fn, void* user, const int32_t* shapes,
  *   2. shapes <= graph_max are the captured graph sizes and must include graph_max;
  *      entry t <= graph_max is the cost of the smallest captured shape >= t (t = 0
  *      counts as 1): a step runs, and pays for, the padded graph, so the table is a
- *      staircase (a batch of 121 tokens runs the 128-token graph);
+ *      staircase (121 tokens are charged what the 128-token graph costs);
  *   3. past the capture limit the cost is continuous: entry t > graph_max lies on
  *      the line through the two nearest measured shapes above graph_max (the first
  *      or last segment extended beyond them; a single such shape gives a constant),

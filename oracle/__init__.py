@@ -16,6 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import threading
 
 import numpy as np
 
@@ -23,35 +24,41 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "chain.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle_chain.so")
 _lib = None
+_lock = threading.Lock()  # tests call the oracle from several host threads at once
 
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (-O2, no contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+    with _lock:
+        if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            tmp = f"{_LIB_PATH}.tmp{os.getpid()}"
+            subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                                   "-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
 
 def _load():
     global _lib
-    if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
-        p = ctypes.c_void_p
-        lib.oracle_chain.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_int, p, ctypes.c_int, p, p, p, p]
-        lib.oracle_chain.restype = ctypes.c_int
-        lib.oracle_chain_sample.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                            ctypes.c_int, p, ctypes.c_int, p, ctypes.c_double, ctypes.c_uint64,
-                                            p, p, p]
-        lib.oracle_chain_sample.restype = ctypes.c_int
-        lib.oracle_philox4x32.argtypes = [p, p, p]
-        lib.oracle_philox4x32.restype = None
-        _lib = lib
-    return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+    build(force=False)
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(_LIB_PATH)
+            p = ctypes.c_void_p
+            lib.oracle_chain.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, p, ctypes.c_int, p, p, p, p]
+            lib.oracle_chain.restype = ctypes.c_int
+            lib.oracle_chain_sample.argtypes = [p, p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, p, ctypes.c_int, p, ctypes.c_double,
+                                                ctypes.c_uint64, p, p, p]
+            lib.oracle_chain_sample.restype = ctypes.c_int
+            lib.oracle_philox4x32.argtypes = [p, p, p]
+            lib.oracle_philox4x32.restype = None
+            _lib = lib
+        return _lib
 
 
 def _ptr(a):

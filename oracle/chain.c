@@ -9,8 +9,8 @@
  * What it computes (DSpark summary, "Draft better": a lightweight Markov head
  * nudges each position's odds using only the token chosen just before it,
  * stored as a rank-256 factorisation; MAX worklog, "What DSpark is", item 3:
- * the chain is a low-rank bias keyed on the previous chosen token followed by
- * an argmax):
+ * the chain adds a rank-r term selected by the token chosen one position
+ * earlier and takes an argmax):
  *
  *   prev = prev0[r]
  *   for i = 0 .. K-1:

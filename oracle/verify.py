@@ -15,8 +15,8 @@ Layout readings:
   * request r's verified drafts are ver_tokens[offsets[r] .. offsets[r+1]), the
     compacted list of the allocation stage, L_r = offsets[r+1] - offsets[r];
   * the target pass runs 1 + L_r tokens per request (the last accepted token and
-    the L_r drafts; vLLM blog, section "Varlen decode CUDA graphs": any mix of 1
-    to k+1 tokens per request), so its greedy tokens for request r are
+    the L_r drafts; vLLM blog, section "Varlen decode CUDA graphs": each request
+    may carry between 1 and k+1 tokens), so its greedy tokens for request r are
     target[offsets[r] + r .. offsets[r] + r + L_r], entry j being the target's
     choice after the request's first j drafts;
   * accepted a_r = the number of leading j < L_r with draft j == target entry j;
