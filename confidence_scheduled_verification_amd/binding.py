@@ -37,7 +37,7 @@ MARKOV_HEADER_BYTES = 256
 EXPORTS = ["dspark_last_error", "dspark_version", "dspark_workspace_bytes", "dspark_markov_state_bytes",
            "dspark_markov_prepare", "dspark_set_chain_form", "dspark_get_chain_form",
            "dspark_chain", "dspark_chain_sample", "dspark_survival", "dspark_topb_select", "dspark_choose_budget", "dspark_allocate",
-           "dspark_step", "dspark_step_sized", "dspark_schedule", "dspark_accept_greedy", "dspark_set_timing_events",
+           "dspark_step", "dspark_step_sized", "dspark_step_static", "dspark_schedule", "dspark_accept_greedy", "dspark_set_timing_events",
            "dspark_force_monotone", "dspark_profile_shapes", "dspark_build_cost_table", "dspark_set_launch_mode",
            "dspark_get_launch_mode"]
 
@@ -90,6 +90,8 @@ def lib():
         L.dspark_allocate.argtypes = [p, p, i, i, p, p, p, p, p, p]
         L.dspark_step.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, p, i, p, i, p, p, p, p, p, p, p, p,
                                   p, p, p, p, sz, p]
+        L.dspark_step_static.argtypes = [p, p, p, i, p, i, i, i, i, p, p, i, i, i, p, i, p, i, p, p, p, p, p, p,
+                                         p, p, p, p, p, p]
         L.dspark_step_sized.argtypes = [p, p, p, i, p, i, i, i, i, p, p, p, i, i, i, i, i, p, i, p, i, p, p, p,
                                         p, p, p, p, p, p, p, p, p, sz, p]
         L.dspark_accept_greedy.argtypes = [p, p, p, i, i, p, p, p, p, p]
@@ -272,7 +274,7 @@ def dspark_allocate(order, b_star, R: int, K: int, prefix_len, offsets, ver_idx,
 
 
 def _step_checks(base, markov: MarkovHead, prev0, conf, verify_cost, draft_cost, out: "StepBuffers", ws, status,
-                 what):
+                 what, need_ws=True):
     R, K, V = _chain_checks(base, markov, prev0, out.tokens, None, what)
     _shape(conf, (R, K), f"{what}: conf")
     for t, n in ((conf, "conf"), (verify_cost, "verify_cost"), (draft_cost, "draft_cost")):
@@ -288,7 +290,7 @@ def _step_checks(base, markov: MarkovHead, prev0, conf, verify_cost, draft_cost,
     if status is not None and (status.numel() < 1 or status.element_size() != 4):
         raise ValueError(f"{what}: status must hold one 32-bit word")
     need = dspark_workspace_bytes(R, K, V, markov.rank, markov.dtype)
-    if _ws_bytes(ws) < need:
+    if need_ws and _ws_bytes(ws) < need:
         raise ValueError(f"{what}: workspace of {need} bytes needed, {_ws_bytes(ws)} given")
     return R, K, V
 
@@ -308,6 +310,19 @@ def dspark_step(base, markov: MarkovHead, prev0, conf, n_sampling: int, T: int, 
                              _p(out.sorted_surv), _p(out.b_star), _p(out.best_obj), _p(out.prefix_len),
                              _p(out.offsets), _p(out.ver_idx), _p(out.ver_tokens), _p(status), _p(ws),
                              _ws_bytes(ws), _stream(stream)))
+
+
+def dspark_step_static(base, markov: MarkovHead, prev0, conf, n_sampling: int, T: int, num_reqs: int, verify_cost,
+                       draft_cost, out: "StepBuffers", status=None, stream=None):
+    """dspark_step with the library's static workspace (no workspace argument)."""
+    R, K, V = _step_checks(base, markov, prev0, conf, verify_cost, draft_cost, out, None, status,
+                           "dspark_step_static", need_ws=False)
+    _check(lib().dspark_step_static(_p(base), _p(markov.A), _p(markov.Bmat), markov.dtype, _p(prev0), R, K, V,
+                                    markov.rank, markov._ref, _p(conf), n_sampling, T, num_reqs, _p(verify_cost),
+                                    verify_cost.numel(), _p(draft_cost), draft_cost.numel(), _p(out.tokens),
+                                    _p(out.surv), _p(out.order), _p(out.sorted_surv), _p(out.b_star),
+                                    _p(out.best_obj), _p(out.prefix_len), _p(out.offsets), _p(out.ver_idx),
+                                    _p(out.ver_tokens), _p(status), _stream(stream)))
 
 
 def dspark_schedule(conf, n_sampling: int, T: int, num_reqs: int, verify_cost, draft_cost, out: "StepBuffers",

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "dspark.h"
@@ -400,6 +401,69 @@ int dspark_step(const void* base, const void* A, const void* Bmat, int dtype, co
                              n_sampling, T, num_reqs, verify_cost, verify_len, draft_cost, draft_len, tokens, surv,
                              order, sorted_surv, b_star, best_obj, prefix_len, offsets, ver_idx, ver_tokens, status,
                              ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// The workspace of dspark_step_static: one array per GPU, in the library's device code,
+// zero at load and held until the process ends.  Host code never uses its name as an
+// address: each device's copy is found once with hipGetSymbolAddress and kept here.
+static __device__ __align__(256) unsigned char scratch[DSPARK_STATIC_WS_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices] = {};
+
+// The current device's copy of `scratch` (found on the first call made on that device).
+int static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "step_static (current device)");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(DSPARK_EUNSUPPORTED, "step_static: device %d beyond the %d this library tracks", dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "step_static (address of the static workspace)");
+        if (!ptr) return fail(DSPARK_EHIP, "step_static: no address for the static workspace");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_step_static(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0, int R,
+                       int K, int V, int rank, const dspark_markov_t* markov, const float* conf, int n_sampling,
+                       int T, int num_reqs, const float* verify_cost, int verify_len, const float* draft_cost,
+                       int draft_len, int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                       int32_t* b_star, double* best_obj, int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx,
+                       int32_t* ver_tokens, uint32_t* status, void* stream) {
+    int rc = check_chain(base, A, Bmat, dtype, prev0, R, K, V, rank, tokens);
+    if (rc != DSPARK_OK) return rc;
+    const size_t need = R > 0 && K > 0 ? ws_need(R, K, V, dtype) : 0;
+    if (need > (size_t)DSPARK_STATIC_WS_BYTES)
+        return fail(DSPARK_ERANGE, "step_static: R=%d, K=%d need %zu bytes of workspace, the static one holds %d", R,
+                    K, need, DSPARK_STATIC_WS_BYTES);
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws)) != DSPARK_OK) return rc;
+    // The dense forms need their counters and keys at zero; an earlier call may have left
+    // them set (a DSPARK_STATUS_SYNC_TIMEOUT), so they are cleared by a fill kernel first.
+    // The pruned chain and the schedule keep nothing in the workspace.
+    if (need > 0 && !use_pruned(dtype, R, K, V, A, nullptr)) {
+        const hipError_t e = dspark::launch_zero_keys((uint64_t*)ws, need / 8, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "step_static (clearing the static workspace)");
+    }
+    return dspark_step(base, A, Bmat, dtype, prev0, R, K, V, rank, markov, conf, n_sampling, T, num_reqs, verify_cost,
+                       verify_len, draft_cost, draft_len, tokens, surv, order, sorted_surv, b_star, best_obj,
+                       prefix_len, offsets, ver_idx, ver_tokens, status, ws, (size_t)DSPARK_STATIC_WS_BYTES, stream);
 }
 
 int dspark_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R, int K,

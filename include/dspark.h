@@ -312,6 +312,28 @@ int dspark_step(const void* base, const void* A, const void* Bmat, int dtype, co
                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dspark_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments
+ * and results without ws / ws_bytes.  The workspace is a static array of
+ * DSPARK_STATIC_WS_BYTES in the library's device code, one per GPU (each GPU holds it
+ * from the first call made on it until the process ends), which covers every shape
+ * dspark_step accepts; a shape needing more returns DSPARK_ERANGE.  The call allocates
+ * nothing and enqueues, before the step, one fill kernel that clears the array's
+ * counters and keys when a dense form will run.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from different host
+ * threads without ordering) race and must be serialised by the caller.
+ */
+#define DSPARK_STATIC_WS_BYTES (512 * 1024)
+int dspark_step_static(const void* base, const void* A, const void* Bmat, int dtype, const int32_t* prev0,
+                       int R, int K, int V, int rank, const dspark_markov_t* markov,
+                       const float* conf, int n_sampling, int T, int num_reqs,
+                       const float* verify_cost, int verify_len, const float* draft_cost, int draft_len,
+                       int32_t* tokens, float* surv, int32_t* order, float* sorted_surv,
+                       int32_t* b_star, double* best_obj,
+                       int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
+                       uint32_t* status, void* stream);
+
+/*
  * Stages 2-5 alone, in one kernel (one workgroup of 1024 threads working out of LDS):
  * survival, global top-B, the budget under `rule` (optionally sized from another
  * confidence array, as in dspark_step_sized) and the allocation, with no host
