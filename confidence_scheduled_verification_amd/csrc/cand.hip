@@ -168,15 +168,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The prepared head's bound: ab2 = 2 a b (1 + 2^-10) rounded up, ok = it is finite.
+// The prepared head's bound: ab2 = 2 a b (1 + 2^-10) rounded up, ok = it is finite, and
+// b1 = b (1 + 2^-10) rounded up (a, b: the largest row norms of A and Bt).
 struct HeaderView {
     float ab2;
     bool ok;
+    float b1;
 };
 
 __device__ __forceinline__ HeaderView header_view(const void* hdr) {
     const uint32_t* h = (const uint32_t*)hdr;
-    return HeaderView{__uint_as_float(h[4]), h[5] != 0u};
+    return HeaderView{__uint_as_float(h[4]), h[5] != 0u, __uint_as_float(h[6])};
 }
 
 // LDS of one request.
@@ -505,8 +507,24 @@ __device__ __forceinline__ void score_list(const QLds& L, uint32_t n, const uint
     }
 }
 
+// Bound on the norm of the key row this wave holds (lane l: entries 4l .. 4l+3): the
+// square root of the sum of squares, times 1 + 2^-12 for the sum's rounding; the same
+// value in every lane.
+__device__ __forceinline__ float key_norm_up(const u32x2& key) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const float lo = __uint_as_float(key[d] << 16), hi = __uint_as_float(key[d] & 0xFFFF0000u);
+        s = __builtin_fmaf(lo, lo, s);
+        s = __builtin_fmaf(hi, hi, s);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+    return __builtin_sqrtf(s) * (1.0f + 0x1p-12f);
+}
+
 // The chain wave's work on request r (see the file comment).
-__device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, float ab2, bool bound_ok) {
+__device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, float ab2, float b1, bool bound_ok) {
     const int lane = threadIdx.x & 63;
     const int K = a.K, NC = a.NC, V = a.V, rank = a.rank;
     const long row0 = (long)r * K;
@@ -559,7 +577,10 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
         } else {
             // list the kept entries that clear the final floor, score them in lists of
             // at most kQList; note the largest (the likely token)
-            const float fl = cand_floor(M, ab2);
+            // Once the position's key row is known, every bias is at most |key| b in size, so
+            // the floor may use 2 |key| b1 where the streams had to use 2 a b (the lower wins).
+            const float ab2_key = 2.0f * key_norm_up(key) * b1 * (1.0f + 0x1p-20f);
+            const float fl = cand_floor(M, ab2_key < ab2 ? ab2_key : ab2);
             uint64_t best = 0ull, top = 0ull;
             uint32_t n = 0;
             bool prefetched = false;
@@ -613,7 +634,7 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
         if ((int)(threadIdx.x >> 6) < kQS)
             stream_items<VEC>(S, a.base + (size_t)r * (size_t)a.K * (size_t)a.V, per_req, a.NC, a.V, hv.ab2);
         else
-            chain_wave(a, S, r, hv.ab2, hv.ok);
+            chain_wave(a, S, r, hv.ab2, hv.b1, hv.ok);
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
     }
 }
@@ -641,6 +662,7 @@ __global__ void markov_bound_kernel(uint64_t* hdr) {
     const bool ok = ab2 == ab2 && ab2 < 1e30;
     f[0] = ok ? __double2float_ru(ab2) : 0.f;
     reinterpret_cast<uint32_t*>(&hdr[2])[1] = ok ? 1u : 0u;
+    f[2] = ok ? __double2float_ru(__builtin_sqrt(b2) * (1.0 + 0x1p-10)) : 0.f;
 }
 
 __global__ void zero_u64_kernel(uint64_t* p, int n) {

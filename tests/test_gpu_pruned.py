@@ -133,3 +133,38 @@ def test_pruned_step_matches_the_oracle_on_a_fresh_draw_each_step():
         got, status, _ = gu.run_step(sub, conf, R, w.T, R, vc, dc)
         assert status == 0
         gu.assert_chain_parity(got["tokens"], None, base, ins.A, ins.Bmat, w.dtype, prev0)
+
+
+def test_winner_at_the_edge_of_the_key_row_bound():
+    # Position 0 of request 0 is keyed on a row of A whose norm is well below A's largest,
+    # so the chain's floor uses the key row's own norm.  The winner's Bt row points along
+    # the key row and the row maximum's against it: the winner's logit lies 2|a||b| below
+    # the maximum plus 0.03, just inside that floor, and only its exact score finds it.
+    R, K, V, rank = 2, 2, 5000, 64
+    c = _case(4242, R, K, V, rank, base_std=0.3, factor_std=0.02)
+    rng = np.random.default_rng(4243)
+    p, u_top, v_win, b = 7, 100, 200, 0.5
+    key = rng.standard_normal(rank).astype(np.float32)
+    key *= 0.5 / np.linalg.norm(key)
+    A_f = rng.standard_normal((V, rank)).astype(np.float32) * 0.125  # other rows: norm about 1
+    A_f[p] = key
+    c["A"] = inputs.round_to_bf16(A_f)
+    unit = key / np.linalg.norm(key)
+    Bm = (rng.standard_normal((rank, V)).astype(np.float32) * 0.02)
+    Bm[:, v_win] = b * unit
+    Bm[:, u_top] = -b * unit
+    c["Bmat"] = inputs.round_to_bf16(Bm)
+    c["prev0"][0] = p
+    # the exact biases of the two rows from the bf16 values, and the base logits around them
+    a16 = c["A"].astype(np.uint32) << 16
+    m16 = c["Bmat"].astype(np.uint32) << 16
+    a_row = a16[p].view(np.float32).astype(np.float64)
+    bias = lambda v: float(a_row @ m16[:, v].view(np.float32).astype(np.float64))
+    top = 4.0
+    base = (c["base"].astype(np.uint32) << 16).view(np.float32)
+    base[0, 0, u_top] = top
+    base[0, 0, v_win] = top + bias(u_top) - bias(v_win) + 0.03
+    c["base"] = inputs.round_to_bf16(base)
+    tp, sp, sd, _ = _both_forms(c, R, K, V, rank)
+    assert sp == sd == 0
+    assert tp[0, 0] == v_win
