@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kST, 1) void topb_kernel(const float* __restrict__ 
     __shared__ SchedShared<kST> sh;
     const int n = R * K;
     surv_global_to_lds<kST>(sh, surv, n);
-    const uint64_t* rk = merge_sort_slots<kST>(sh, n, 1);  // the survivals may come in any order
+    const uint64_t* rk = rank_slots<kST>(sh, n, 1);  // the survivals may come in any order
     write_ranking<kST>(rk, n, order, sorted_surv, rank);
 }
 

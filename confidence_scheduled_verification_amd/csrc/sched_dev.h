@@ -12,12 +12,16 @@
 //   * Ranking sorts one 64-bit word per slot, (0x3F800000 - bits(s)) << 16 | flat id:
 //     non-negative floats order like their bit patterns, so ascending words are
 //     (s descending, request ascending, position ascending) and every word is
-//     distinct.  The sort is a bottom-up merge over runs that are adjacent in flat
-//     order: each level moves a slot to its own index in its run plus the number of
-//     smaller words in the partner run (a binary search in LDS), so a level is one
-//     parallel step with no counters or scans.  A request's survivals never rise
-//     along its positions (each factor is at most 1 and rounding is monotone), so
-//     the first runs are whole requests and R requests take ceil(log2 R) levels.
+//     distinct.  Up to two slots per thread the sort is a bottom-up merge over runs
+//     that are adjacent in flat order: each level moves a slot to its own index in its
+//     run plus the number of smaller words in the partner run (a binary search in
+//     LDS), so a level is one parallel step with no counters or scans.  A request's
+//     survivals never rise along its positions (each factor is at most 1 and rounding
+//     is monotone), so the first runs are whole requests and R requests take
+//     ceil(log2 R) levels.  Past that size the merge's n log n searches cost more than
+//     a stable LSD radix sort of the key bits (four 8-bit passes, each ranking a
+//     wave's 64 words per round by wavefront ballots of the digit bits, with per-wave
+//     digit counters and one block scan), which takes over.
 //   * S_B is summed EXACTLY: each float32 survival is an integer multiple of
 //     2^-149, held as a 192-bit integer, scanned in any order with the same
 //     result; N + S_B is rounded to double once (round to nearest even) and the
@@ -372,62 +376,147 @@ __device__ __forceinline__ void merge_dest2(const uint64_t* src, int n, int p0, 
     d1 = m1.base + (c1 < m1.len ? c1 : m1.len);
 }
 
-// Sorts the n slot words in sh.item, whose runs [j*run0, (j+1)*run0) are each ascending
-// already (run0 = 1 for arbitrary words); returns where the sorted words are (sh.item or
-// its upper half).  Entered after a barrier that follows the last writes of the words.
+// Sorts the n <= kMaxN / 2 slot words in sh.item, whose runs [j*run0, (j+1)*run0) are
+// each ascending already (run0 = 1 for arbitrary words); returns where the sorted words
+// are (sh.item or its upper half, the two halves serving as source and destination in
+// turn).  Entered after a barrier that follows the last writes of the words.
 // Level l merges run pairs of width W = run0 << l: the word at index p of run j moves to
 // (start of the pair) + (p - j W) + (number of words of the partner run below it), so
 // runs that are adjacent in flat order stay adjacent and no two words share a place.
 template <int NT>
 __device__ __forceinline__ const uint64_t* merge_sort_slots(SchedShared<NT>& sh, int n, int run0) {
-    constexpr int JM = kMaxN / NT;
     const int tid = threadIdx.x;
-    const bool pp = n <= kMaxN / 2;
     uint64_t* src = sh.item;
-    uint64_t* dst = pp ? sh.item + kMaxN / 2 : sh.item;
+    uint64_t* dst = sh.item + kMaxN / 2;
     const uint32_t magic = run0 > 1 ? (uint32_t)((0xFFFFFFFFull + (uint64_t)run0) / (uint64_t)run0) : 0u;
-    int top = 1;
+    int top = 1;  // largest power of two <= W
     while (2 * top <= run0) top *= 2;
     int lvl = 0;
 #pragma unroll 1
     for (int W = run0; W < n; W *= 2, top *= 2, ++lvl) {
-        if (pp) {  // source and destination apart: each word moves as soon as its place is known
 #pragma unroll 1
-            for (int p0 = tid; p0 < n; p0 += 2 * NT) {
-                const int p1 = p0 + NT;
-                const uint64_t v0 = src[p0];
-                if (p1 < n) {
-                    const uint64_t v1 = src[p1];
-                    int d0, d1;
-                    merge_dest2(src, n, p0, v0, p1, v1, run0, magic, lvl, W, top, d0, d1);
-                    dst[d0] = v0;
-                    dst[d1] = v1;
-                } else {
-                    dst[merge_dest(src, n, p0, v0, run0, magic, lvl, W, top)] = v0;
-                }
+        for (int p0 = tid; p0 < n; p0 += 2 * NT) {
+            const int p1 = p0 + NT;
+            const uint64_t v0 = src[p0];
+            if (p1 < n) {
+                const uint64_t v1 = src[p1];
+                int d0, d1;
+                merge_dest2(src, n, p0, v0, p1, v1, run0, magic, lvl, W, top, d0, d1);
+                dst[d0] = v0;
+                dst[d1] = v1;
+            } else {
+                dst[merge_dest(src, n, p0, v0, run0, magic, lvl, W, top)] = v0;
             }
-            __syncthreads();
-            uint64_t* t = src;
-            src = dst;
-            dst = t;
-        } else {  // in place: every word of the level is read before any moves
-            int dest[JM];
-#pragma unroll
-            for (int k = 0; k < JM; ++k) {
-                const int p = tid + k * NT;
-                dest[k] = p < n ? merge_dest(src, n, p, src[p], run0, magic, lvl, W, top) : -1;
-            }
-            uint64_t v[JM];
-#pragma unroll
-            for (int k = 0; k < JM; ++k) v[k] = dest[k] >= 0 ? src[tid + k * NT] : 0ull;
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < JM; ++k)
-                if (dest[k] >= 0) src[dest[k]] = v[k];
-            __syncthreads();
         }
+        __syncthreads();
+        uint64_t* t = src;
+        src = dst;
+        dst = t;
     }
     return src;
+}
+
+// Digit counters of the radix passes, digit-major with a stride of (waves + 1) words so
+// that both the per-wave ranking (one digit per lane) and the block scan (consecutive
+// (digit, wave) entries per thread) touch distinct LDS banks.  They live in the space of
+// the per-thread partials (free until the selection map is built).
+template <int NT>
+__device__ __forceinline__ int hist_at(int d, int w) { return d * (NT / 64 + 1) + w; }
+
+template <int NT>
+__device__ __forceinline__ uint32_t* radix_hist(SchedShared<NT>& sh) {
+    static_assert(sizeof(sh.part) >= 256 * (NT / 64 + 1) * sizeof(uint32_t), "the digit counters fit");
+    return reinterpret_cast<uint32_t*>(&sh.part[0]);
+}
+
+// One stable counting pass over the 8-bit digit at key bit `shift` of the n_pad words in
+// sh.item.  Wave w owns words [w*S, (w+1)*S) of the current order, 64 per round; a
+// word's rank among equal digits of its wave comes from a ballot match of the digit
+// bits and a running per-(digit, wave) counter.  Entered after a barrier that follows
+// the last writes of the words.  A wave's counter column is written and read by that
+// wave alone until the barrier before the offset scan, so clearing it needs no barrier
+// of its own.
+template <int NT>
+__device__ __forceinline__ void radix_pass(SchedShared<NT>& sh, int n_pad, int shift) {
+    constexpr int kSW = NT / 64, JM = kMaxN / NT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int S = n_pad / kSW;  // words per wave, a multiple of 64
+    const int J = S / 64;       // rounds, <= JM
+    uint32_t* hist = radix_hist<NT>(sh);
+    uint32_t k[JM];   // key bits of the word
+    uint32_t il[JM];  // its flat id (low 16 bits) and rank among equal digits of the wave (high 16 bits)
+    for (int d = lane; d < 256; d += 64) hist[hist_at<NT>(d, w)] = 0u;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        if (j < J) {
+            const uint64_t x = sh.item[w * S + j * 64 + lane];
+            k[j] = word_key(x);
+            il[j] = (uint32_t)x & 0xFFFFu;
+        }
+    }
+    const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        if (j < J) {
+            const uint32_t d = (k[j] >> shift) & 0xFFu;
+            uint64_t peers = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const bool on = (d >> b) & 1u;
+                const uint64_t m = __ballot(on);
+                peers &= on ? m : ~m;
+            }
+            const uint32_t before = (uint32_t)__popcll(peers & lt);
+            const uint32_t h = hist[hist_at<NT>(d, w)];
+            il[j] |= (h + before) << 16;
+            if (before == 0u) hist[hist_at<NT>(d, w)] = h + (uint32_t)__popcll(peers);
+        }
+    }
+    __syncthreads();
+    // offsets in (digit, wave) order: entries e = 4*tid .. 4*tid+3 (256 digits x kSW
+    // waves = 4 per thread), digit e / kSW, wave e % kSW
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        c[q] = hist[hist_at<NT>(e / kSW, e % kSW)];
+        sum += c[q];
+    }
+    uint32_t ex = block_excl_scan<NT, false>(sh, sum, nullptr);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        hist[hist_at<NT>(e / kSW, e % kSW)] = ex;
+        ex += c[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        if (j < J) {
+            const uint32_t d = (k[j] >> shift) & 0xFFu;
+            sh.item[hist[hist_at<NT>(d, w)] + (il[j] >> 16)] = slot_word(k[j], (int)(il[j] & 0xFFFFu));
+        }
+    }
+    __syncthreads();
+}
+
+// The n slot words in sh.item sorted by four radix passes over their 32 key bits (the
+// flat ids below them ride along; the passes are stable and the words start in flat
+// order).  Pads up to a multiple of NT carry the largest key and sort last.
+template <int NT>
+__device__ __forceinline__ const uint64_t* radix_sort_words(SchedShared<NT>& sh, int n) {
+    const int n_pad = pad_slots<NT>(n);
+    for (int f = n + (int)threadIdx.x; f < n_pad; f += NT) sh.item[f] = ~0ull;
+    __syncthreads();
+#pragma unroll 1
+    for (int shift = 0; shift < 32; shift += 8) radix_pass<NT>(sh, n_pad, shift);
+    return sh.item;
+}
+
+// The n slot words ranked (see the file comment); run0 as in merge_sort_slots.
+template <int NT>
+__device__ __forceinline__ const uint64_t* rank_slots(SchedShared<NT>& sh, int n, int run0) {
+    return n <= 2 * NT ? merge_sort_slots<NT>(sh, n, run0) : radix_sort_words<NT>(sh, n);
 }
 
 template <int NT>
@@ -483,6 +572,12 @@ __device__ __forceinline__ int choose_budget_lds(SchedShared<NT>& sh, const uint
     constexpr int kNone = 0x7FFFFFFF;
     const int C = n_pad / NT;
     const int j0 = tid * C;
+    // this thread's cost-table entries (those past the prefetched ones requested now, so
+    // that their memory round trip overlaps the scan)
+    float vq[QM];
+#pragma unroll
+    for (int q = 0; q < QM; ++q)
+        vq[q] = (q < C && j0 + q <= bmax) ? (q < kCostPre ? cp.vc[q < kCostPre ? q : 0] : vcT[j0 + q]) : 0.f;
     U192 local = {0ull, 0ull, 0ull};
     for (int q = 0; q < C; ++q) {
         const int j = j0 + q;
@@ -528,7 +623,7 @@ __device__ __forceinline__ int choose_budget_lds(SchedShared<NT>& sh, const uint
     for (int q = 0; q < QM; ++q) {
         if (q < C) {
             const int B = j0 + q;
-            if (B <= bmax) take(B, eval(q < kCostPre ? cp.vc[q < kCostPre ? q : 0] : vcT[B]), true);
+            if (B <= bmax) take(B, eval(vq[q]), true);
             if (B < n) S = add192(S, fixed_from_bits(kOne - word_key(rk[B])));
         }
     }
@@ -678,7 +773,7 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
         CostPrefetch cp;
         if (sizing) prefetch_costs<NT>(cp, vc, dc, T, num_reqs, bm, m_pad);
         survival_to_lds<NT>(sh, src, rows, K, last ? surv_out : nullptr, status, tokens, last ? tok_lds : nullptr);
-        rk = merge_sort_slots<NT>(sh, m, K);  // each request's row is a sorted run
+        rk = rank_slots<NT>(sh, m, K);  // each request's row is a sorted run
         if (sizing) {
             if (last) write_ranking<NT>(rk, n, order, sorted_surv, nullptr);
             B = choose_budget_lds<NT>(sh, rk, cp, vc + T, m, m_pad, n_sampling, bm, sz.rule, last ? b_star : nullptr,
