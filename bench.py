@@ -610,7 +610,7 @@ def main():
     log(f"bench: event pass {KE} steps: {step_ms.mean() * 1e3:.1f} us/step "
         f"(chain {chain_ms.mean() * 1e3:.1f} us, after it {post_ms.mean() * 1e3:.1f} us)")
 
-    # Parity against the oracle (two sampled rows + the whole schedule) on steps 0, 1, 499
+    # Parity against the oracle (every chain row + the whole schedule) on steps 0, 1, 499
     # and the last of the timed sequence, each run again untimed (a step's result
     # depends only on its inputs, which cycle through the pool).
     import oracle
