@@ -346,7 +346,13 @@ int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dty
                                   draft_cost, bmax, sizing,    surv,       order,  sorted_surv, b_star,
                                   best_obj, prefix_len, offsets, ver_idx,   status, nullptr, 0,
                                   tokens,   ver_tokens};
-        e = dspark::launch_sched_fused(sa, s);
+        if (!stale && n <= dspark::kWideMaxN) {
+            // stages 2-5 over many workgroups (their counter and results in the workspace)
+            sa.ws = (uint64_t*)((char*)ws + dspark::ws_wide_off());
+            e = dspark::launch_sched_wide(sa, s);
+        } else {
+            e = dspark::launch_sched_fused(sa, s);
+        }
         return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (schedule)");
     }
     if (n > 0) {

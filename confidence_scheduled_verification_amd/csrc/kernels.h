@@ -13,6 +13,8 @@ namespace dspark {
 //   [0, ws_sync_bytes)   the single-launch step kernel's counters [K][kMaxGroups] and
 //                        ready flag (uint32), sized for the largest K so that the region
 //                        does not move with the shape;
+//   then ws_wide_bytes   the many-workgroup schedule's per-workgroup results and the
+//                        slots' ranks (fixed size, written before they are read);
 //   then                 the per-position argmax keys [K][R] (uint64) and the
 //                        persistent chain kernel's barrier counters [K][kMaxGroups].
 // The stage-wise paths zero the keys and counters they use first.  The step kernel
@@ -30,7 +32,14 @@ inline size_t ws_keys_bytes(int R, int K) { return ws_round((size_t)R * (size_t)
 inline size_t ws_bar_bytes(int K) { return ws_round((size_t)K * kMaxGroups * 4); }
 // Keys and chain counters: what the stage-wise paths clear.
 inline size_t ws_chain_bytes(int R, int K) { return ws_keys_bytes(R, K) + ws_bar_bytes(K); }
-inline size_t ws_chain_off() { return ws_sync_bytes(); }
+// The many-workgroup schedule (sched.hip): up to kWideMaxN slots, kWideSlots per workgroup.
+constexpr int kWideMaxN = 2048;
+constexpr int kWideSlots = 8;
+constexpr int kWideMaxGroups = kWideMaxN / kWideSlots;
+constexpr size_t kWidePartialBytes = 48;  // one workgroup's result
+inline size_t ws_wide_off() { return ws_sync_bytes(); }
+inline size_t ws_wide_bytes() { return ws_round((size_t)kWideMaxGroups * kWidePartialBytes + (size_t)kWideMaxN * 4); }
+inline size_t ws_chain_off() { return ws_sync_bytes() + ws_wide_bytes(); }
 inline size_t ws_total_bytes(int R, int K) { return ws_chain_off() + ws_chain_bytes(R, K); }
 
 // Probabilistic drafting: Gumbel-max sampling of softmax(x / temperature) with
@@ -192,6 +201,9 @@ hipError_t launch_allocate(const int32_t* order, const int32_t* b_star, int R, i
                            int32_t* prefix_len, int32_t* offsets, int32_t* ver_idx, int32_t* ver_tokens,
                            hipStream_t s);
 hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s);
+// Stages 2-5 over many workgroups, then one (sizing from the current confidences, R*K <=
+// kWideMaxN): a.ws is the workspace region at ws_wide_off().
+hipError_t launch_sched_wide(const FusedSchedArgs& a, hipStream_t s);
 hipError_t launch_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R,
                                 int K, int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens,
                                 uint32_t* status, hipStream_t s);
