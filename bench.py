@@ -269,9 +269,10 @@ def sampled_chain(w, B, pool, host_steps, ins, mk, ws, dev, steps) -> dict:
 
 
 def sched_kernel_us(B, pool, w, vc_d, dc_d, dev, calls) -> float:
-    """Stages 2-5 alone (dspark_schedule: one 1024-thread workgroup) on the pool's
-    confidences; mean microseconds per call.  Inside the single-launch step the same work
-    runs on a 512-thread workgroup beside the chain."""
+    """Stages 2-5 alone through dspark_schedule (one 1024-thread workgroup) on the pool's
+    confidences; mean microseconds per call.  The step itself runs them over many
+    workgroups when its slots allow (a ranking launch, then a one-workgroup finish), and
+    event_pass.after_chain_us times that part of the step."""
     import torch
     out = B.StepBuffers(w.R, w.K, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)

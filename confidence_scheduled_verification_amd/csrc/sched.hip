@@ -176,8 +176,12 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
     int32_t* rank_of = reinterpret_cast<int32_t*>(ws + (size_t)kWideMaxGroups * kWidePartialBytes);
 
     // survival of every slot (each thread one request at a time, eight confidences per
-    // memory round trip), and the cost-table entries B = 0 .. bmax
-    for (int j = tid; j <= bmax; j += kWT) sh.vc[j] = vc[T + j];
+    // memory round trip), and the cost-table entries B = 0 .. bmax, all requested before
+    // the first is used
+    constexpr int kVq = kWideMaxN / kWT + 1;
+    float vq[kVq];
+#pragma unroll
+    for (int u = 0; u < kVq; ++u) vq[u] = tid + u * kWT <= bmax ? vc[T + tid + u * kWT] : 0.f;
     const float dcost_f = dc[num_reqs];
     bool bad = false;
     for (int r = tid; r < R; r += kWT) {
@@ -204,6 +208,9 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
         }
     }
     if (bad && g == 0) raise_status(status, kStatusConfSanitized);
+#pragma unroll
+    for (int u = 0; u < kVq; ++u)
+        if (tid + u * kWT <= bmax) sh.vc[tid + u * kWT] = vq[u];
     __syncthreads();
 
     // this workgroup's slots: thread (el, pt) counts slot 8g + el over words [y0, y1)
@@ -328,9 +335,17 @@ __global__ __launch_bounds__(kWT) void sched_finish_kernel(
     __shared__ int s_b[kWT / 64], s_d[kWT / 64];
     __shared__ double s_fdrop, s_fbmax;
     __shared__ uint32_t s_wsum[kWT / 64];
-    // each request's count of selected slots needs B, so its ranks are requested first
     const int CR = (R + kWT - 1) / kWT;
     const int r0 = tid * CR;
+    // With one request per thread and K <= 8, its ranks and draft tokens are requested
+    // with the workgroups' candidates, in the same memory round trip.
+    const bool pre = CR == 1 && K <= 8 && r0 < R;
+    int32_t rk8[8], tk8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        rk8[u] = pre && u < K ? rank_of[r0 * K + u] : kNone;
+        tk8[u] = pre && u < K && ver_tokens ? tokens[r0 * K + u] : 0;
+    }
     // the budget from every workgroup's candidates
     WidePartial q = tid < G ? parts[tid] : no_partial();
     const double Fw = wave_max_f64(q.f);
@@ -370,10 +385,15 @@ __global__ __launch_bounds__(kWT) void sched_finish_kernel(
     // the allocation: a request's selected slots are its first ones (its ranks rise
     // along its positions), so its prefix length counts its ranks below B
     uint32_t cnt = 0u;
-    for (int e = 0; e < CR; ++e) {
-        const int r = r0 + e;
-        if (r < R)
-            for (int i = 0; i < K; ++i) cnt += rank_of[r * K + i] < B ? 1u : 0u;
+    if (pre) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cnt += rk8[u] < B ? 1u : 0u;
+    } else {
+        for (int e = 0; e < CR; ++e) {
+            const int r = r0 + e;
+            if (r < R)
+                for (int i = 0; i < K; ++i) cnt += rank_of[r * K + i] < B ? 1u : 0u;
+        }
     }
     const uint32_t x = wave_incl_scan_u32(cnt);
     if (lane == 63) s_wsum[w] = x;
@@ -383,18 +403,30 @@ __global__ __launch_bounds__(kWT) void sched_finish_kernel(
         if (e < w) o += s_wsum[e];
         total += s_wsum[e];
     }
-    for (int e = 0; e < CR; ++e) {
-        const int r = r0 + e;
-        if (r >= R) break;
-        uint32_t L = 0;
-        for (int i = 0; i < K; ++i) L += rank_of[r * K + i] < B ? 1u : 0u;
-        offsets[r] = (int32_t)o;
-        prefix_len[r] = (int32_t)L;
-        for (uint32_t i = 0; i < L; ++i) {
-            ver_idx[o + i] = r * K + (int)i;
-            if (ver_tokens) ver_tokens[o + i] = tokens[r * K + (int)i];
+    if (pre) {
+        offsets[r0] = (int32_t)o;
+        prefix_len[r0] = (int32_t)cnt;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if ((uint32_t)u < cnt) {
+                ver_idx[o + u] = r0 * K + u;
+                if (ver_tokens) ver_tokens[o + u] = tk8[u];
+            }
         }
-        o += L;
+    } else {
+        for (int e = 0; e < CR; ++e) {
+            const int r = r0 + e;
+            if (r >= R) break;
+            uint32_t L = 0;
+            for (int i = 0; i < K; ++i) L += rank_of[r * K + i] < B ? 1u : 0u;
+            offsets[r] = (int32_t)o;
+            prefix_len[r] = (int32_t)L;
+            for (uint32_t i = 0; i < L; ++i) {
+                ver_idx[o + i] = r * K + (int)i;
+                if (ver_tokens) ver_tokens[o + i] = tokens[r * K + (int)i];
+            }
+            o += L;
+        }
     }
     if (tid == 0) offsets[R] = (int32_t)total;
     for (int j = B + tid; j < n; j += kWT) {
