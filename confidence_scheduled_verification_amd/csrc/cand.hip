@@ -31,12 +31,14 @@
 // is ceil(V/4096) items); a wave takes the next item from an LDS counter whenever it
 // starts a load, keeps the next two items' loads in flight, and never waits for the
 // other waves.  For each item it folds the item's maximum into the row's maximum in LDS
-// and keeps the entries that clear the floor of the row's maximum seen so far (a lower
-// bound of the final one, so nothing that can win is dropped), with one directory word
-// for the item, in its part of the LDS; then it counts the item into its row.
+// and appends the entries that clear the floor of the row's maximum seen so far (a lower
+// bound of the final one, so nothing that can win is dropped) to the row's part of the
+// LDS store, claiming their places with the row's LDS counter; then it counts the item
+// into its row.
 //
 // Chain (wave 7), concurrently.  Position by position it waits for the row's count to
-// reach its item count, lists the kept entries that clear the row's final floor, and
+// reach its item count, lists the row's kept entries (contiguous in its part of the
+// store) that clear the row's final floor, and
 // scores them with the key row of the previous token, two lanes per candidate with the
 // whole Bt rows of up to 64 candidates in flight at once (x = value + the dot product,
 // each lane's half by fused multiply-adds in increasing k, then the halves added).  The
@@ -54,17 +56,15 @@ namespace {
 constexpr int kQS = 7;                   // streaming waves (with the chain wave, two waves per SIMD)
 constexpr int kQT = (kQS + 1) * 64;      // threads per workgroup: the streaming waves and the chain wave
 constexpr int kQItem = kCandItem;        // base entries per item: 64 lanes x 8 loads x 8 entries
-constexpr int kQStage = kCandWaveStage;  // entries a streaming wave keeps for its items of one request
+constexpr int kQStore = kCandStore;     // kept entries in LDS per request, row i's in [i cap, (i + 1) cap), cap = kQStore / K
 constexpr int kQList = 256;              // candidates the chain wave lists at once
-constexpr uint32_t kQOverflow = 0xFFFFFFFFu;
 constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
 constexpr long kQSpinLimit = 1L << 26;   // polls (with a short sleep each) before the chain wave gives up
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-static_assert(kCandMaxK * kCandMaxItems <= 2048, "a request's directory fits the LDS array");
-static_assert(kQS * kQStage < (1 << 16), "LDS slots fit the directory word");
+static_assert(kQStore >= kCandMaxK * 64, "every row's part of the store holds a wave's worth of entries");
 
 // Order-preserving image of a float in the unsigned integers (NaN above every number,
 // -0 equal to +0); never 0.
@@ -148,19 +148,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     return x;
 }
 
-// Exclusive prefix sum over the wave; *total receives the sum.
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
-    const int lane = threadIdx.x & 63;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    *total = __shfl(x, 63, 64);
-    return x - v;
-}
-
 // LDS written by some lanes of a wave and read by others: the writes come first.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -183,9 +170,9 @@ __device__ __forceinline__ HeaderView header_view(const void* hdr) {
 
 // LDS of one request.
 struct QLds {
-    uint64_t stage[kQS * kQStage];           // kept entries, wave w's in [w kQStage, (w + 1) kQStage): (index << 32) | value bits
-    uint64_t dir[kCandMaxK * kCandMaxItems]; // per item: (first slot << 32) | count (kQOverflow: no room)
-    uint32_t pfx[kCandMaxK * kCandMaxItems]; // per item: prefix of its row's counts (written by the chain wave)
+    uint64_t stage[kQStore];                 // kept entries, row i's in [i cap, (i + 1) cap): (index << 32) | value bits
+    uint32_t rowfill[kCandMaxK];             // places claimed in each row's part of the store
+    uint32_t rowover[kCandMaxK];             // 1: a row's part overflowed (the row is scored densely)
     uint64_t clist[kQList];                  // the chain wave's listed candidates
     uint16_t akey[256];                      // key row of a densely scored row
     uint32_t rowmax[kCandMaxK];              // the rows' maxima so far (order-preserving image; 0 = none yet)
@@ -275,11 +262,10 @@ __device__ __forceinline__ float entry_of(const u32x4& word4, int t) {
 
 // One item of a streaming wave (see the file comment): the item's maximum into its row's
 // (or its first NaN into the row's mark), its entries that clear the floor of the row's
-// maximum so far -- in entry order, from slot w kQStage + used -- and its directory
-// word; then the item is counted into its row.  -inf never wins unless the whole row is
-// -inf, which is handled apart, so it is never kept.
-__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j, int i, int v0, uint32_t& used,
-                                          float ab2) {
+// maximum so far -- in entry order, at places claimed in row i's part of the store, which
+// holds cap entries -- and then the item is counted into its row.  -inf never wins unless
+// the whole row is -inf, which is handled apart, so it is never kept.
+__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, uint32_t cap, float ab2) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     constexpr float kNegInf = -__builtin_huge_valf();
     float gm[8];
@@ -288,8 +274,6 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
 #pragma unroll
     for (int q = 1; q < 8; ++q) m = __builtin_elementwise_maximum(m, gm[q]);
     const float mw = wave_max(m);
-    uint32_t count = 0;
-    const uint32_t first_slot = (uint32_t)(w * kQStage) + used;
     if (mw != mw) {
         // the row's token is its first NaN, whatever the bias
         uint32_t first = 0xFFFFFFFFu;
@@ -330,8 +314,12 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
         uint32_t total = 0;
         const uint32_t before = wave_excl_scan_small(c, &total);
         if (total != 0u) {
-            if (used + total <= (uint32_t)kQStage) {
-                uint32_t slot = first_slot + before;
+            uint32_t at = 0u;
+            if (lane == 0)
+                at = __hip_atomic_fetch_add(&L.rowfill[i], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            at = __builtin_amdgcn_readfirstlane(at);
+            if (at + total <= cap) {
+                uint32_t slot = (uint32_t)i * cap + at + before;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     if (__ballot(gmask[q] != 0u) == 0ull) continue;
@@ -345,14 +333,11 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
                         L.stage[slot++] = ((uint64_t)v << 32) | bits;
                     }
                 }
-                count = total;
-                used += total;
-            } else {
-                count = kQOverflow;  // no room: the row is scored densely
+            } else if (lane == 0) {
+                L.rowover[i] = 1u;  // no room: the row is scored densely
             }
         }
     }
-    if (lane == 0) L.dir[j] = ((uint64_t)first_slot << 32) | count;
     lds_writes_done();
     if (lane == 0) __hip_atomic_fetch_add(&L.rowdone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -365,7 +350,7 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int j,
 // entry reads as -inf).
 template <bool VEC>
 __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int per_req, int NC, int V, float ab2) {
-    uint32_t used = 0;
+    const uint32_t cap = (uint32_t)kQStore / (uint32_t)(per_req / NC);  // entries per row's part
     auto claim = [&]() -> int {
         uint32_t j = 0u;
         if ((threadIdx.x & 63) == 0) j = atomicAdd(&L.next, 1u);
@@ -378,7 +363,7 @@ __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int
     auto take = [&](const u32x4 (&buf)[8], int j) {
         if (j < per_req) {
             const int i = j / NC;
-            keep_item(L, buf, j, i, (j - i * NC) * kQItem, used, ab2);
+            keep_item(L, buf, i, (j - i * NC) * kQItem, cap, ab2);
         }
     };
     if (VEC) {
@@ -420,19 +405,6 @@ __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int
 __device__ __forceinline__ u32x2 row_quad(const uint16_t* __restrict__ M, int u, int rank) {
     const int lane = threadIdx.x & 63;
     return 4 * lane < rank ? *(const u32x2*)(M + (size_t)u * rank + 4 * lane) : u32x2{0u, 0u};
-}
-
-// Kept entry e (< the row's count) of row i: the item holding it is the last whose
-// prefix is <= e.
-__device__ __forceinline__ uint64_t kept_entry(const QLds& L, int i, int NC, uint32_t e) {
-    int lo = 0, hi = NC - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (L.pfx[i * NC + mid] <= e) lo = mid;
-        else hi = mid - 1;
-    }
-    const uint32_t slot = (uint32_t)(L.dir[i * NC + lo] >> 32) + (e - L.pfx[i * NC + lo]);
-    return L.stage[slot < (uint32_t)(kQS * kQStage) ? slot : 0u];
 }
 
 // Candidates are scored two lanes each: lane pair (2c, 2c+1) takes candidate c, the even
@@ -527,6 +499,7 @@ __device__ __forceinline__ float key_norm_up(const u32x2& key) {
 __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, float ab2, float b1, bool bound_ok) {
     const int lane = threadIdx.x & 63;
     const int K = a.K, NC = a.NC, V = a.V, rank = a.rank;
+    const uint32_t cap = (uint32_t)kQStore / (uint32_t)K;  // entries per row's part of the store
     const long row0 = (long)r * K;
     constexpr float kNegInf = -__builtin_huge_valf();
     int prev = a.prev0[r];
@@ -546,19 +519,10 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
             __builtin_amdgcn_s_sleep(1);
         }
         asm volatile("" ::: "memory");
-        // the row's directory: counts, their prefix, overflow
-        uint32_t cnt = 0;
-        bool ov = false;
-        if (lane < NC) {
-            cnt = (uint32_t)L.dir[i * NC + lane];
-            ov = cnt == kQOverflow;
-        }
-        const bool over = __ballot(ov) != 0ull;
-        if (over) cnt = 0;
-        uint32_t total = 0;
-        const uint32_t pre = wave_excl_scan(cnt, &total);
-        if (lane < NC) L.pfx[i * NC + lane] = pre;
-        wave_lds_sync();
+        // the row's kept entries: [i cap, i cap + total) of the store, unless it overflowed
+        const bool over = L.rowover[i] != 0u;
+        const uint32_t total = over ? 0u : L.rowfill[i];
+        const uint64_t* kept = L.stage + (size_t)i * cap;
         if (4 * lane < rank) *(u32x2*)(L.akey + 4 * lane) = key;  // this position's key row, for every lane
         wave_lds_sync();
         const uint32_t nk = L.rownan[i];
@@ -586,7 +550,7 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
             bool prefetched = false;
             for (uint32_t e0 = 0; e0 < total; e0 += 64) {
                 const uint32_t e = e0 + lane;
-                const uint64_t ent = e < total ? kept_entry(L, i, NC, e) : 0ull;
+                const uint64_t ent = e < total ? kept[e] : 0ull;
                 const bool ok = e < total && __uint_as_float((uint32_t)ent) >= fl;
                 const uint64_t bal = __ballot(ok);
                 if (ok) {
@@ -628,6 +592,8 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
             S.rowmax[threadIdx.x] = 0u;
             S.rownan[threadIdx.x] = 0u;
             S.rowdone[threadIdx.x] = 0u;
+            S.rowfill[threadIdx.x] = 0u;
+            S.rowover[threadIdx.x] = 0u;
         }
         if (threadIdx.x == 0) S.next = 0u;
         __syncthreads();

@@ -144,11 +144,11 @@ struct StepArgs {
 };
 
 // Candidate-pruned chain (cand.hip).  Limits of that path: K <= kCandMaxK positions and
-// V <= kCandMaxItems * 4096 entries per row (its per-request directory lives in LDS).
+// V <= kCandMaxItems * 4096 entries per row.
 constexpr int kCandMaxK = 32;
 constexpr int kCandMaxItems = 64;
 constexpr int kCandItem = 4096;           // base entries per streaming item
-constexpr int kCandWaveStage = 1024;      // entries a streaming wave keeps in LDS for one request
+constexpr int kCandStore = 16384;         // kept entries a request's LDS holds, split evenly among its rows
 constexpr int kCandMaxGroups = 256;       // workgroups of one launch at most
 constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, then Bt
 
