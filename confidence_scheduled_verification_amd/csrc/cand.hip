@@ -20,8 +20,8 @@
 // argmax of fl32(base + fl32 dot).  Where the bound cannot prune, the row is scored over
 // the whole vocabulary, so the result never depends on the data: a NaN in the row makes
 // the first NaN the token (the bias is finite whenever the bound is, so x is NaN exactly
-// where base is); a row of -inf gives 0; a row whose candidates overflow a buffer, or
-// weights whose bound is not finite, are scored densely.
+// where base is); a row of -inf gives 0; a row whose kept groups do not fit the LDS
+// pool, or weights whose bound is not finite, are scored densely.
 //
 // One workgroup per compute unit takes requests g, g + G, ... whole, so a request's
 // candidates never leave the compute unit's LDS.  Its eight waves (two per SIMD) split
@@ -29,17 +29,18 @@
 //
 // Streaming (waves 0-6).  The request's K*V base entries are items of 4096 entries (a row
 // is ceil(V/4096) items); a wave takes the next item from an LDS counter whenever it
-// starts a load, keeps the next two items' loads in flight, and never waits for the
-// other waves.  For each item it folds the item's maximum into the row's maximum in LDS
-// and appends the entries that clear the floor of the row's maximum seen so far (a lower
-// bound of the final one, so nothing that can win is dropped) to the row's part of the
-// LDS store, claiming their places with the row's LDS counter; then it counts the item
-// into its row.
+// starts a load, keeps the next item's loads in flight, and never waits for the other
+// waves.  For each item it folds the item's maximum into the row's maximum in LDS
+// and keeps, whole, every 8-entry group whose maximum clears the floor of the row's
+// maximum seen so far (a lower bound of the final one, so nothing that can win is
+// dropped): no entry is tested on its own here.  A row's kept groups are numbered by an
+// LDS counter and stored in 64-group chunks of a per-request LDS pool, which the wave
+// that claims a chunk's first place takes from the pool; then the item is counted into
+// its row.
 //
 // Chain (wave 7), concurrently.  Position by position it waits for the row's count to
-// reach its item count, lists the row's kept entries (contiguous in its part of the
-// store) that clear the row's final floor, and
-// scores them with the key row of the previous token, two lanes per candidate with the
+// reach its item count, lists the entries of the row's kept groups that clear the row's
+// final floor, and scores them with the key row of the previous token, two lanes per candidate with the
 // whole Bt rows of up to 64 candidates in flight at once (x = value + the dot product,
 // each lane's half by fused multiply-adds in increasing k, then the halves added).  The
 // key row of the next position is prefetched for the row's largest entry -- the token
@@ -56,15 +57,20 @@ namespace {
 constexpr int kQS = 7;                   // streaming waves (with the chain wave, two waves per SIMD)
 constexpr int kQT = (kQS + 1) * 64;      // threads per workgroup: the streaming waves and the chain wave
 constexpr int kQItem = kCandItem;        // base entries per item: 64 lanes x 8 loads x 8 entries
-constexpr int kQStore = kCandStore;     // kept entries in LDS per request, row i's in [i cap, (i + 1) cap), cap = kQStore / K
-constexpr int kQList = 256;              // candidates the chain wave lists at once
+constexpr int kQChunk = 64;              // kept groups per chunk of the pool
+constexpr int kQChunks = kCandGroups / kQChunk;  // chunks of the pool
+constexpr uint8_t kQUnset = 0xFF;        // chunk table: not taken yet
+constexpr uint8_t kQNone = 0xFE;         // chunk table: the pool was empty (the row is scored densely)
+constexpr int kQList = 768;              // candidates the chain wave lists at once (256 + 64 groups' 512 at most)
+constexpr int kQGList = 256;             // kept groups the chain wave lists at once
 constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
 constexpr long kQSpinLimit = 1L << 26;   // polls (with a short sleep each) before the chain wave gives up
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-static_assert(kQStore >= kCandMaxK * 64, "every row's part of the store holds a wave's worth of entries");
+static_assert(kQChunks <= 0xFE, "chunk numbers fit a byte beside the two marks");
+static_assert((long)kCandMaxItems * kQItem / 8 <= 65536, "group numbers within a row fit 16 bits");
 
 // Order-preserving image of a float in the unsigned integers (NaN above every number,
 // -0 equal to +0); never 0.
@@ -100,6 +106,24 @@ __device__ __forceinline__ float dpp_f32(float x, int ctrl) {
         case kDppHalfMirror:
             return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppHalfMirror, 0xF, 0xF, false));
         default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppMirror, 0xF, 0xF, false));
+    }
+}
+
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x, int ctrl) {
+    const uint32_t lo = __float_as_uint(dpp_f32(__uint_as_float((uint32_t)x), ctrl));
+    const uint32_t hi = __float_as_uint(dpp_f32(__uint_as_float((uint32_t)(x >> 32)), ctrl));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t pack_u64(int hi, int lo) { return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo; }
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+    const int hi = (int)(x >> 32), lo = (int)x;
+    switch (lane) {  // the lane must be a constant of the builtin
+        case 0: return pack_u64(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(lo, 0));
+        case 16: return pack_u64(__builtin_amdgcn_readlane(hi, 16), __builtin_amdgcn_readlane(lo, 16));
+        case 32: return pack_u64(__builtin_amdgcn_readlane(hi, 32), __builtin_amdgcn_readlane(lo, 32));
+        default: return pack_u64(__builtin_amdgcn_readlane(hi, 48), __builtin_amdgcn_readlane(lo, 48));
     }
 }
 
@@ -142,10 +166,13 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
     return x;
 }
 
+// The largest key over the wave (every lane active), the same in every lane: as wave_max.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = umax64(x, shfl_xor_u64(x, o));
-    return x;
+    x = umax64(x, dpp_u64(x, kDppXor1));
+    x = umax64(x, dpp_u64(x, kDppXor2));
+    x = umax64(x, dpp_u64(x, kDppHalfMirror));
+    x = umax64(x, dpp_u64(x, kDppMirror));
+    return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
 }
 
 // LDS written by some lanes of a wave and read by others: the writes come first.
@@ -170,10 +197,14 @@ __device__ __forceinline__ HeaderView header_view(const void* hdr) {
 
 // LDS of one request.
 struct QLds {
-    uint64_t stage[kQStore];                 // kept entries, row i's in [i cap, (i + 1) cap): (index << 32) | value bits
-    uint32_t rowfill[kCandMaxK];             // places claimed in each row's part of the store
-    uint32_t rowover[kCandMaxK];             // 1: a row's part overflowed (the row is scored densely)
+    u32x4 grp[kCandGroups];                  // kept 8-entry groups (bf16), in chunks of kQChunk
+    uint16_t gid[kCandGroups];               // their group numbers within the row (first entry / 8)
+    uint8_t ctab[kCandMaxK][kQChunks];       // per row: pool chunk of each of its chunks (kQUnset, kQNone)
+    uint32_t rowfill[kCandMaxK];             // groups each row has kept (places claimed)
+    uint32_t rowover[kCandMaxK];             // 1: some of a row's groups found no chunk (the row is scored densely)
+    uint32_t pool;                           // chunks taken from the pool
     uint64_t clist[kQList];                  // the chain wave's listed candidates
+    uint16_t glist[kQGList];                 // the chain wave's listed groups (their places in the pool)
     uint16_t akey[256];                      // key row of a densely scored row
     uint32_t rowmax[kCandMaxK];              // the rows' maxima so far (order-preserving image; 0 = none yet)
     uint32_t rownan[kCandMaxK];              // ~(first NaN index), 0 = none
@@ -231,26 +262,6 @@ __device__ __forceinline__ void group_maxima(const u32x4 (&cur)[8], float (&gm)[
     }
 }
 
-// Word d (0..3, not a constant) of a 16-byte group, by selects.
-__device__ __forceinline__ uint32_t pick_word(const u32x4& g, int d) {
-    const uint32_t lo = (d & 1) ? g[1] : g[0];
-    const uint32_t hi = (d & 1) ? g[3] : g[2];
-    return (d & 2) ? hi : lo;
-}
-
-// Bit t of the result: entry t (0..7) of 16-byte group `g` is >= fl and above -inf.
-__device__ __forceinline__ uint32_t pass_mask(const u32x4& g, float fl) {
-    constexpr float kNegInf = -__builtin_huge_valf();
-    uint32_t mk = 0u;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float lo = __uint_as_float(g[d] << 16), hi = __uint_as_float(g[d] & 0xFFFF0000u);
-        mk |= (lo >= fl && lo > kNegInf) ? (1u << (2 * d)) : 0u;
-        mk |= (hi >= fl && hi > kNegInf) ? (2u << (2 * d)) : 0u;
-    }
-    return mk;
-}
-
 // Entry t (0..7) of 16-byte group `word4` as a float.  The word goes through an empty asm
 // statement first, so the compiler recomputes the unpacking where it is used instead of
 // keeping all 64 unpacked entries of an item live across the passes over it.
@@ -260,13 +271,35 @@ __device__ __forceinline__ float entry_of(const u32x4& word4, int t) {
     return __uint_as_float((t & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
+// Pool chunks for row i's kept-group places [at, at + n), just claimed by this wave.  The
+// chunks whose first place lies in the range are this wave's to take (a lane each); the
+// chunk holding `at`, when `at` is not its first place, is taken by the wave that claimed
+// that first place -- an earlier claim, whose wave takes its chunks straight after it --
+// and is waited for.  A chunk past the table, or not found, reads as none.
+__device__ __forceinline__ void take_chunks(QLds& L, int i, uint32_t at, uint32_t n) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t c0 = at / kQChunk, c1 = (at + n - 1u) / kQChunk;
+    const uint32_t first = (at % kQChunk == 0u) ? c0 : c0 + 1u;
+    const uint32_t c = first + (uint32_t)lane;  // n <= 512: at most 9 chunks
+    if (c <= c1 && c < (uint32_t)kQChunks) {
+        const uint32_t id = __hip_atomic_fetch_add(&L.pool, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        L.ctab[i][c] = id < (uint32_t)kQChunks ? (uint8_t)id : kQNone;
+    }
+    if (first != c0 && c0 < (uint32_t)kQChunks && lane == 0) {
+        const volatile uint8_t* t = &L.ctab[i][c0];
+        for (long n_polls = 0; *t == kQUnset && n_polls < kQSpinLimit; ++n_polls) __builtin_amdgcn_s_sleep(1);
+    }
+    wave_lds_sync();
+}
+
 // One item of a streaming wave (see the file comment): the item's maximum into its row's
-// (or its first NaN into the row's mark), its entries that clear the floor of the row's
-// maximum so far -- in entry order, at places claimed in row i's part of the store, which
-// holds cap entries -- and then the item is counted into its row.  -inf never wins unless
-// the whole row is -inf, which is handled apart, so it is never kept.
-__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, uint32_t cap, float ab2) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// (or its first NaN into the row's mark), then every 8-entry group of the item whose
+// maximum clears the floor of the row's maximum so far, kept whole with its group number
+// at places claimed in row i's chunks; then the item is counted into its row.  A group of
+// -inf entries never wins unless the whole row is -inf, which is handled apart, so it is
+// never kept.
+__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, float ab2) {
+    const int lane = threadIdx.x & 63;
     constexpr float kNegInf = -__builtin_huge_valf();
     float gm[8];
     group_maxima(cur, gm);
@@ -295,47 +328,40 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i,
         seen = __builtin_amdgcn_readfirstlane(seen);
         const uint32_t now = seen > ord32(mw) ? seen : ord32(mw);
         const float fl = cand_floor(unord32(now), ab2);
-        // per 8-entry group, a mask of this lane's entries that clear the floor; groups
-        // no lane needs are skipped by the whole wave
-        uint32_t gmask[8];
-        uint32_t c = 0;
+        uint32_t need = 0u;  // bit q: group q of this lane is kept
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const bool need = gm[q] >= fl && gm[q] > kNegInf;
-            uint32_t mk = 0u;
-            if (need) {
-                // (a branch, not a select: a group that no lane needs is skipped by the wave)
-                asm volatile("");
-                mk = pass_mask(cur[q], fl);
-            }
-            gmask[q] = mk;
-            c += (uint32_t)__builtin_popcount(mk);
-        }
+        for (int q = 0; q < 8; ++q) need |= (gm[q] >= fl && gm[q] > kNegInf) ? (1u << q) : 0u;
         uint32_t total = 0;
-        const uint32_t before = wave_excl_scan_small(c, &total);
+        const uint32_t before = wave_excl_scan_small((uint32_t)__builtin_popcount(need), &total);
         if (total != 0u) {
             uint32_t at = 0u;
             if (lane == 0)
                 at = __hip_atomic_fetch_add(&L.rowfill[i], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             at = __builtin_amdgcn_readfirstlane(at);
-            if (at + total <= cap) {
-                uint32_t slot = (uint32_t)i * cap + at + before;
+            take_chunks(L, i, at, total);
+            // this lane's places [p, p + popcount(need)) lie in chunk ca or the next
+            uint32_t p = at + before;
+            const uint32_t ca = p / kQChunk;
+            const uint32_t ida = ca < (uint32_t)kQChunks ? (uint32_t)L.ctab[i][ca] : (uint32_t)kQNone;
+            const uint32_t idb = ca + 1u < (uint32_t)kQChunks ? (uint32_t)L.ctab[i][ca + 1u] : (uint32_t)kQNone;
+            const uint32_t g0 = ((uint32_t)v0 >> 3) + (uint32_t)lane;
+            bool lost = false;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (__ballot(gmask[q] != 0u) == 0ull) continue;
-                    uint32_t mk = gmask[q];
-                    while (mk != 0u) {
-                        const int t = __builtin_ctz(mk);
-                        mk &= mk - 1u;
-                        const uint32_t word = pick_word(cur[q], t >> 1);
-                        const uint32_t bits = (t & 1) ? (word & 0xFFFF0000u) : (word << 16);
-                        const uint32_t v = (uint32_t)(v0 + q * 512 + lane * 8 + t);
-                        L.stage[slot++] = ((uint64_t)v << 32) | bits;
+            for (int q = 0; q < 8; ++q) {
+                if (__ballot((need >> q) & 1u) == 0ull) continue;
+                if ((need >> q) & 1u) {
+                    const uint32_t id = p / kQChunk == ca ? ida : idb;
+                    if (id < (uint32_t)kQChunks) {
+                        const uint32_t slot = id * kQChunk + p % kQChunk;
+                        L.grp[slot] = cur[q];
+                        L.gid[slot] = (uint16_t)(g0 + (uint32_t)q * 64u);
+                    } else {
+                        lost = true;
                     }
+                    ++p;
                 }
-            } else if (lane == 0) {
-                L.rowover[i] = 1u;  // no room: the row is scored densely
             }
+            if (__ballot(lost) != 0ull && lane == 0) L.rowover[i] = 1u;  // the row is scored densely
         }
     }
     lds_writes_done();
@@ -345,12 +371,10 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i,
 // A streaming wave's items of one request: it takes the next item from the workgroup's
 // counter whenever it starts loading one, so that waves which happen to be served faster
 // take more, and items are taken in order (rows complete in order).  Each item is loaded
-// two items ahead (three buffers in turn, so no item waits for another's loads; one
-// ahead with element-wise loads).  An item past the request loads nothing (v0 = V: every
-// entry reads as -inf).
+// one item ahead (two buffers in turn).  An item past the request loads nothing (v0 = V:
+// every entry reads as -inf).
 template <bool VEC>
 __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int per_req, int NC, int V, float ab2) {
-    const uint32_t cap = (uint32_t)kQStore / (uint32_t)(per_req / NC);  // entries per row's part
     auto claim = [&]() -> int {
         uint32_t j = 0u;
         if ((threadIdx.x & 63) == 0) j = atomicAdd(&L.next, 1u);
@@ -363,38 +387,21 @@ __device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int
     auto take = [&](const u32x4 (&buf)[8], int j) {
         if (j < per_req) {
             const int i = j / NC;
-            keep_item(L, buf, i, (j - i * NC) * kQItem, cap, ab2);
+            keep_item(L, buf, i, (j - i * NC) * kQItem, ab2);
         }
     };
-    if (VEC) {
-        u32x4 b0[8], b1[8], b2[8];
-        int j0 = claim(), j1 = claim(), j2;
-        issue(b0, j0);
+    // (one item ahead already reads at the device's rate, and the chain wave's own loads
+    // then queue behind fewer of the streams' than with two)
+    u32x4 b0[8], b1[8];
+    int j0 = claim(), j1;
+    issue(b0, j0);
+    while (j0 < per_req) {
+        j1 = claim();
         issue(b1, j1);
-        while (j0 < per_req) {
-            j2 = claim();
-            issue(b2, j2);
-            take(b0, j0);
-            j0 = claim();
-            issue(b0, j0);
-            take(b1, j1);
-            j1 = claim();
-            issue(b1, j1);
-            take(b2, j2);
-        }
-    } else {
-        // element-wise loads take more registers: one item ahead
-        u32x4 b0[8], b1[8];
-        int j0 = claim(), j1;
+        take(b0, j0);
+        j0 = claim();
         issue(b0, j0);
-        while (j0 < per_req) {
-            j1 = claim();
-            issue(b1, j1);
-            take(b0, j0);
-            j0 = claim();
-            issue(b0, j0);
-            take(b1, j1);
-        }
+        take(b1, j1);
     }
 }
 
@@ -438,7 +445,7 @@ __device__ __forceinline__ float pair_x(const QLds& L, const u32x4 (&bt)[kQHalf]
             }
         }
     }
-    const float other = __shfl_xor(acc, 1, 64);
+    const float other = dpp_f32(acc, kDppXor1);  // the pair's other lane
     return value + (half ? other + acc : acc + other);
 }
 
@@ -490,8 +497,15 @@ __device__ __forceinline__ float key_norm_up(const u32x2& key) {
         s = __builtin_fmaf(lo, lo, s);
         s = __builtin_fmaf(hi, hi, s);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+    // the sum over the wave, within rows of 16 by lane moves and then over the four rows
+    s += dpp_f32(s, kDppXor1);
+    s += dpp_f32(s, kDppXor2);
+    s += dpp_f32(s, kDppHalfMirror);
+    s += dpp_f32(s, kDppMirror);
+    s = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16))) +
+        (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48)));
     return __builtin_sqrtf(s) * (1.0f + 0x1p-12f);
 }
 
@@ -499,7 +513,6 @@ __device__ __forceinline__ float key_norm_up(const u32x2& key) {
 __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, float ab2, float b1, bool bound_ok) {
     const int lane = threadIdx.x & 63;
     const int K = a.K, NC = a.NC, V = a.V, rank = a.rank;
-    const uint32_t cap = (uint32_t)kQStore / (uint32_t)K;  // entries per row's part of the store
     const long row0 = (long)r * K;
     constexpr float kNegInf = -__builtin_huge_valf();
     int prev = a.prev0[r];
@@ -519,26 +532,21 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
             __builtin_amdgcn_s_sleep(1);
         }
         asm volatile("" ::: "memory");
-        // the row's kept entries: [i cap, i cap + total) of the store, unless it overflowed
+        // the row's kept groups: places [0, total) of its chunks, unless some found no chunk
         const bool over = L.rowover[i] != 0u;
         const uint32_t total = over ? 0u : L.rowfill[i];
-        const uint64_t* kept = L.stage + (size_t)i * cap;
         if (4 * lane < rank) *(u32x2*)(L.akey + 4 * lane) = key;  // this position's key row, for every lane
         wave_lds_sync();
         const uint32_t nk = L.rownan[i];
         const float M = unord32(L.rowmax[i]);
         // (a row of candidates always keeps its maximum; an empty one is scored densely all the same)
-        const int kind = nk ? 1 : (M == kNegInf ? 2 : ((!bound_ok || over || total == 0) ? 3 : 0));
-        int tok;
+        int kind = nk ? 1 : (M == kNegInf ? 2 : ((!bound_ok || over || total == 0) ? 3 : 0));
+        int tok = 0;  // (kind 2)
         u32x2 next_key{0u, 0u};
         bool have_next = false;
         if (kind == 1) {
             tok = (int)~nk;
-        } else if (kind == 2) {
-            tok = 0;
-        } else if (kind == 3) {
-            tok = key_index(dense_row(L, a.base + (size_t)(row0 + i) * (size_t)V, V, a.Bt, rank));
-        } else {
+        } else if (kind == 0) {
             // list the kept entries that clear the final floor, score them in lists of
             // at most kQList; note the largest (the likely token)
             // Once the position's key row is known, every bias is at most |key| b in size, so
@@ -546,35 +554,80 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
             const float ab2_key = 2.0f * key_norm_up(key) * b1 * (1.0f + 0x1p-20f);
             const float fl = cand_floor(M, ab2_key < ab2 ? ab2_key : ab2);
             uint64_t best = 0ull, top = 0ull;
-            uint32_t n = 0;
-            bool prefetched = false;
-            for (uint32_t e0 = 0; e0 < total; e0 += 64) {
-                const uint32_t e = e0 + lane;
-                const uint64_t ent = e < total ? kept[e] : 0ull;
-                const bool ok = e < total && __uint_as_float((uint32_t)ent) >= fl;
-                const uint64_t bal = __ballot(ok);
-                if (ok) {
-                    L.clist[n + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] = ent;
-                    top = umax64(top, argmax_key(__uint_as_float((uint32_t)ent), (uint32_t)(ent >> 32)));
+            uint32_t n = 0, ng = 0;
+            // The groups whose maximum clears the floor, a lane per kept group and a chunk at
+            // a time, are listed; then, a lane per listed group, their entries that clear it,
+            // which are scored once more than 256 are listed.
+            for (uint32_t e0 = 0; e0 < total; e0 += kQChunk) {
+                const uint32_t slot = (L.ctab[i][e0 / kQChunk] % (uint32_t)kQChunks) * kQChunk + (uint32_t)lane;
+                float gmx = kNegInf;
+                if (e0 + (uint32_t)lane < total) {
+                    const u32x4 g = L.grp[slot];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        gmx = __builtin_elementwise_maximum(
+                            gmx, __builtin_elementwise_maximum(__uint_as_float(g[d] << 16),
+                                                               __uint_as_float(g[d] & 0xFFFF0000u)));
                 }
-                n += (uint32_t)__builtin_popcountll(bal);
-                const bool last = e0 + 64 >= total;
-                if (last && !prefetched && i + 1 < K) {
-                    // the next position's key row, for the likely token, while this row is scored
-                    top = wave_max_u64(top);
-                    next_key = row_quad(a.A, key_index(top), rank);
-                    prefetched = true;
-                }
-                if (n > (uint32_t)(kQList - 64) || last) {
+                const bool pass = gmx >= fl;
+                const uint64_t bal = __ballot(pass);
+                if (pass) L.glist[ng + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (uint16_t)slot;
+                ng += (uint32_t)__builtin_popcountll(bal);
+                if (ng > (uint32_t)(kQGList - 64) || (e0 + kQChunk >= total && ng != 0u)) {
                     wave_lds_sync();
-                    score_list(L, n, a.Bt, rank, best);
+                    for (uint32_t b0 = 0; b0 < ng; b0 += 64) {
+                        uint32_t mk = 0u, v = 0u;
+                        u32x4 g{kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair};
+                        if (b0 + (uint32_t)lane < ng) {
+                            const uint32_t gs = L.glist[b0 + (uint32_t)lane];
+                            g = L.grp[gs];
+                            v = (uint32_t)L.gid[gs] * 8u;
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) {
+                                const uint32_t w = g[t >> 1];
+                                mk |= __uint_as_float((t & 1) ? (w & 0xFFFF0000u) : (w << 16)) >= fl ? (1u << t) : 0u;
+                            }
+                        }
+                        uint32_t cnt = 0;
+                        uint32_t at = n + wave_excl_scan_small((uint32_t)__builtin_popcount(mk), &cnt);
+                        while (mk != 0u) {
+                            const int t = __builtin_ctz(mk);
+                            mk &= mk - 1u;
+                            const uint32_t w = g[t >> 1];
+                            const uint32_t bits = (t & 1) ? (w & 0xFFFF0000u) : (w << 16);
+                            L.clist[at++] = ((uint64_t)(v + (uint32_t)t) << 32) | bits;
+                            top = umax64(top, argmax_key(__uint_as_float(bits), v + (uint32_t)t));
+                        }
+                        n += cnt;
+                        if (n > (uint32_t)(kQList - 8 * 64) && (b0 + 64 < ng || e0 + kQChunk < total)) {
+                            wave_lds_sync();
+                            score_list(L, n, a.Bt, rank, best);
+                            wave_lds_sync();
+                            n = 0;
+                        }
+                    }
                     wave_lds_sync();
-                    n = 0;
+                    ng = 0;
                 }
             }
-            tok = key_index(wave_max_u64(best));
-            have_next = prefetched && key_index(top) == tok;
+            top = wave_max_u64(top);
+            if (i + 1 < K && top != 0ull) {
+                // the next position's key row, for the likely token, while the rest is scored
+                next_key = row_quad(a.A, key_index(top), rank);
+                have_next = true;
+            }
+            if (n != 0u) {
+                wave_lds_sync();
+                score_list(L, n, a.Bt, rank, best);
+                wave_lds_sync();
+            }
+            best = wave_max_u64(best);
+            // (the group of the row's maximum is always kept and listed; scored densely otherwise)
+            if (best != 0ull) tok = key_index(best);
+            else kind = 3;
+            have_next = have_next && best != 0ull && key_index(top) == tok;
         }
+        if (kind == 3) tok = key_index(dense_row(L, a.base + (size_t)(row0 + i) * (size_t)V, V, a.Bt, rank));
         wave_lds_sync();  // L.akey is read before the next position's key row is written
         if (lane == 0) a.tokens[row0 + i] = tok;
         if (i + 1 < K) key = have_next ? next_key : row_quad(a.A, tok, rank);
@@ -595,12 +648,20 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
             S.rowfill[threadIdx.x] = 0u;
             S.rowover[threadIdx.x] = 0u;
         }
-        if (threadIdx.x == 0) S.next = 0u;
+        for (int t = (int)threadIdx.x; t < a.K * kQChunks / 4; t += kQT) reinterpret_cast<uint32_t*>(S.ctab)[t] = 0xFFFFFFFFu;
+        if (threadIdx.x == 0) {
+            S.next = 0u;
+            S.pool = 0u;
+        }
         __syncthreads();
-        if ((int)(threadIdx.x >> 6) < kQS)
+        if ((int)(threadIdx.x >> 6) < kQS) {
             stream_items<VEC>(S, a.base + (size_t)r * (size_t)a.K * (size_t)a.V, per_req, a.NC, a.V, hv.ab2);
-        else
+        } else {
+            // the chain is the request's critical path: its wave goes first on its SIMD
+            __builtin_amdgcn_s_setprio(3);
             chain_wave(a, S, r, hv.ab2, hv.b1, hv.ok);
+            __builtin_amdgcn_s_setprio(0);
+        }
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
     }
 }

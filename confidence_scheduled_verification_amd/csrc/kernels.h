@@ -148,7 +148,7 @@ struct StepArgs {
 constexpr int kCandMaxK = 32;
 constexpr int kCandMaxItems = 64;
 constexpr int kCandItem = 4096;           // base entries per streaming item
-constexpr int kCandStore = 16384;         // kept entries a request's LDS holds, split evenly among its rows
+constexpr int kCandGroups = 8192;         // kept 8-entry groups a request's LDS pool holds
 constexpr int kCandMaxGroups = 256;       // workgroups of one launch at most
 constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, then Bt
 

@@ -41,7 +41,8 @@ def _case(seed, R, K, V, rank, base_std=2.0, factor_std=0.05):
 @pytest.mark.parametrize("R,K,V,rank,factor_std", [
     (6, 3, 20000, 64, 1.0),      # bias far above the logits' spread: every entry a candidate
     (5, 4, 9000, 256, 0.2),      # candidates past the per-row share of the list
-    (2, 32, 5000, 64, 1.0),      # the most rows, so the smallest part of the store per row
+    (2, 32, 5000, 64, 1.0),      # more kept groups than the LDS pool holds
+    (1, 2, 70000, 32, 1.0),      # one row's kept groups past the chunk table
 ])
 def test_rows_the_bound_cannot_prune_are_scored_densely(R, K, V, rank, factor_std):
     gu.say(f"weak bound R={R} K={K} V={V} rank={rank} factor_std={factor_std}")
