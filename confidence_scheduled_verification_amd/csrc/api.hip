@@ -87,7 +87,7 @@ bool use_pruned(int dtype, int R, int K, int V, const void* A, const float* chai
 }
 
 dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int32_t* prev0, int R, int K, int V,
-                           int rank, int32_t* tokens, uint32_t* status, void* ws) {
+                           int rank, int32_t* tokens, uint32_t* status, void* ws, size_t ws_bytes) {
     dspark::CandArgs a{};
     a.base = (const uint16_t*)base;
     a.A = (const uint16_t*)m->A;
@@ -101,7 +101,17 @@ dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int
     a.NC = dspark::cand_items_per_row(V);
     a.tokens = tokens;
     a.status = status;
-    (void)ws;
+    // fewer requests than compute units: split each over several workgroups when the
+    // workspace holds the helpers' groups (dspark_workspace_bytes sizes it so)
+    a.S = 1;
+    const int S = dspark::cand_split(R, a.NC, num_cu());
+    if (S > 1 && ws_bytes >= dspark::ws_split_dat_off(R, K) + dspark::ws_split_dat_bytes(R, K, S)) {
+        char* w = (char*)ws;
+        a.S = S;
+        a.split_ctl = (uint32_t*)(w + dspark::ws_split_ctl_off());
+        a.split_grp = w + dspark::ws_split_dat_off(R, K);
+        a.split_gid = (uint32_t*)(w + dspark::ws_split_dat_off(R, K) + dspark::ws_split_grp_bytes(R, K, S));
+    }
     return a;
 }
 
@@ -157,7 +167,10 @@ const char* dspark_version(void) { return "dspark-gfx950 0.1"; }
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype) {
     (void)rank;
     if (R <= 0 || K <= 0) return 0;
-    return ws_need(R, K, V < 1 ? 1 : V, dtype);
+    // the minimum, and room for the pruned chain's split requests (on up to kCandMaxGroups
+    // compute units)
+    const int S = dspark::cand_split(R, dspark::cand_items_per_row(V < 1 ? 1 : V), dspark::kCandMaxGroups);
+    return ws_need(R, K, V < 1 ? 1 : V, dtype) + dspark::ws_split_dat_bytes(R, K, S);
 }
 
 size_t dspark_markov_state_bytes(int V, int rank, int dtype) {
@@ -205,8 +218,8 @@ int dspark_chain(const void* base, const void* A, const void* Bmat, int dtype, c
     hipStream_t s = (hipStream_t)stream;
     const void* Bt = markov_bt(markov);
     if (use_pruned(dtype, R, K, V, A, chained_logits)) {
-        const hipError_t e = dspark::launch_cand(cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws),
-                                                 num_cu(), s);
+        const dspark::CandArgs ca = cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws, ws_bytes);
+        const hipError_t e = dspark::launch_cand(ca, num_cu(), s);
         return e == hipSuccess ? DSPARK_OK : hip_fail(e, "chain (pruned)");
     }
     char* chain_ws = (char*)ws + dspark::ws_chain_off();
@@ -338,7 +351,8 @@ int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dty
         // method the confidences score the drafted tokens, so the schedule follows)
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
-        e = dspark::launch_cand(cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws), num_cu(), s);
+        const dspark::CandArgs ca = cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws, ws_bytes);
+        e = dspark::launch_cand(ca, num_cu(), s);
         if (e != hipSuccess) return hip_fail(e, "step (pruned chain)");
         if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");

@@ -295,10 +295,11 @@ __device__ __forceinline__ void take_chunks(QLds& L, int i, uint32_t at, uint32_
 // One item of a streaming wave (see the file comment): the item's maximum into its row's
 // (or its first NaN into the row's mark), then every 8-entry group of the item whose
 // maximum clears the floor of the row's maximum so far, kept whole with its group number
-// at places claimed in row i's chunks; then the item is counted into its row.  A group of
+// at places claimed in row i's chunks; then the item is counted into its row (the count
+// after it is returned).  A group of
 // -inf entries never wins unless the whole row is -inf, which is handled apart, so it is
 // never kept.
-__device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, float ab2) {
+__device__ __forceinline__ uint32_t keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, float ab2) {
     const int lane = threadIdx.x & 63;
     constexpr float kNegInf = -__builtin_huge_valf();
     float gm[8];
@@ -365,29 +366,197 @@ __device__ __forceinline__ void keep_item(QLds& L, const u32x4 (&cur)[8], int i,
         }
     }
     lds_writes_done();
-    if (lane == 0) __hip_atomic_fetch_add(&L.rowdone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    uint32_t done = 0u;
+    if (lane == 0) done = __hip_atomic_fetch_add(&L.rowdone[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(done) + 1u;
 }
 
-// A streaming wave's items of one request: it takes the next item from the workgroup's
-// counter whenever it starts loading one, so that waves which happen to be served faster
-// take more, and items are taken in order (rows complete in order).  Each item is loaded
-// one item ahead (two buffers in turn).  An item past the request loads nothing (v0 = V:
-// every entry reads as -inf).
-template <bool VEC>
-__device__ __forceinline__ void stream_items(QLds& L, const uint16_t* rbase, int per_req, int NC, int V, float ab2) {
+// ---------------------------------------------------------------------------------
+// One request over several workgroups (a.S > 1)
+
+// Header of a helper's row in the workspace: the launch epoch it was written in (set
+// last), the row's maximum over the helper's share (order-preserving image, 0 = none),
+// its kept groups (kSplitNone: more than kSplitCap) and ~(first NaN index) (0 = none).
+struct SplitHdr {
+    uint32_t flag, max, count, nan;
+};
+constexpr uint32_t kSplitNone = 0xFFFFFFFFu;
+static_assert(sizeof(SplitHdr) == kSplitHdrBytes, "header size");
+
+// Helper h = r (S - 1) + s - 1 of request r (share s >= 1): header of its row i, and its
+// groups for that row.
+__device__ __forceinline__ SplitHdr* split_hdr(const CandArgs& a, int h, int i) {
+    return reinterpret_cast<SplitHdr*>(reinterpret_cast<char*>(a.split_ctl) + 256) + (size_t)h * kCandMaxK + i;
+}
+__device__ __forceinline__ size_t split_row(const CandArgs& a, int h, int i) {
+    return ((size_t)h * (size_t)a.K + (size_t)i) * kSplitCap;
+}
+__device__ __forceinline__ u32x4* split_grp(const CandArgs& a) { return reinterpret_cast<u32x4*>(a.split_grp); }
+__device__ __forceinline__ uint32_t* split_gid(const CandArgs& a) { return a.split_gid; }
+
+// Items of share s of a row of NC items split S ways: share s takes every S-th item from
+// the s-th on (in the request's rotated order, below), so that the workgroups of one
+// request read neighbouring items at any time.
+__device__ __forceinline__ int share_items(int s, int NC, int S) { return (NC - s + S - 1) / S; }
+
+// Words exchanged between workgroups, which may sit on different dies, are stored and
+// loaded as relaxed device-scope atomics: each access is coherent by itself, without the
+// whole-cache write-back or invalidation that a release or acquire fence would cost
+// every other workgroup on the die.  Order comes from waiting: the writer's stores have
+// all completed before it stores the epoch, and the reader loads nothing before it has
+// seen the epoch.
+__device__ __forceinline__ void put_u32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get_u32(uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_grp(u32x4* p, const u32x4& g) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    __hip_atomic_store(q, ((uint64_t)g[1] << 32) | g[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, ((uint64_t)g[3] << 32) | g[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 get_grp(u32x4* p) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+// Every memory access of this wave so far has completed (stores included).
+__device__ __forceinline__ void wave_memory_done() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
+
+// A helper's wave that has just completed row i: the row's kept groups (unless more than
+// kSplitCap, or some found no chunk) and its header go to the workspace, the epoch last.
+__device__ __forceinline__ void export_row(QLds& L, const CandArgs& a, int h, int i, uint32_t ep) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t total = L.rowfill[i];
+    const bool none = L.rowover[i] != 0u || total > (uint32_t)kSplitCap;
+    if (!none) {
+        u32x4* gd = split_grp(a) + split_row(a, h, i);
+        uint32_t* gg = split_gid(a) + split_row(a, h, i);
+        for (uint32_t e = (uint32_t)lane; e < total; e += 64u) {
+            const uint32_t slot = (L.ctab[i][e / kQChunk] % (uint32_t)kQChunks) * kQChunk + e % kQChunk;
+            put_grp(gd + e, L.grp[slot]);
+            put_u32(gg + e, L.gid[slot]);
+        }
+    }
+    SplitHdr* hd = split_hdr(a, h, i);
+    if (lane == 0) {
+        put_u32(&hd->max, L.rowmax[i]);
+        put_u32(&hd->count, none ? kSplitNone : total);
+        put_u32(&hd->nan, L.rownan[i]);
+    }
+    wave_memory_done();
+    if (lane == 0) put_u32(&hd->flag, ep);
+}
+
+// The owner's import of share p >= 1 of row i: once the helper has written the row in this
+// launch (its epoch), the row's maximum, first NaN and kept groups join the owner's, and
+// the share's items are counted into the row.  A helper not heard from within the poll
+// limit, or with more groups than it could hand over, leaves the row to be scored densely.
+__device__ __forceinline__ void import_row(QLds& L, const CandArgs& a, int r, int p, int i, uint32_t ep) {
+    const int lane = threadIdx.x & 63;
+    const int h = r * (a.S - 1) + p - 1;
+    SplitHdr* hd = split_hdr(a, h, i);
+    uint32_t seen = 1u;
+    if (lane == 0) {
+        for (long n_polls = 0; get_u32(&hd->flag) != ep;) {
+            if (++n_polls > kQSpinLimit) {
+                seen = 0u;
+                raise_status(a.status, kStatusSyncTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    seen = __builtin_amdgcn_readfirstlane(seen);
+    asm volatile("" ::: "memory");
+    if (seen == 0u) {
+        if (lane == 0) L.rowover[i] = 1u;
+    } else {
+        const uint32_t hmax = get_u32(&hd->max), cnt = get_u32(&hd->count), hnan = get_u32(&hd->nan);
+        if (lane == 0) {
+            if (hnan != 0u) atomicMax(&L.rownan[i], hnan);
+            if (hmax != 0u) atomicMax(&L.rowmax[i], hmax);
+        }
+        if (cnt > (uint32_t)kSplitCap) {
+            if (lane == 0) L.rowover[i] = 1u;
+        } else if (cnt != 0u) {
+            uint32_t at = 0u;
+            if (lane == 0) at = __hip_atomic_fetch_add(&L.rowfill[i], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            at = __builtin_amdgcn_readfirstlane(at);
+            take_chunks(L, i, at, cnt);
+            u32x4* gd = split_grp(a) + split_row(a, h, i);
+            uint32_t* gg = split_gid(a) + split_row(a, h, i);
+            bool lost = false;
+            for (uint32_t e = (uint32_t)lane; e < cnt; e += 64u) {
+                const uint32_t q = at + e, c = q / kQChunk;
+                const uint32_t id = c < (uint32_t)kQChunks ? (uint32_t)L.ctab[i][c] : (uint32_t)kQNone;
+                if (id < (uint32_t)kQChunks) {
+                    L.grp[id * kQChunk + q % kQChunk] = get_grp(gd + e);
+                    L.gid[id * kQChunk + q % kQChunk] = (uint16_t)get_u32(gg + e);
+                } else {
+                    lost = true;
+                }
+            }
+            if (__ballot(lost) != 0ull && lane == 0) L.rowover[i] = 1u;
+        }
+    }
+    lds_writes_done();
+    const uint32_t items = (uint32_t)share_items(p, a.NC, a.S);
+    if (lane == 0) __hip_atomic_fetch_add(&L.rowdone[i], items, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// ---------------------------------------------------------------------------------
+// A streaming wave's tasks of one request.  Every row has T tasks: the workgroup's share
+// of the row's items (all of them when S = 1) and, for the owner of a split request
+// (MODE 2), one import per helper.  Request r visits a row's items from item r mod NC on,
+// wrapping round, so that requests whose rows lie a power of two apart do not all read
+// the same offset (and so the same memory channels) at once.
+// MODE 0: whole requests; MODE 1: a helper (exports each row it completes); MODE 2: the
+// owner.  A wave takes the next task from the workgroup's counter whenever it starts
+// loading one, so that waves which happen to be served faster take more, and tasks are
+// taken in order (rows complete in order).  Each item is loaded one item ahead (two
+// buffers in turn); a task that is no item (an import, or past the request) loads nothing
+// (v0 = V: every entry reads as -inf).
+template <bool VEC, int MODE>
+__device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, int s, float ab2, uint32_t ep) {
+    const int K = a.K, NC = a.NC, V = a.V;
+    const int S = MODE == 0 ? 1 : a.S;
+    const int n_own = share_items(s, NC, S);
+    const int T = n_own + (MODE == 2 ? S - 1 : 0);
+    const int rot = r % NC + s;
+    auto item_of = [&](int t) {  // item index within the row of the t-th own task
+        const int u = rot + t * S;
+        return u < NC ? u : (u - NC < NC ? u - NC : u % NC);
+    };
+    const int per_req = K * T;
+    const uint16_t* rbase = a.base + (size_t)r * (size_t)K * (size_t)V;
     auto claim = [&]() -> int {
         uint32_t j = 0u;
         if ((threadIdx.x & 63) == 0) j = atomicAdd(&L.next, 1u);
         return (int)__builtin_amdgcn_readfirstlane(j);
     };
     auto issue = [&](u32x4 (&buf)[8], int j) {
-        const bool ok = j < per_req;
-        load_item<VEC>(buf, rbase + (size_t)(ok ? j / NC : 0) * V, ok ? (j % NC) * kQItem : V, V);
+        const int i = j / T, t = j - i * T;
+        const bool ok = j < per_req && t < n_own;
+        load_item<VEC>(buf, rbase + (size_t)(ok ? i : 0) * V, ok ? item_of(t) * kQItem : V, V);
     };
     auto take = [&](const u32x4 (&buf)[8], int j) {
         if (j < per_req) {
-            const int i = j / NC;
-            keep_item(L, buf, i, (j - i * NC) * kQItem, ab2);
+            const int i = j / T, t = j - i * T;
+            if (t < n_own) {
+                const uint32_t done = keep_item(L, buf, i, item_of(t) * kQItem, ab2);
+                if constexpr (MODE == 1) {
+                    if (done == (uint32_t)n_own) export_row(L, a, r * (a.S - 1) + s - 1, i, ep);
+                }
+            } else if constexpr (MODE == 2) {
+                import_row(L, a, r, t - n_own + 1, i, ep);
+            }
         }
     };
     // (one item ahead already reads at the device's rate, and the chain wave's own loads
@@ -634,34 +803,67 @@ __device__ __forceinline__ void chain_wave(const CandArgs& a, QLds& L, int r, fl
     }
 }
 
-// Stage 1 in one launch: workgroup g takes requests g, g + G, ...
+// The request's LDS state before its first item.
+__device__ __forceinline__ void reset_request(QLds& L, int K) {
+    if ((int)threadIdx.x < K) {
+        L.rowmax[threadIdx.x] = 0u;
+        L.rownan[threadIdx.x] = 0u;
+        L.rowdone[threadIdx.x] = 0u;
+        L.rowfill[threadIdx.x] = 0u;
+        L.rowover[threadIdx.x] = 0u;
+    }
+    for (int t = (int)threadIdx.x; t < K * kQChunks / 4; t += kQT) reinterpret_cast<uint32_t*>(L.ctab)[t] = 0xFFFFFFFFu;
+    if (threadIdx.x == 0) {
+        L.next = 0u;
+        L.pool = 0u;
+    }
+}
+
+__device__ __forceinline__ void run_chain(const CandArgs& a, QLds& L, int r, const HeaderView& hv) {
+    // the chain is the request's critical path: its wave goes first on its SIMD
+    __builtin_amdgcn_s_setprio(3);
+    chain_wave(a, L, r, hv.ab2, hv.b1, hv.ok);
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Stage 1 in one launch.  S = 1: workgroup g takes requests g, g + G, ...  S > 1: the
+// first R (S - 1) workgroups are the helpers (dispatched first, and they never wait for
+// another workgroup), the last R the owners.  The launch's epoch is one more than the
+// workspace's; the last workgroup to finish stores it there for the next launch.
 template <bool VEC>
 __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
     __shared__ QLds S;
     const HeaderView hv = header_view(a.hdr);
-    const int per_req = a.K * a.NC;
-    for (int r = blockIdx.x; r < a.R; r += (int)gridDim.x) {
-        if ((int)threadIdx.x < a.K) {
-            S.rowmax[threadIdx.x] = 0u;
-            S.rownan[threadIdx.x] = 0u;
-            S.rowdone[threadIdx.x] = 0u;
-            S.rowfill[threadIdx.x] = 0u;
-            S.rowover[threadIdx.x] = 0u;
-        }
-        for (int t = (int)threadIdx.x; t < a.K * kQChunks / 4; t += kQT) reinterpret_cast<uint32_t*>(S.ctab)[t] = 0xFFFFFFFFu;
-        if (threadIdx.x == 0) {
-            S.next = 0u;
-            S.pool = 0u;
-        }
+    if (a.S > 1) {
+        __shared__ uint32_t ep_lds;
+        const int nh = a.R * (a.S - 1);
+        const int b = (int)blockIdx.x;
+        const bool helper = b < nh;
+        const int r = helper ? b / (a.S - 1) : b - nh;
+        const int s = helper ? 1 + b % (a.S - 1) : 0;
+        if (threadIdx.x == 0)
+            ep_lds = __hip_atomic_load(&a.split_ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        reset_request(S, a.K);
         __syncthreads();
-        if ((int)(threadIdx.x >> 6) < kQS) {
-            stream_items<VEC>(S, a.base + (size_t)r * (size_t)a.K * (size_t)a.V, per_req, a.NC, a.V, hv.ab2);
-        } else {
-            // the chain is the request's critical path: its wave goes first on its SIMD
-            __builtin_amdgcn_s_setprio(3);
-            chain_wave(a, S, r, hv.ab2, hv.b1, hv.ok);
-            __builtin_amdgcn_s_setprio(0);
-        }
+        const uint32_t ep = ep_lds;
+        if (helper)
+            stream_tasks<VEC, 1>(S, a, r, s, hv.ab2, ep);
+        else if ((int)(threadIdx.x >> 6) < kQS)
+            stream_tasks<VEC, 2>(S, a, r, 0, hv.ab2, ep);
+        else
+            run_chain(a, S, r, hv);
+        __syncthreads();
+        if (threadIdx.x == 0 && atomicInc(&a.split_ctl[1], gridDim.x - 1u) == gridDim.x - 1u)
+            __hip_atomic_store(&a.split_ctl[0], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    for (int r = blockIdx.x; r < a.R; r += (int)gridDim.x) {
+        reset_request(S, a.K);
+        __syncthreads();
+        if ((int)(threadIdx.x >> 6) < kQS)
+            stream_tasks<VEC, 0>(S, a, r, 0, hv.ab2, 0u);
+        else
+            run_chain(a, S, r, hv);
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
     }
 }
@@ -708,9 +910,10 @@ hipError_t launch_markov_bound(const void* A, const void* Bt, int V, int rank, v
 }
 
 hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s) {
-    // one workgroup per compute unit, at most one per request
+    // one workgroup per compute unit, at most one per request, or S per request
     int grid = num_cu < kCandMaxGroups ? num_cu : kCandMaxGroups;
     if (grid > a.R) grid = a.R;
+    if (a.S > 1) grid = a.R * a.S;
     CandArgs arg = a;
     void* args[] = {&arg};
     // 16-byte loads of the base logits need 8 | V and an aligned base

@@ -15,8 +15,13 @@ namespace dspark {
 //                        does not move with the shape;
 //   then ws_wide_bytes   the many-workgroup schedule's per-workgroup results and the
 //                        slots' ranks (fixed size, written before they are read);
+//   then ws_split_ctl_bytes  the pruned chain's split of requests over workgroups: its
+//                        launch epoch and finished-workgroup counter, then one 16-byte
+//                        header per (helper workgroup, row) whose first word is an epoch
+//                        (fixed size, so each word keeps its role whatever the shape);
 //   then                 the per-position argmax keys [K][R] (uint64) and the
-//                        persistent chain kernel's barrier counters [K][kMaxGroups].
+//                        persistent chain kernel's barrier counters [K][kMaxGroups];
+//   then (optional)      the helpers' kept groups, ws_split_dat_bytes (cand.hip).
 // The stage-wise paths zero the keys and counters they use first.  The step kernel
 // zeroes its keys in-launch and puts its counters and flag back to zero when it ends,
 // so once the workspace was zero-filled one time they are zero at every launch,
@@ -39,7 +44,9 @@ constexpr int kWideMaxGroups = kWideMaxN / kWideSlots;
 constexpr size_t kWidePartialBytes = 48;  // one workgroup's result
 inline size_t ws_wide_off() { return ws_sync_bytes(); }
 inline size_t ws_wide_bytes() { return ws_round((size_t)kWideMaxGroups * kWidePartialBytes + (size_t)kWideMaxN * 4); }
-inline size_t ws_chain_off() { return ws_sync_bytes() + ws_wide_bytes(); }
+inline size_t ws_split_ctl_off() { return ws_sync_bytes() + ws_wide_bytes(); }
+inline size_t ws_split_ctl_bytes();  // defined with the pruned chain's constants below
+inline size_t ws_chain_off() { return ws_split_ctl_off() + ws_split_ctl_bytes(); }
 inline size_t ws_total_bytes(int R, int K) { return ws_chain_off() + ws_chain_bytes(R, K); }
 
 // Probabilistic drafting: Gumbel-max sampling of softmax(x / temperature) with
@@ -154,6 +161,31 @@ constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, th
 
 inline int cand_items_per_row(int V) { return (V + kCandItem - 1) / kCandItem; }
 
+// With fewer requests than compute units a request is streamed by S <= kSplitMax
+// workgroups: its owner (which also runs the chain) and S - 1 helpers, each taking a
+// contiguous share of every row's items.  A helper hands each row's kept groups (at
+// most kSplitCap) and maximum over to the owner through the workspace.
+constexpr int kSplitMax = 4;
+constexpr int kSplitCap = 512;
+constexpr size_t kSplitHdrBytes = 16;
+inline size_t ws_split_ctl_bytes() { return 256 + (size_t)kCandMaxGroups * kCandMaxK * kSplitHdrBytes; }
+inline int cand_split(int R, int NC, int num_cu) {
+    const int cus = num_cu < kCandMaxGroups ? num_cu : kCandMaxGroups;
+    int S = R > 0 ? cus / R : 1;
+    S = S < kSplitMax ? S : kSplitMax;
+    S = S < NC ? S : NC;
+    return S > 1 ? S : 1;
+}
+inline size_t ws_split_dat_off(int R, int K) { return ws_total_bytes(R, K); }
+// groups [R (S-1)][K][kSplitCap] as 16-byte data, then their group numbers (uint32)
+inline size_t ws_split_grp_bytes(int R, int K, int S) {
+    return S > 1 ? ws_round((size_t)R * (size_t)(S - 1) * (size_t)K * kSplitCap * 16) : 0;
+}
+inline size_t ws_split_dat_bytes(int R, int K, int S) {
+    return S > 1 ? ws_split_grp_bytes(R, K, S) + ws_round((size_t)R * (size_t)(S - 1) * (size_t)K * kSplitCap * 4)
+                 : 0;
+}
+
 struct CandArgs {
     const uint16_t* base;
     const uint16_t* A;
@@ -163,6 +195,10 @@ struct CandArgs {
     int R, K, V, rank, NC;
     int32_t* tokens;
     uint32_t* status;
+    int S;                // workgroups per request (1: one workgroup takes whole requests)
+    uint32_t* split_ctl;  // S > 1: the workspace at ws_split_ctl_off
+    void* split_grp;      // S > 1: the workspace at ws_split_dat_off: the helpers' groups
+    uint32_t* split_gid;  // S > 1: then their group numbers
 };
 
 int chain_tile_vocab();
@@ -189,8 +225,8 @@ hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes,
 // squared row norms of A and Bt, then 2 max|A| max|Bt| (1 + 2^-10) rounded up and a flag
 // that it is finite.
 hipError_t launch_markov_bound(const void* A, const void* Bt, int V, int rank, void* hdr, hipStream_t s);
-// The candidate-pruned chain, one 1024-thread workgroup per compute unit (at most
-// kCandMaxGroups of them).
+// The candidate-pruned chain: one 512-thread workgroup per compute unit (at most
+// kCandMaxGroups of them), or R S workgroups when a request is split (a.S > 1).
 hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s);
 
 hipError_t launch_survival(const float* conf, int R, int K, float* surv, uint32_t* status, hipStream_t s);
