@@ -394,10 +394,22 @@ __device__ __forceinline__ size_t split_row(const CandArgs& a, int h, int i) {
 __device__ __forceinline__ u32x4* split_grp(const CandArgs& a) { return reinterpret_cast<u32x4*>(a.split_grp); }
 __device__ __forceinline__ uint32_t* split_gid(const CandArgs& a) { return a.split_gid; }
 
-// Items of share s of a row of NC items split S ways: share s takes every S-th item from
-// the s-th on (in the request's rotated order, below), so that the workgroups of one
-// request read neighbouring items at any time.
-__device__ __forceinline__ int share_items(int s, int NC, int S) { return (NC - s + S - 1) / S; }
+// A row's NC items split S ways (in the request's rotated order, below) are dealt in
+// rounds of P = 2S - 1: the owner (share 0) takes the first of each round, helper s the
+// (2s - 1)-th and 2s-th, so that the owner, which also imports the helpers' groups and
+// runs the chain, streams half as much as a helper, and the workgroups of one request
+// read neighbouring items at any time.  S = 1: every item, in order.
+__device__ __forceinline__ int share_items(int s, int NC, int S) {
+    const int P = 2 * S - 1, full = NC / P, rem = NC - full * P;
+    if (s == 0) return full + (rem > 0 ? 1 : 0);
+    const int extra = rem - (2 * s - 1);
+    return 2 * full + (extra < 0 ? 0 : (extra > 2 ? 2 : extra));
+}
+// Position within the row's dealing of share s's t-th item.
+__device__ __forceinline__ int share_item(int s, int t, int S) {
+    const int P = 2 * S - 1;
+    return s == 0 ? t * P : (t >> 1) * P + 2 * s - 1 + (t & 1);
+}
 
 // Words exchanged between workgroups, which may sit on different dies, are stored and
 // loaded as relaxed device-scope atomics: each access is coherent by itself, without the
@@ -529,10 +541,10 @@ __device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, 
     const int S = MODE == 0 ? 1 : a.S;
     const int n_own = share_items(s, NC, S);
     const int T = n_own + (MODE == 2 ? S - 1 : 0);
-    const int rot = r % NC + s;
+    const int rot = r % NC;
     auto item_of = [&](int t) {  // item index within the row of the t-th own task
-        const int u = rot + t * S;
-        return u < NC ? u : (u - NC < NC ? u - NC : u % NC);
+        const int u = rot + share_item(s, t, S);
+        return u < NC ? u : u - NC;
     };
     const int per_req = K * T;
     const uint16_t* rbase = a.base + (size_t)r * (size_t)K * (size_t)V;

@@ -163,8 +163,9 @@ inline int cand_items_per_row(int V) { return (V + kCandItem - 1) / kCandItem; }
 
 // With fewer requests than compute units a request is streamed by S <= kSplitMax
 // workgroups: its owner (which also runs the chain) and S - 1 helpers, each taking a
-// contiguous share of every row's items.  A helper hands each row's kept groups (at
-// most kSplitCap) and maximum over to the owner through the workspace.
+// share of every row's items (dealt in rounds of 2S - 1, so NC >= 2S - 1).  A helper
+// hands each row's kept groups (at most kSplitCap) and maximum over to the owner through
+// the workspace.
 constexpr int kSplitMax = 4;
 constexpr int kSplitCap = 512;
 constexpr size_t kSplitHdrBytes = 16;
@@ -173,7 +174,7 @@ inline int cand_split(int R, int NC, int num_cu) {
     const int cus = num_cu < kCandMaxGroups ? num_cu : kCandMaxGroups;
     int S = R > 0 ? cus / R : 1;
     S = S < kSplitMax ? S : kSplitMax;
-    S = S < NC ? S : NC;
+    S = S < (NC + 1) / 2 ? S : (NC + 1) / 2;  // a round of 2S - 1 items per row at least
     return S > 1 ? S : 1;
 }
 inline size_t ws_split_dat_off(int R, int K) { return ws_total_bytes(R, K); }
