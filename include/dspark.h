@@ -91,15 +91,18 @@ const char* dspark_last_error(void);
 /* Library version string. */
 const char* dspark_version(void);
 
-/* Bytes of device workspace needed by dspark_chain / dspark_chain_sample / dspark_step /
- * dspark_step_sized for this shape (0 when R*K == 0).  Zero-fill a workspace once, before
+/* Bytes of device workspace for dspark_chain / dspark_chain_sample / dspark_step /
+ * dspark_step_sized at this shape (0 when R*K == 0).  Zero-fill a workspace once, before
  * its first use: the kernels keep counters in it (grid-barrier counters and a ready flag
- * of the dense single-launch step) and put each back to zero before they end, so later
- * calls need no clearing.  A
+ * of the dense single-launch step, the pruned chain's launch epoch and finished-workgroup
+ * counter) and leave them ready for the next call, so later calls need no clearing.  A
  * call that ends with DSPARK_STATUS_SYNC_TIMEOUT may leave counters set: zero-fill the
- * workspace again before its next use.  A workspace sized for one shape serves any
- * smaller R and K and any V, rank and dtype (the pruned chain keeps its candidates in
- * LDS). */
+ * workspace again before its next use.  The size includes room for the pruned chain to
+ * split each request over several workgroups when there are fewer requests than compute
+ * units (the helpers hand their kept candidates over through it); the calls also accept a
+ * smaller workspace, down to the size without that room (DSPARK_EINVAL below it), and then
+ * stream each request with one workgroup.  So a workspace sized for one shape serves any
+ * smaller R and K and any V, rank and dtype. */
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
 
 /*
