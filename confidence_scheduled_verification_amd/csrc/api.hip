@@ -101,7 +101,6 @@ dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int
     a.NC = dspark::cand_items_per_row(V);
     a.tokens = tokens;
     a.status = status;
-    a.split_ctl = (uint32_t*)((char*)ws + dspark::ws_split_ctl_off());
     // fewer requests than compute units: split each over several workgroups when the
     // workspace holds the helpers' groups (dspark_workspace_bytes sizes it so)
     a.S = 1;
@@ -109,6 +108,7 @@ dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int
     if (S > 1 && ws_bytes >= dspark::ws_split_dat_off(R, K) + dspark::ws_split_dat_bytes(R, K, S)) {
         char* w = (char*)ws;
         a.S = S;
+        a.split_ctl = (uint32_t*)(w + dspark::ws_split_ctl_off());
         a.split_grp = w + dspark::ws_split_dat_off(R, K);
         a.split_gid = (uint32_t*)(w + dspark::ws_split_dat_off(R, K) + dspark::ws_split_grp_bytes(R, K, S));
     }
@@ -349,26 +349,24 @@ int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dty
     if (n > 0 && use_pruned(dtype, R, K, V, A, nullptr)) {
         // the chain, then stages 2-5 over the confidences and the verified tokens (in the
         // method the confidences score the drafted tokens, so the schedule follows)
-        dspark::FusedSchedArgs sa{conf,   R,        K,          n_sampling, T,      num_reqs, verify_cost,
-                                  draft_cost, bmax, sizing,    surv,       order,  sorted_surv, b_star,
-                                  best_obj, prefix_len, offsets, ver_idx,   status, nullptr, 0,
-                                  tokens,   ver_tokens};
-        const bool wide = !stale && n <= dspark::kWideMaxN;
-        dspark::CandArgs ca = cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws, ws_bytes);
-        if (wide) {
-            // stages 3-4's ranking inside the chain's launch (it reads only the
-            // confidences), its shares taken by workgroups whose requests are done; its
-            // results and share counter in the workspace; then the finish launch
-            sa.ws = (uint64_t*)((char*)ws + dspark::ws_wide_off());
-            ca.rk = dspark::rank_args(sa, ca.split_ctl + 2);
-        }
         if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
+        const dspark::CandArgs ca = cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws, ws_bytes);
         e = dspark::launch_cand(ca, num_cu(), s);
         if (e != hipSuccess) return hip_fail(e, "step (pruned chain)");
         if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
             return hip_fail(e, "step (timing event)");
-        e = wide ? dspark::launch_sched_finish(sa, s) : dspark::launch_sched_fused(sa, s);
+        dspark::FusedSchedArgs sa{conf,   R,        K,          n_sampling, T,      num_reqs, verify_cost,
+                                  draft_cost, bmax, sizing,    surv,       order,  sorted_surv, b_star,
+                                  best_obj, prefix_len, offsets, ver_idx,   status, nullptr, 0,
+                                  tokens,   ver_tokens};
+        if (!stale && n <= dspark::kWideMaxN) {
+            // stages 2-5 over many workgroups (their counter and results in the workspace)
+            sa.ws = (uint64_t*)((char*)ws + dspark::ws_wide_off());
+            e = dspark::launch_sched_wide(sa, s);
+        } else {
+            e = dspark::launch_sched_fused(sa, s);
+        }
         return e == hipSuccess ? DSPARK_OK : hip_fail(e, "step (schedule)");
     }
     if (n > 0) {

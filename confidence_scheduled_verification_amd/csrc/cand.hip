@@ -49,7 +49,6 @@
 // row's scoring is left once the last item arrives.
 #include "common.h"
 #include "kernels.h"
-#include "sched_dev.h"
 
 namespace dspark {
 
@@ -94,9 +93,11 @@ __device__ __forceinline__ float cand_floor(float M, float ab2) {
     return (M - ab2) - __builtin_fabsf(M) * 0x1p-20f;
 }
 
-// DPP lane moves within rows of 16 lanes (no LDS round trip, unlike a shuffle): kDppXor1
-// (quad_perm [1,0,3,2]), kDppXor2 ([2,3,0,1]), kDppHalfMirror (lane i <-> 7 - i within
-// each 8) and kDppMirror (i <-> 15 - i within each 16), as the schedule's.
+// DPP lane moves within rows of 16 lanes (no LDS round trip, unlike a shuffle).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16
 
 __device__ __forceinline__ float dpp_f32(float x, int ctrl) {
     switch (ctrl) {  // the control must be a constant of the builtin
@@ -837,30 +838,13 @@ __device__ __forceinline__ void run_chain(const CandArgs& a, QLds& L, int r, con
     __builtin_amdgcn_s_setprio(0);
 }
 
-// The end of a workgroup's launch: the step's ranking shares still untaken (rk.groups >
-// 0), then the count of finished workgroups; the last to finish puts the share counter
-// back to 0 and, for split requests, stores the launch's epoch for the next launch.
-__device__ __forceinline__ void finish_launch(const CandArgs& a, RankShared<kQT>& rsh, uint32_t ep) {
-    if (a.rk.groups > 0) rank_phase<kQT>(rsh, a.rk);
-    if (threadIdx.x == 0 && a.split_ctl && atomicInc(&a.split_ctl[1], gridDim.x - 1u) == gridDim.x - 1u) {
-        if (a.rk.groups > 0) __hip_atomic_store(a.rk.claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (a.S > 1) __hip_atomic_store(&a.split_ctl[0], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
 // Stage 1 in one launch.  S = 1: workgroup g takes requests g, g + G, ...  S > 1: the
 // first R (S - 1) workgroups are the helpers (dispatched first, and they never wait for
 // another workgroup), the last R the owners.  The launch's epoch is one more than the
-// workspace's; the last workgroup to finish stores it there for the next launch.  A
-// workgroup whose requests are done takes shares of the step's ranking (which reads only
-// the confidences), so that the ranking runs while the slowest chains finish.
+// workspace's; the last workgroup to finish stores it there for the next launch.
 template <bool VEC>
 __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
-    __shared__ union LdsUse {
-        QLds q;
-        RankShared<kQT> rk;
-    } U;
-    QLds& S = U.q;
+    __shared__ QLds S;
     const HeaderView hv = header_view(a.hdr);
     if (a.S > 1) {
         __shared__ uint32_t ep_lds;
@@ -881,7 +865,8 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
         else
             run_chain(a, S, r, hv);
         __syncthreads();
-        finish_launch(a, U.rk, ep);
+        if (threadIdx.x == 0 && atomicInc(&a.split_ctl[1], gridDim.x - 1u) == gridDim.x - 1u)
+            __hip_atomic_store(&a.split_ctl[0], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
     for (int r = blockIdx.x; r < a.R; r += (int)gridDim.x) {
@@ -893,7 +878,6 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
             run_chain(a, S, r, hv);
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
     }
-    finish_launch(a, U.rk, 0u);
 }
 
 __global__ void markov_norms_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, int V, int rank,

@@ -97,23 +97,6 @@ struct BudgetArgs {
     uint32_t* status;
 };
 
-// Stages 3-4's ranking over many workgroups (shares of kWideSlots slots): the arguments of
-// sched_rank_kernel, which the pruned chain kernel can also run in its own launch.
-struct RankArgs {
-    const float* conf;
-    int R, K, n_sampling, T, num_reqs;
-    const float* vc;
-    const float* dc;
-    int bmax;
-    float* surv;          // survival out, or null
-    int32_t* order;       // or null
-    float* sorted_surv;   // or null
-    uint32_t* status;
-    unsigned char* ws;    // the workspace at ws_wide_off
-    int groups;           // shares, ceil(R K / kWideSlots); 0: none in this launch
-    uint32_t* claim;      // the next share to take (device; back at 0 after each launch)
-};
-
 struct FusedSchedArgs {
     const float* conf;
     int R, K, n_sampling, T, num_reqs;
@@ -214,10 +197,9 @@ struct CandArgs {
     int32_t* tokens;
     uint32_t* status;
     int S;                // workgroups per request (1: one workgroup takes whole requests)
-    uint32_t* split_ctl;  // the workspace at ws_split_ctl_off (S > 1, or a ranking to run)
+    uint32_t* split_ctl;  // S > 1: the workspace at ws_split_ctl_off
     void* split_grp;      // S > 1: the workspace at ws_split_dat_off: the helpers' groups
     uint32_t* split_gid;  // S > 1: then their group numbers
-    RankArgs rk;          // rk.groups > 0: the step's ranking, taken by workgroups as they finish
 };
 
 int chain_tile_vocab();
@@ -259,9 +241,6 @@ hipError_t launch_sched_fused(const FusedSchedArgs& a, hipStream_t s);
 // Stages 2-5 over many workgroups, then one (sizing from the current confidences, R*K <=
 // kWideMaxN): a.ws is the workspace region at ws_wide_off().
 hipError_t launch_sched_wide(const FusedSchedArgs& a, hipStream_t s);
-// The finish launch of launch_sched_wide alone, after a chain launch that ran the ranking.
-hipError_t launch_sched_finish(const FusedSchedArgs& a, hipStream_t s);
-RankArgs rank_args(const FusedSchedArgs& a, uint32_t* claim);
 hipError_t launch_accept_greedy(const int32_t* ver_tokens, const int32_t* offsets, const int32_t* target, int R,
                                 int K, int32_t* accept_len, int32_t* next_prev0, int32_t* out_tokens,
                                 uint32_t* status, hipStream_t s);

@@ -109,11 +109,218 @@ __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restr
 // one-workgroup kernel, so B* and f(B*) are the same doubles.
 
 constexpr int kWT = 256;                     // threads per workgroup
+constexpr int kWParts = kWT / kWideSlots;    // thread groups counting for one slot
+constexpr int kNone = 0x7FFFFFFF;
 
-__global__ __launch_bounds__(kWT) void sched_rank_kernel(RankArgs a) {
-    __shared__ RankShared<kWT> sh;
-    rank_prepare<kWT>(sh, a);
-    rank_share<kWT>(sh, a, (int)blockIdx.x);
+struct WidePartial {  // kWidePartialBytes
+    double f;      // largest f(B) among this workgroup's B
+    double fdrop;  // f at the drop below
+    double fbmax;  // f(bmax), if this workgroup evaluated it
+    int32_t B;     // the smallest B reaching f
+    int32_t drop;  // the smallest B with f(B+1) <= f(B) among this workgroup's slots, or kNone
+    int32_t has_fbmax;
+    int32_t pad[3];
+};
+static_assert(sizeof(WidePartial) == kWidePartialBytes, "the workspace holds kWidePartialBytes per workgroup");
+
+__device__ __forceinline__ WidePartial no_partial() {
+    WidePartial p;
+    p.f = -INFINITY;
+    p.fdrop = 0.0;
+    p.fbmax = 0.0;
+    p.B = kNone;
+    p.drop = kNone;
+    p.has_fbmax = 0;
+    p.pad[0] = p.pad[1] = p.pad[2] = 0;
+    return p;
+}
+
+// a takes over b's candidates where they are better (argmax: larger f, then smaller B;
+// first drop: smaller B; f(bmax) from whichever has it)
+__device__ __forceinline__ void merge_partial(WidePartial& a, const WidePartial& b) {
+    if (b.f > a.f || (b.f == a.f && b.B < a.B)) {
+        a.f = b.f;
+        a.B = b.B;
+    }
+    if (b.drop < a.drop) {
+        a.drop = b.drop;
+        a.fdrop = b.fdrop;
+    }
+    if (b.has_fbmax) {
+        a.fbmax = b.fbmax;
+        a.has_fbmax = 1;
+    }
+}
+
+struct RankShared {
+    uint64_t word[kWideMaxN];    // slot words in flat order
+    uint64_t fa[kWideMaxN], fb[kWideMaxN], fc[kWideMaxN];  // each slot's survival, exact (units of 2^-149)
+    float vc[kWideMaxN + 1];     // vc[T + B], B = 0 .. bmax
+    uint32_t wcnt[kWT / 64][kWideSlots];
+    U192 wsum[kWT / 64][kWideSlots];
+    WidePartial part[kWideSlots];
+};
+
+__device__ __forceinline__ U192 shfl_xor_192(const U192& x, int m) {
+    return U192{shfl_xor_u64(x.a, m), shfl_xor_u64(x.b, m), shfl_xor_u64(x.c, m)};
+}
+
+__global__ __launch_bounds__(kWT) void sched_rank_kernel(
+    const float* __restrict__ conf, int R, int K, int n_sampling, int T, int num_reqs, const float* __restrict__ vc,
+    const float* __restrict__ dc, int bmax, float* __restrict__ surv_out, int32_t* __restrict__ order,
+    float* __restrict__ sorted_surv, uint32_t* status, unsigned char* __restrict__ ws) {
+    __shared__ RankShared sh;
+    const int tid = threadIdx.x, g = blockIdx.x;
+    const int n = R * K;
+    WidePartial* parts = reinterpret_cast<WidePartial*>(ws);
+    int32_t* rank_of = reinterpret_cast<int32_t*>(ws + (size_t)kWideMaxGroups * kWidePartialBytes);
+
+    // survival of every slot (each thread one request at a time, eight confidences per
+    // memory round trip), and the cost-table entries B = 0 .. bmax, all requested before
+    // the first is used
+    constexpr int kVq = kWideMaxN / kWT + 1;
+    float vq[kVq];
+#pragma unroll
+    for (int u = 0; u < kVq; ++u) vq[u] = tid + u * kWT <= bmax ? vc[T + tid + u * kWT] : 0.f;
+    const float dcost_f = dc[num_reqs];
+    bool bad = false;
+    for (int r = tid; r < R; r += kWT) {
+        const int f0 = r * K;
+        float s = 0.f;
+        for (int i0 = 0; i0 < K; i0 += 8) {
+            float c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = i0 + u < K ? conf[f0 + i0 + u] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u;
+                if (i < K) {
+                    const float cu = sanitize_conf(c[u], bad);
+                    s = (i == 0) ? cu : s * cu;
+                    sh.word[f0 + i] = slot_word(kOne - __float_as_uint(s), f0 + i);
+                    const U192 fs = fixed_from_bits(__float_as_uint(s));
+                    sh.fa[f0 + i] = fs.a;
+                    sh.fb[f0 + i] = fs.b;
+                    sh.fc[f0 + i] = fs.c;
+                    if (g == 0 && surv_out) surv_out[f0 + i] = s;
+                }
+            }
+        }
+    }
+    if (bad && g == 0) raise_status(status, kStatusConfSanitized);
+#pragma unroll
+    for (int u = 0; u < kVq; ++u)
+        if (tid + u * kWT <= bmax) sh.vc[tid + u * kWT] = vq[u];
+    __syncthreads();
+
+    // this workgroup's slots: thread (el, pt) counts slot 8g + el over words [y0, y1)
+    const int el = tid % kWideSlots, pt = tid / kWideSlots;
+    const int x = g * kWideSlots + el;
+    const int lane = tid & 63, w = tid >> 6;
+    uint32_t cnt = 0u;
+    U192 S = {0ull, 0ull, 0ull};
+    if (x < n) {
+        const uint64_t wx = sh.word[x];
+        const int y0 = (int)(((long)pt * n) / kWParts), y1 = (int)(((long)(pt + 1) * n) / kWParts);
+        int y = y0;
+        for (; y + 4 <= y1; y += 4) {  // four words' reads in flight together
+            uint64_t wy[4], a[4], b[4], c[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wy[u] = sh.word[y + u];
+                a[u] = sh.fa[y + u];
+                b[u] = sh.fb[y + u];
+                c[u] = sh.fc[y + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool lt = wy[u] < wx;
+                cnt += lt ? 1u : 0u;
+                S = add192(S, lt ? U192{a[u], b[u], c[u]} : U192{0ull, 0ull, 0ull});
+            }
+        }
+        for (; y < y1; ++y) {
+            const bool lt = sh.word[y] < wx;
+            cnt += lt ? 1u : 0u;
+            S = add192(S, lt ? U192{sh.fa[y], sh.fb[y], sh.fc[y]} : U192{0ull, 0ull, 0ull});
+        }
+    }
+    // the wave's eight groups of each slot (lanes el, el + 8, ..., el + 56), then the waves
+#pragma unroll
+    for (int m = 8; m < 64; m <<= 1) {
+        cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
+        S = add192(S, shfl_xor_192(S, m));
+    }
+    if (lane < kWideSlots) {
+        sh.wcnt[w][lane] = cnt;
+        sh.wsum[w][lane] = S;
+    }
+    __syncthreads();
+    if (tid < kWideSlots) {
+        WidePartial p = no_partial();
+        if (x < n) {
+            uint32_t rk = 0u;
+            U192 Sx = {0ull, 0ull, 0ull};
+#pragma unroll
+            for (int q = 0; q < kWT / 64; ++q) {
+                rk += sh.wcnt[q][tid];
+                Sx = add192(Sx, sh.wsum[q][tid]);
+            }
+            const int r = (int)rk;
+            const uint64_t wx = sh.word[x];
+            if (order) order[r] = x;
+            if (sorted_surv) sorted_surv[r] = __uint_as_float(kOne - word_key(wx));
+            rank_of[x] = r;
+            const double dcost = (double)dcost_f;
+            const uint64_t ns_hi = (uint64_t)(uint32_t)n_sampling << 21;  // n_sampling * 2^149
+            bool badc = false;
+            auto eval = [&](const U192& s_excl, float vcost) -> double {
+                U192 X = s_excl;
+                X.c += ns_hi;
+                const double num = fixed_to_double(X);
+                const double den = (double)vcost + dcost;
+                if (den > 0.0 && den <= 1.7976931348623157e308) return num / den;
+                badc = true;
+                return -INFINITY;
+            };
+            // f(r) and f(r+1): the argmax candidate B = r + 1 (and B = 0 from rank 0), the
+            // first-drop test at B = r, and f(bmax) from whichever slot evaluates it
+            if (r <= bmax) {
+                const double fr = eval(Sx, sh.vc[r]);
+                if (r == 0) {
+                    p.f = fr;
+                    p.B = 0;
+                    if (bmax == 0) {
+                        p.fbmax = fr;
+                        p.has_fbmax = 1;
+                    }
+                }
+                if (r + 1 <= bmax) {
+                    const double f1 = eval(add192(Sx, U192{sh.fa[x], sh.fb[x], sh.fc[x]}), sh.vc[r + 1]);
+                    if (f1 > p.f || (f1 == p.f && r + 1 < p.B)) {
+                        p.f = f1;
+                        p.B = r + 1;
+                    }
+                    if (!(f1 > fr)) {
+                        p.drop = r;
+                        p.fdrop = fr;
+                    }
+                    if (r + 1 == bmax) {
+                        p.fbmax = f1;
+                        p.has_fbmax = 1;
+                    }
+                }
+            }
+            if (badc) raise_status(status, kStatusCostInvalid);
+        }
+        sh.part[tid] = p;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        WidePartial q = sh.part[0];
+        for (int e = 1; e < kWideSlots; ++e) merge_partial(q, sh.part[e]);
+        parts[g] = q;
+    }
 }
 
 __global__ __launch_bounds__(kWT) void sched_finish_kernel(
@@ -267,28 +474,12 @@ hipError_t launch_sched_wide(const FusedSchedArgs& a, hipStream_t s) {
     if (n <= 0 || n > kWideMaxN || a.sizing.separate || !a.ws) return hipErrorInvalidValue;
     const int G = (n + kWideSlots - 1) / kWideSlots;
     unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
-    hipLaunchKernelGGL(sched_rank_kernel, dim3(G), dim3(kWT), 0, s, rank_args(a, nullptr));
+    hipLaunchKernelGGL(sched_rank_kernel, dim3(G), dim3(kWT), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs,
+                       a.vc, a.dc, a.bmax, a.surv, a.order, a.sorted_surv, a.status, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sched_finish_kernel, dim3(1), dim3(kWT), 0, s, a.R, a.K, G, a.bmax, a.sizing.rule, a.b_star,
                        a.best_obj, a.prefix_len, a.offsets, a.ver_idx, ws, a.tokens, a.ver_tokens);
-    return hipGetLastError();
-}
-
-RankArgs rank_args(const FusedSchedArgs& a, uint32_t* claim) {
-    const int n = a.R * a.K;
-    return RankArgs{a.conf,  a.R,     a.K,     a.n_sampling, a.T,  a.num_reqs, a.vc,
-                    a.dc,    a.bmax,  a.surv,  a.order,      a.sorted_surv, a.status,
-                    reinterpret_cast<unsigned char*>(a.ws), (n + kWideSlots - 1) / kWideSlots, claim};
-}
-
-hipError_t launch_sched_finish(const FusedSchedArgs& a, hipStream_t s) {
-    const int n = a.R * a.K;
-    if (n <= 0 || n > kWideMaxN || a.sizing.separate || !a.ws) return hipErrorInvalidValue;
-    const int G = (n + kWideSlots - 1) / kWideSlots;
-    hipLaunchKernelGGL(sched_finish_kernel, dim3(1), dim3(kWT), 0, s, a.R, a.K, G, a.bmax, a.sizing.rule, a.b_star,
-                       a.best_obj, a.prefix_len, a.offsets, a.ver_idx, reinterpret_cast<unsigned char*>(a.ws),
-                       a.tokens, a.ver_tokens);
     return hipGetLastError();
 }
 

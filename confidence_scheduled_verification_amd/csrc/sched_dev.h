@@ -32,7 +32,6 @@
 #include <math.h>
 
 #include "common.h"
-#include "kernels.h"
 
 namespace dspark {
 
@@ -793,271 +792,6 @@ __device__ __forceinline__ void sched_pass(SchedShared<NT>& sh, const float* __r
     __syncthreads();
     allocate_lds<NT>(sh, sel, R, K, B, tokens, prefix_len, offsets, ver_idx, ver_tokens, lds_rows, tok_lds);
 }
-
-
-// ---------------------------------------------------------------------------------
-// Stages 3-4's ranking over many workgroups, kWideSlots slots per share (sched.hip runs it
-// as sched_rank_kernel; the pruned chain kernel can run it in its own launch).
-
-constexpr int kNone = 0x7FFFFFFF;
-
-struct WidePartial {  // kWidePartialBytes
-    double f;      // largest f(B) among this workgroup's B
-    double fdrop;  // f at the drop below
-    double fbmax;  // f(bmax), if this workgroup evaluated it
-    int32_t B;     // the smallest B reaching f
-    int32_t drop;  // the smallest B with f(B+1) <= f(B) among this workgroup's slots, or kNone
-    int32_t has_fbmax;
-    int32_t pad[3];
-};
-static_assert(sizeof(WidePartial) == kWidePartialBytes, "the workspace holds kWidePartialBytes per workgroup");
-
-__device__ __forceinline__ WidePartial no_partial() {
-    WidePartial p;
-    p.f = -INFINITY;
-    p.fdrop = 0.0;
-    p.fbmax = 0.0;
-    p.B = kNone;
-    p.drop = kNone;
-    p.has_fbmax = 0;
-    p.pad[0] = p.pad[1] = p.pad[2] = 0;
-    return p;
-}
-
-// a takes over b's candidates where they are better (argmax: larger f, then smaller B;
-// first drop: smaller B; f(bmax) from whichever has it)
-__device__ __forceinline__ void merge_partial(WidePartial& a, const WidePartial& b) {
-    if (b.f > a.f || (b.f == a.f && b.B < a.B)) {
-        a.f = b.f;
-        a.B = b.B;
-    }
-    if (b.drop < a.drop) {
-        a.drop = b.drop;
-        a.fdrop = b.fdrop;
-    }
-    if (b.has_fbmax) {
-        a.fbmax = b.fbmax;
-        a.has_fbmax = 1;
-    }
-}
-
-template <int NT>
-struct RankShared {
-    uint64_t word[kWideMaxN];    // slot words in flat order
-    uint64_t fa[kWideMaxN], fb[kWideMaxN], fc[kWideMaxN];  // each slot's survival, exact (units of 2^-149)
-    float vc[kWideMaxN + 1];     // vc[T + B], B = 0 .. bmax
-    uint32_t wcnt[NT / 64][kWideSlots];
-    U192 wsum[NT / 64][kWideSlots];
-    WidePartial part[kWideSlots];
-    int claim;     // the share this workgroup takes next (rank_phase)
-    uint32_t bad;  // some confidence was sanitised
-};
-
-__device__ __forceinline__ U192 shfl_xor_192(const U192& x, int m) {
-    return U192{shfl_xor_u64(x.a, m), shfl_xor_u64(x.b, m), shfl_xor_u64(x.c, m)};
-}
-
-// Every slot's survival into the workgroup's LDS (its word and exact value) and the cost
-// table's entries B = 0 .. bmax: what every share of the ranking reads.
-template <int NT>
-__device__ __forceinline__ void rank_prepare(RankShared<NT>& sh, const RankArgs& ra) {
-    const int tid = threadIdx.x;
-    const float* __restrict__ conf = ra.conf;
-    const float* __restrict__ vc = ra.vc;
-    const int R = ra.R, K = ra.K, T = ra.T, bmax = ra.bmax;
-    if (tid == 0) sh.bad = 0u;
-
-    // survival of every slot (each thread one request at a time, eight confidences per
-    // memory round trip), and the cost-table entries B = 0 .. bmax, all requested before
-    // the first is used
-    constexpr int kVq = kWideMaxN / NT + 1;
-    float vq[kVq];
-#pragma unroll
-    for (int u = 0; u < kVq; ++u) vq[u] = tid + u * NT <= bmax ? vc[T + tid + u * NT] : 0.f;
-    bool bad = false;
-    __syncthreads();  // (sh.bad cleared)
-    for (int r = tid; r < R; r += NT) {
-        const int f0 = r * K;
-        float s = 0.f;
-        for (int i0 = 0; i0 < K; i0 += 8) {
-            float c[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = i0 + u < K ? conf[f0 + i0 + u] : 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u;
-                if (i < K) {
-                    const float cu = sanitize_conf(c[u], bad);
-                    s = (i == 0) ? cu : s * cu;
-                    sh.word[f0 + i] = slot_word(kOne - __float_as_uint(s), f0 + i);
-                    const U192 fs = fixed_from_bits(__float_as_uint(s));
-                    sh.fa[f0 + i] = fs.a;
-                    sh.fb[f0 + i] = fs.b;
-                    sh.fc[f0 + i] = fs.c;
-                }
-            }
-        }
-    }
-    if (bad) atomicOr(&sh.bad, 1u);
-#pragma unroll
-    for (int u = 0; u < kVq; ++u)
-        if (tid + u * NT <= bmax) sh.vc[tid + u * NT] = vq[u];
-    __syncthreads();
-}
-
-// Share g of the ranking: for slots [8g, 8g+8) the rank (the number of smaller words) and
-// the exact sum of the survivals ranked before (NT / 8 thread groups per slot count over a
-// part of the words each), then f(rank) and f(rank+1); order / sorted_surv, the slots'
-// ranks and the share's best candidates into the workspace.  Share 0 also writes the
-// survivals out and raises the sanitised-confidence flag.
-template <int NT>
-__device__ __forceinline__ void rank_share(RankShared<NT>& sh, const RankArgs& ra, int g) {
-    constexpr int kParts = NT / kWideSlots;  // thread groups counting for one slot
-    const int tid = threadIdx.x;
-    const int R = ra.R, K = ra.K, bmax = ra.bmax;
-    const int n = R * K;
-    WidePartial* parts = reinterpret_cast<WidePartial*>(ra.ws);
-    int32_t* rank_of = reinterpret_cast<int32_t*>(ra.ws + (size_t)kWideMaxGroups * kWidePartialBytes);
-    int32_t* __restrict__ order = ra.order;
-    float* __restrict__ sorted_surv = ra.sorted_surv;
-    uint32_t* status = ra.status;
-    const int n_sampling = ra.n_sampling;
-    const float dcost_f = ra.dc[ra.num_reqs];
-    if (g == 0) {
-        if (ra.surv)
-            for (int f = tid; f < n; f += NT) ra.surv[f] = __uint_as_float(kOne - word_key(sh.word[f]));
-        if (tid == 0 && sh.bad) raise_status(status, kStatusConfSanitized);
-    }
-
-    // this workgroup's slots: thread (el, pt) counts slot 8g + el over words [y0, y1)
-    const int el = tid % kWideSlots, pt = tid / kWideSlots;
-    const int x = g * kWideSlots + el;
-    const int lane = tid & 63, w = tid >> 6;
-    uint32_t cnt = 0u;
-    U192 S = {0ull, 0ull, 0ull};
-    if (x < n) {
-        const uint64_t wx = sh.word[x];
-        const int y0 = (int)(((long)pt * n) / kParts), y1 = (int)(((long)(pt + 1) * n) / kParts);
-        int y = y0;
-        for (; y + 4 <= y1; y += 4) {  // four words' reads in flight together
-            uint64_t wy[4], a[4], b[4], c[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                wy[u] = sh.word[y + u];
-                a[u] = sh.fa[y + u];
-                b[u] = sh.fb[y + u];
-                c[u] = sh.fc[y + u];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool lt = wy[u] < wx;
-                cnt += lt ? 1u : 0u;
-                S = add192(S, lt ? U192{a[u], b[u], c[u]} : U192{0ull, 0ull, 0ull});
-            }
-        }
-        for (; y < y1; ++y) {
-            const bool lt = sh.word[y] < wx;
-            cnt += lt ? 1u : 0u;
-            S = add192(S, lt ? U192{sh.fa[y], sh.fb[y], sh.fc[y]} : U192{0ull, 0ull, 0ull});
-        }
-    }
-    // the wave's eight groups of each slot (lanes el, el + 8, ..., el + 56), then the waves
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-        cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
-        S = add192(S, shfl_xor_192(S, m));
-    }
-    if (lane < kWideSlots) {
-        sh.wcnt[w][lane] = cnt;
-        sh.wsum[w][lane] = S;
-    }
-    __syncthreads();
-    if (tid < kWideSlots) {
-        WidePartial p = no_partial();
-        if (x < n) {
-            uint32_t rk = 0u;
-            U192 Sx = {0ull, 0ull, 0ull};
-#pragma unroll
-            for (int q = 0; q < NT / 64; ++q) {
-                rk += sh.wcnt[q][tid];
-                Sx = add192(Sx, sh.wsum[q][tid]);
-            }
-            const int r = (int)rk;
-            const uint64_t wx = sh.word[x];
-            if (order) order[r] = x;
-            if (sorted_surv) sorted_surv[r] = __uint_as_float(kOne - word_key(wx));
-            rank_of[x] = r;
-            const double dcost = (double)dcost_f;
-            const uint64_t ns_hi = (uint64_t)(uint32_t)n_sampling << 21;  // n_sampling * 2^149
-            bool badc = false;
-            auto eval = [&](const U192& s_excl, float vcost) -> double {
-                U192 X = s_excl;
-                X.c += ns_hi;
-                const double num = fixed_to_double(X);
-                const double den = (double)vcost + dcost;
-                if (den > 0.0 && den <= 1.7976931348623157e308) return num / den;
-                badc = true;
-                return -INFINITY;
-            };
-            // f(r) and f(r+1): the argmax candidate B = r + 1 (and B = 0 from rank 0), the
-            // first-drop test at B = r, and f(bmax) from whichever slot evaluates it
-            if (r <= bmax) {
-                const double fr = eval(Sx, sh.vc[r]);
-                if (r == 0) {
-                    p.f = fr;
-                    p.B = 0;
-                    if (bmax == 0) {
-                        p.fbmax = fr;
-                        p.has_fbmax = 1;
-                    }
-                }
-                if (r + 1 <= bmax) {
-                    const double f1 = eval(add192(Sx, U192{sh.fa[x], sh.fb[x], sh.fc[x]}), sh.vc[r + 1]);
-                    if (f1 > p.f || (f1 == p.f && r + 1 < p.B)) {
-                        p.f = f1;
-                        p.B = r + 1;
-                    }
-                    if (!(f1 > fr)) {
-                        p.drop = r;
-                        p.fdrop = fr;
-                    }
-                    if (r + 1 == bmax) {
-                        p.fbmax = f1;
-                        p.has_fbmax = 1;
-                    }
-                }
-            }
-            if (badc) raise_status(status, kStatusCostInvalid);
-        }
-        sh.part[tid] = p;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        WidePartial q = sh.part[0];
-        for (int e = 1; e < kWideSlots; ++e) merge_partial(q, sh.part[e]);
-        parts[g] = q;
-    }
-}
-
-// The ranking's shares taken one at a time from a device counter by a workgroup whose own
-// work is done (survivals prepared before its first share), until none is left.
-template <int NT>
-__device__ __forceinline__ void rank_phase(RankShared<NT>& sh, const RankArgs& ra) {
-    bool ready = false;
-    for (;;) {
-        if (threadIdx.x == 0) sh.claim = (int)atomicAdd(ra.claim, 1u);
-        __syncthreads();
-        const int g = sh.claim;
-        __syncthreads();
-        if (g >= ra.groups) break;
-        if (!ready) {
-            rank_prepare<NT>(sh, ra);
-            ready = true;
-        }
-        rank_share<NT>(sh, ra, g);
-    }
-}
-
 
 }  // namespace
 
