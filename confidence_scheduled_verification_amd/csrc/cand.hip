@@ -467,10 +467,12 @@ __device__ __forceinline__ void export_row(QLds& L, const CandArgs& a, int h, in
 }
 
 // The owner's import of share p >= 1 of row i: once the helper has written the row in this
-// launch (its epoch), the row's maximum, first NaN and kept groups join the owner's, and
-// the share's items are counted into the row.  A helper not heard from within the poll
-// limit, or with more groups than it could hand over, leaves the row to be scored densely.
-__device__ __forceinline__ void import_row(QLds& L, const CandArgs& a, int r, int p, int i, uint32_t ep) {
+// launch (its epoch), the row's maximum and first NaN join the owner's, and so do the
+// helper's kept groups that clear the floor of the row's maximum as now known (the helper
+// kept against its share's maximum alone); the share's items are counted into the row.  A
+// helper not heard from within the poll limit, or with more groups than it could hand
+// over, leaves the row to be scored densely.
+__device__ __forceinline__ void import_row(QLds& L, const CandArgs& a, int r, int p, int i, uint32_t ep, float ab2) {
     const int lane = threadIdx.x & 63;
     const int h = r * (a.S - 1) + p - 1;
     SplitHdr* hd = split_hdr(a, h, i);
@@ -498,21 +500,56 @@ __device__ __forceinline__ void import_row(QLds& L, const CandArgs& a, int r, in
         if (cnt > (uint32_t)kSplitCap) {
             if (lane == 0) L.rowover[i] = 1u;
         } else if (cnt != 0u) {
-            uint32_t at = 0u;
-            if (lane == 0) at = __hip_atomic_fetch_add(&L.rowfill[i], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            at = __builtin_amdgcn_readfirstlane(at);
-            take_chunks(L, i, at, cnt);
+            constexpr float kNegInf = -__builtin_huge_valf();
+            const uint32_t own = __hip_atomic_load(&L.rowmax[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t now = own > hmax ? own : hmax;
+            const float fl = now != 0u ? cand_floor(unord32(now), ab2) : kNegInf;
             u32x4* gd = split_grp(a) + split_row(a, h, i);
             uint32_t* gg = split_gid(a) + split_row(a, h, i);
             bool lost = false;
-            for (uint32_t e = (uint32_t)lane; e < cnt; e += 64u) {
-                const uint32_t q = at + e, c = q / kQChunk;
-                const uint32_t id = c < (uint32_t)kQChunks ? (uint32_t)L.ctab[i][c] : (uint32_t)kQNone;
-                if (id < (uint32_t)kQChunks) {
-                    L.grp[id * kQChunk + q % kQChunk] = get_grp(gd + e);
-                    L.gid[id * kQChunk + q % kQChunk] = (uint16_t)get_u32(gg + e);
-                } else {
-                    lost = true;
+            // four lists of 64 groups at a time, their loads all in flight together
+            for (uint32_t e0 = 0; e0 < cnt; e0 += 4u * 64u) {
+                u32x4 gv[4];
+                uint32_t iv[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t e = e0 + (uint32_t)b * 64u + (uint32_t)lane;
+                    if (e < cnt) {
+                        gv[b] = get_grp(gd + e);
+                        iv[b] = get_u32(gg + e);
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t e = e0 + (uint32_t)b * 64u + (uint32_t)lane;
+                    float gx = kNegInf;
+                    if (e < cnt) {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            gx = __builtin_elementwise_maximum(
+                                gx, __builtin_elementwise_maximum(__uint_as_float(gv[b][d] << 16),
+                                                                  __uint_as_float(gv[b][d] & 0xFFFF0000u)));
+                    }
+                    const bool keep = e < cnt && gx >= fl && gx > kNegInf;
+                    const uint64_t bal = __ballot(keep);
+                    const uint32_t nk = (uint32_t)__builtin_popcountll(bal);
+                    if (nk == 0u) continue;
+                    uint32_t at = 0u;
+                    if (lane == 0)
+                        at = __hip_atomic_fetch_add(&L.rowfill[i], nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    at = __builtin_amdgcn_readfirstlane(at);
+                    take_chunks(L, i, at, nk);
+                    if (keep) {
+                        const uint32_t q = at + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                        const uint32_t c = q / kQChunk;
+                        const uint32_t id = c < (uint32_t)kQChunks ? (uint32_t)L.ctab[i][c] : (uint32_t)kQNone;
+                        if (id < (uint32_t)kQChunks) {
+                            L.grp[id * kQChunk + q % kQChunk] = gv[b];
+                            L.gid[id * kQChunk + q % kQChunk] = (uint16_t)iv[b];
+                        } else {
+                            lost = true;
+                        }
+                    }
                 }
             }
             if (__ballot(lost) != 0ull && lane == 0) L.rowover[i] = 1u;
@@ -567,7 +604,7 @@ __device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, 
                     if (done == (uint32_t)n_own) export_row(L, a, r * (a.S - 1) + s - 1, i, ep);
                 }
             } else if constexpr (MODE == 2) {
-                import_row(L, a, r, t - n_own + 1, i, ep);
+                import_row(L, a, r, t - n_own + 1, i, ep, ab2);
             }
         }
     };
