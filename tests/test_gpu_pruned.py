@@ -170,3 +170,27 @@ def test_winner_at_the_edge_of_the_key_row_bound():
     tp, sp, sd, _ = _both_forms(c, R, K, V, rank)
     assert sp == sd == 0
     assert tp[0, 0] == v_win
+
+
+@pytest.mark.parametrize("R,K,V,rank", [
+    (8, 5, 30000, 64),     # 4 workgroups per request
+    (100, 3, 20000, 256),  # 2 per request
+    (3, 7, 9000, 32),      # 2 per request over 3 items a row, the fewest a split allows
+])
+def test_split_requests_match_one_workgroup_per_request(R, K, V, rank):
+    # With fewer requests than compute units each request is streamed by several
+    # workgroups whose helpers hand their kept groups to the owner through the workspace.
+    # A workspace without room for those groups keeps one workgroup per request: both
+    # must give the oracle's tokens, and the same ones (the argmax is unique here).
+    gu.say(f"split vs whole requests R={R} K={K} V={V} rank={rank}")
+    c = _case(77 + R * 13 + V % 101, R, K, V, rank)
+    ch = gu.Chain(c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    split, _, st_split = ch.run()
+    small = B.workspace(256, K, V, rank, inputs.BF16)  # the minimum at R <= 256: no room for the split
+    assert small.numel() * 8 < B.dspark_workspace_bytes(R, K, V, rank, inputs.BF16)
+    ch.ws = small
+    whole, _, st_whole = ch.run()
+    assert st_split == st_whole == 0
+    split, whole = split.cpu().numpy(), whole.cpu().numpy()
+    gu.assert_chain_parity(split, None, c["base"], c["A"], c["Bmat"], inputs.BF16, c["prev0"])
+    np.testing.assert_array_equal(split, whole)
