@@ -102,7 +102,8 @@ const char* dspark_version(void);
  * units (the helpers hand their kept candidates over through it); the calls also accept a
  * smaller workspace, down to the size without that room (DSPARK_EINVAL below it), and then
  * stream each request with one workgroup.  So a workspace sized for one shape serves any
- * smaller R and K and any V, rank and dtype. */
+ * smaller R and K and any V, rank and dtype.  Calls that share a workspace must not
+ * overlap (enqueue them on one stream, or order them with events). */
 size_t dspark_workspace_bytes(int R, int K, int V, int rank, int dtype);
 
 /*
