@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restr
 // launches (the boundary between them is cheaper than a device-wide fence and counter):
 //   sched_rank_kernel, workgroup g: survival of all n slots into LDS (their words and
 //     exact values); for slots [8g, 8g+8) the rank (the number of smaller words) and the
-//     exact sum of the survivals ranked before (32 thread groups per slot count over a
+//     exact sum of the survivals ranked before (64 thread groups per slot count over a
 //     share of the words each), so S_rank needs no scan; then f(rank) and f(rank+1),
 //     i.e. every B the argmax and the first-drop rule look at, order / sorted_surv and
 //     the workgroup's best candidates into the workspace;
@@ -108,8 +108,9 @@ __global__ __launch_bounds__(kST, 1) void allocate_kernel(const int32_t* __restr
 // f(B) is computed from the same exact integer S_B and the same rounding as in the
 // one-workgroup kernel, so B* and f(B*) are the same doubles.
 
-constexpr int kWT = 256;                     // threads per workgroup
-constexpr int kWParts = kWT / kWideSlots;    // thread groups counting for one slot
+constexpr int kWT = 256;                     // threads of the finish workgroup
+constexpr int kWR = 512;                     // threads of a ranking workgroup
+constexpr int kWRParts = kWR / kWideSlots;   // thread groups counting for one slot
 constexpr int kNone = 0x7FFFFFFF;
 
 struct WidePartial {  // kWidePartialBytes
@@ -156,8 +157,8 @@ struct RankShared {
     uint64_t word[kWideMaxN];    // slot words in flat order
     uint64_t fa[kWideMaxN], fb[kWideMaxN], fc[kWideMaxN];  // each slot's survival, exact (units of 2^-149)
     float vc[kWideMaxN + 1];     // vc[T + B], B = 0 .. bmax
-    uint32_t wcnt[kWT / 64][kWideSlots];
-    U192 wsum[kWT / 64][kWideSlots];
+    uint32_t wcnt[kWR / 64][kWideSlots];
+    U192 wsum[kWR / 64][kWideSlots];
     WidePartial part[kWideSlots];
 };
 
@@ -165,7 +166,7 @@ __device__ __forceinline__ U192 shfl_xor_192(const U192& x, int m) {
     return U192{shfl_xor_u64(x.a, m), shfl_xor_u64(x.b, m), shfl_xor_u64(x.c, m)};
 }
 
-__global__ __launch_bounds__(kWT) void sched_rank_kernel(
+__global__ __launch_bounds__(kWR) void sched_rank_kernel(
     const float* __restrict__ conf, int R, int K, int n_sampling, int T, int num_reqs, const float* __restrict__ vc,
     const float* __restrict__ dc, int bmax, float* __restrict__ surv_out, int32_t* __restrict__ order,
     float* __restrict__ sorted_surv, uint32_t* status, unsigned char* __restrict__ ws) {
@@ -178,13 +179,13 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
     // survival of every slot (each thread one request at a time, eight confidences per
     // memory round trip), and the cost-table entries B = 0 .. bmax, all requested before
     // the first is used
-    constexpr int kVq = kWideMaxN / kWT + 1;
+    constexpr int kVq = kWideMaxN / kWR + 1;
     float vq[kVq];
 #pragma unroll
-    for (int u = 0; u < kVq; ++u) vq[u] = tid + u * kWT <= bmax ? vc[T + tid + u * kWT] : 0.f;
+    for (int u = 0; u < kVq; ++u) vq[u] = tid + u * kWR <= bmax ? vc[T + tid + u * kWR] : 0.f;
     const float dcost_f = dc[num_reqs];
     bool bad = false;
-    for (int r = tid; r < R; r += kWT) {
+    for (int r = tid; r < R; r += kWR) {
         const int f0 = r * K;
         float s = 0.f;
         for (int i0 = 0; i0 < K; i0 += 8) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
     if (bad && g == 0) raise_status(status, kStatusConfSanitized);
 #pragma unroll
     for (int u = 0; u < kVq; ++u)
-        if (tid + u * kWT <= bmax) sh.vc[tid + u * kWT] = vq[u];
+        if (tid + u * kWR <= bmax) sh.vc[tid + u * kWR] = vq[u];
     __syncthreads();
 
     // this workgroup's slots: thread (el, pt) counts slot 8g + el over words [y0, y1)
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
     U192 S = {0ull, 0ull, 0ull};
     if (x < n) {
         const uint64_t wx = sh.word[x];
-        const int y0 = (int)(((long)pt * n) / kWParts), y1 = (int)(((long)(pt + 1) * n) / kWParts);
+        const int y0 = (int)(((long)pt * n) / kWRParts), y1 = (int)(((long)(pt + 1) * n) / kWRParts);
         int y = y0;
         for (; y + 4 <= y1; y += 4) {  // four words' reads in flight together
             uint64_t wy[4], a[4], b[4], c[4];
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kWT) void sched_rank_kernel(
             uint32_t rk = 0u;
             U192 Sx = {0ull, 0ull, 0ull};
 #pragma unroll
-            for (int q = 0; q < kWT / 64; ++q) {
+            for (int q = 0; q < kWR / 64; ++q) {
                 rk += sh.wcnt[q][tid];
                 Sx = add192(Sx, sh.wsum[q][tid]);
             }
@@ -474,7 +475,7 @@ hipError_t launch_sched_wide(const FusedSchedArgs& a, hipStream_t s) {
     if (n <= 0 || n > kWideMaxN || a.sizing.separate || !a.ws) return hipErrorInvalidValue;
     const int G = (n + kWideSlots - 1) / kWideSlots;
     unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
-    hipLaunchKernelGGL(sched_rank_kernel, dim3(G), dim3(kWT), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs,
+    hipLaunchKernelGGL(sched_rank_kernel, dim3(G), dim3(kWR), 0, s, a.conf, a.R, a.K, a.n_sampling, a.T, a.num_reqs,
                        a.vc, a.dc, a.bmax, a.surv, a.order, a.sorted_surv, a.status, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
