@@ -82,17 +82,18 @@ def chain_kernel(w, num_cu: int = 256, form: int = 0) -> dict:
     return {"kernel": name, "bytes_per_launch": b, "launches_per_step": w.K}
 
 
-def traffic_per_launch(kernel: str):
-    """Measured HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration), or None
-    when any source of the kernel has changed since the counters were taken."""
+def traffic_per_launch(kernel: str, workload: str):
+    """Measured HBM bytes per launch of `kernel` at `workload` from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration), or None
+    when the counters were taken at another workload or any source of the kernel has
+    changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec:
+    if not rec or not rec.get("workload", "").startswith(workload + ":"):
         return None
     h = hashlib.sha256()
     for src in rec["sources"]:
@@ -680,7 +681,7 @@ def main():
     launch_s = chain_ms.mean() * 1e-3 / ck["launches_per_step"]   # event-timed chain phase per launch
     achieved = ck["bytes_per_launch"] / launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ck["kernel"]), **ck,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(ck["kernel"], w.name), **ck,
                 "launch_us": round(launch_s * 1e6, 2),
                 "practical_peak": {"kind": "plain device copy, 1 GiB read + 1 GiB written", "gbs": round(copy_gbs, 1),
                                    "frac": round(achieved / copy_gbs, 4)}}
