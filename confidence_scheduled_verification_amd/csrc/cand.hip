@@ -24,8 +24,10 @@
 // pool, or weights whose bound is not finite, are scored densely.
 //
 // One workgroup per compute unit takes requests g, g + G, ... whole, so a request's
-// candidates never leave the compute unit's LDS.  Its eight waves (two per SIMD) split
-// the work:
+// candidates never leave the compute unit's LDS (with fewer requests than compute units,
+// helper workgroups stream shares of a request's rows and hand their kept groups over;
+// see "One request over several workgroups" below).  Its eight waves (two per SIMD)
+// split the work:
 //
 // Streaming (waves 0-6).  The request's K*V base entries are items of 4096 entries (a row
 // is ceil(V/4096) items); a wave takes the next item from an LDS counter whenever it
@@ -38,15 +40,15 @@
 // that claims a chunk's first place takes from the pool; then the item is counted into
 // its row.
 //
-// Chain (wave 7), concurrently.  Position by position it waits for the row's count to
-// reach its item count, lists the entries of the row's kept groups that clear the row's
-// final floor, and scores them with the key row of the previous token, two lanes per candidate with the
-// whole Bt rows of up to 64 candidates in flight at once (x = value + the dot product,
-// each lane's half by fused multiply-adds in increasing k, then the halves added).  The
-// key row of the next position is prefetched for the row's largest entry -- the token
-// unless the bias reorders the top -- while the row is scored, and loaded again only
-// when that guess misses.  So the chain keeps up with the streaming, and only the last
-// row's scoring is left once the last item arrives.
+// Chain (wave 7), concurrently, at raised issue priority.  Position by position it waits
+// for the row's count to reach its item count, lists the entries of the row's kept groups
+// that clear the row's final floor, and scores them with the key row of the previous
+// token, two lanes per candidate with the whole Bt rows of up to 64 candidates in flight
+// at once (x = value + the dot product, each lane's half by fused multiply-adds in
+// increasing k, then the halves added).  The key row of the next position is prefetched
+// for the row's largest entry -- the token unless the bias reorders the top -- while the
+// row is scored, and loaded again only when that guess misses.  So the chain keeps up
+// with the streaming, and only the last row's scoring is left once the last item arrives.
 #include "common.h"
 #include "kernels.h"
 
