@@ -6,9 +6,9 @@
  * Semi-autoregressive chaining of a K-token draft block, written out plainly in
  * double precision, one request row and one position at a time.
  *
- * What it computes (DSpark summary, "Draft better": a lightweight Markov head
- * nudges each position's odds using only the token chosen just before it,
- * stored as a rank-256 factorisation; MAX worklog, "What DSpark is", item 3:
+ * What it computes (DSpark summary, "Draft better": a first-order Markov term,
+ * held as a rank-256 factorisation and indexed by the previous position's
+ * token, is added to each position's logits; MAX worklog, "What DSpark is", item 3:
  * the chain adds a rank-r term selected by the token chosen one position
  * earlier and takes an argmax):
  *

@@ -26,9 +26,9 @@ Readings of what the pages leave open:
   * the compacted verification list holds flat slot ids r*K+i, ordered by
     request then position, padded with -1 to R*K entries;
   * the first-drop admission rule (AlphaSignal's DSpark summary "How DSpark
-    Speeds Up LLM Inference", section "Verify smarter": slots are admitted in
-    rank order while throughput keeps rising, and admission stops as soon as it
-    would fall) admits slot B+1 only when f(B+1) > f(B) strictly, so it stops at
+    Speeds Up LLM Inference", section "Verify smarter": slots enter in rank
+    order for as long as each one raises the throughput, and the first one that
+    would lower it ends admission) admits slot B+1 only when f(B+1) > f(B) strictly, so it stops at
     the smallest B of a plateau, as the argmax rule does;
   * stale sizing (vLLM blog, "Scheduling the budget": B is sized from a
     confidence array one step old while the slots are handed out with current

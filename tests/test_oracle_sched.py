@@ -216,8 +216,8 @@ def test_cost_jump_right_after_T_gives_zero_budget():
 
 def test_linear_cost_argmax_equals_greedy_first_drop():
     # For cost a + b t the ratio is quasi-concave in B (a concave numerator over a positive
-    # affine denominator), so the global argmax and the "admit one at a time while
-    # throughput rises" rule agree.
+    # affine denominator), so the global argmax and the rule that stops admitting at the
+    # first slot that lowers throughput agree.
     for seed in range(5):
         rng = np.random.default_rng(100 + seed)
         w = inputs.WORKLOADS["headline"]
@@ -282,8 +282,8 @@ def test_first_drop_against_exact_objective():
 
 def test_first_drop_stops_at_a_plateau():
     # Flat cost: f rises with every positive survival, then stays flat over zero-survival
-    # slots.  "While throughput keeps rising" stops at the first flat step, where the
-    # argmax's smallest maximiser is as well.
+    # slots.  The strict first-drop rule stops at the first flat step, where the argmax's
+    # smallest maximiser is as well.
     rng = np.random.default_rng(5)
     conf = rng.uniform(0.5, 1.0, size=(6, 5)).astype(np.float32)
     conf[1, 2] = 0.0
