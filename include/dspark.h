@@ -165,8 +165,8 @@ int dspark_markov_prepare(dspark_markov_t* m, const void* A, const void* Bmat, i
  * DSPARK_PRUNED_MAX_K and V <= DSPARK_PRUNED_MAX_V runs the pruned chain by default:
  * one streaming pass over base keeps each row's entries within the bias bound of its
  * maximum (the only ones that can win), then every request's chain scores those
- * candidates alone (fp32 fused multiply-adds in increasing k within 32-entry slices,
- * slices summed pairwise).  Rows the bound cannot prune (a non-finite bound, more
+ * candidates alone (fp32 fused multiply-adds in increasing k over each half of the
+ * rank, then the two halves added, lower half first).  Rows the bound cannot prune (a non-finite bound, more
  * candidates than the buffers hold) are scored over the whole vocabulary, so the
  * tokens never depend on how well the bound prunes.  Otherwise (and in the dense form)
  * bf16 products are summed in fp32 by the matrix cores over the whole vocabulary;
@@ -296,7 +296,9 @@ int dspark_allocate(const int32_t* order, const int32_t* b_star, int R, int K, c
  * outputs (surv, order, sorted_surv may be NULL).  conf holds R rows (the drafting
  * requests), R*K <= DSPARK_MAX_SLOTS.
  * Order.  Where the pruned chain applies (see dspark_chain), the chain runs first and
- * stages 2-5 start once it has ended, in a second launch: in the method the
+ * stages 2-5 start once it has ended, in launches of their own on the same stream (with
+ * R*K <= 2048 and sizing from the current confidences, a ranking launch over many
+ * workgroups and a one-workgroup finish; otherwise one workgroup): in the method the
  * confidences score the drafted tokens, so the schedule follows the chain (DSpark
  * summary, Figure 1).  Otherwise (and in the dense form) it is ONE launch when the grid
  * fits on the device at once -- one workgroup per 512 vocabulary entries plus one
