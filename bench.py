@@ -587,8 +587,9 @@ def main():
     loop_ms = g0.elapsed_time(g1)
     log(f"bench: wall {wall * 1e3 / K:.2f} ms/step, events {loop_ms * 1e3 / K:.1f} us/step")
 
-    # Pass 2: the same steps with HIP events recorded by the library around the chain
-    # kernel(s) on the step's stream, for the kernel-level roofline.
+    # Pass 2: the same steps with HIP events set by the library around the chain on the
+    # step's stream, for the kernel-level roofline (for the pruned chain they take the
+    # kernel's own start and stop time; otherwise they are markers around its launches).
     KE = max(1, min(args.event_steps, K))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KE)]
     for e in ev:
@@ -728,7 +729,9 @@ def main():
                        "before_chain_us": round(float(pre_ms.mean()) * 1e3, 2),
                        "chain_us": round(float(chain_ms.mean()) * 1e3, 2),
                        "after_chain_us": round(float(post_ms.mean()) * 1e3, 2),
-                       "note": "four timing events per step add their own time between launches"},
+                       "note": ("chain_us: the pruned chain kernel's own start to stop (its launch carries "
+                                "the events), else markers around the chain launches; the markers before "
+                                "and after the step add their own time to the other parts")},
         "parity_last_step": "ok" if checked[K - 1] else "MISMATCH",
         "parity": parity,
         "parity_steps": {str(k): ("ok" if v else "MISMATCH") for k, v in sorted(checked.items())},

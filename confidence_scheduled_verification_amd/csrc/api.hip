@@ -349,13 +349,10 @@ int dspark_step_sized(const void* base, const void* A, const void* Bmat, int dty
     if (n > 0 && use_pruned(dtype, R, K, V, A, nullptr)) {
         // the chain, then stages 2-5 over the confidences and the verified tokens (in the
         // method the confidences score the drafted tokens, so the schedule follows)
-        if (g_ev_before_chain && (e = hipEventRecord(g_ev_before_chain, s)) != hipSuccess)
-            return hip_fail(e, "step (timing event)");
+        // (timing events, when set, take the chain kernel's own start and stop time)
         const dspark::CandArgs ca = cand_args(base, markov, prev0, R, K, V, rank, tokens, status, ws, ws_bytes);
-        e = dspark::launch_cand(ca, num_cu(), s);
+        e = dspark::launch_cand(ca, num_cu(), s, g_ev_before_chain, g_ev_after_chain);
         if (e != hipSuccess) return hip_fail(e, "step (pruned chain)");
-        if (g_ev_after_chain && (e = hipEventRecord(g_ev_after_chain, s)) != hipSuccess)
-            return hip_fail(e, "step (timing event)");
         dspark::FusedSchedArgs sa{conf,   R,        K,          n_sampling, T,      num_reqs, verify_cost,
                                   draft_cost, bmax, sizing,    surv,       order,  sorted_surv, b_star,
                                   best_obj, prefix_len, offsets, ver_idx,   status, nullptr, 0,

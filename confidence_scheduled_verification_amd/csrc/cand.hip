@@ -49,6 +49,8 @@
 // for the row's largest entry -- the token unless the bias reorders the top -- while the
 // row is scored, and loaded again only when that guess misses.  So the chain keeps up
 // with the streaming, and only the last row's scoring is left once the last item arrives.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -960,7 +962,7 @@ hipError_t launch_markov_bound(const void* A, const void* Bt, int V, int rank, v
     return hipGetLastError();
 }
 
-hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s) {
+hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     // one workgroup per compute unit, at most one per request, or S per request
     int grid = num_cu < kCandMaxGroups ? num_cu : kCandMaxGroups;
     if (grid > a.R) grid = a.R;
@@ -970,6 +972,7 @@ hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s) {
     // 16-byte loads of the base logits need 8 | V and an aligned base
     const bool vec = a.V % 8 == 0 && ((uintptr_t)a.base & 15u) == 0;
     const void* fn = vec ? (const void*)cand_chain_kernel<true> : (const void*)cand_chain_kernel<false>;
+    if (start || stop) return hipExtLaunchKernel(fn, dim3(grid), dim3(kQT), args, 0, s, start, stop, 0);
     return hipLaunchKernel(fn, dim3(grid), dim3(kQT), args, 0, s);
 }
 

@@ -228,7 +228,9 @@ hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes,
 hipError_t launch_markov_bound(const void* A, const void* Bt, int V, int rank, void* hdr, hipStream_t s);
 // The candidate-pruned chain: one 512-thread workgroup per compute unit (at most
 // kCandMaxGroups of them), or R S workgroups when a request is split (a.S > 1).
-hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s);
+// start / stop: when non-null, events that take the kernel's own start and stop time.
+hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 hipError_t launch_survival(const float* conf, int R, int K, float* surv, uint32_t* status, hipStream_t s);
 hipError_t launch_topb(const float* surv, int R, int K, int32_t* order, float* sorted_surv, int32_t* rank,

@@ -443,13 +443,14 @@ int dspark_set_launch_mode(int mode);
 int dspark_get_launch_mode(void);
 
 /*
- * Measurement hook.  When set (non-NULL hipEvent_t handles), every later
- * dspark_step call on this thread records `before_chain` on its stream right before
- * the first chain kernel, and `after_chain` right after the last chain kernel (for a
- * single-launch step, around that launch), so a caller can time the chain with
- * hipEventElapsedTime.
- * Pass NULLs to turn it off (the default).  Recording an event enqueues a marker
- * only; no synchronisation happens.
+ * Measurement hook.  When set (non-NULL hipEvent_t handles, created before the call),
+ * every later dspark_step call on this thread sets `before_chain` and `after_chain` on
+ * its stream around the chain, so a caller can time the chain with
+ * hipEventElapsedTime: for the pruned chain (one kernel) they take that kernel's own
+ * start and stop time (hipExtLaunchKernel); otherwise they are markers recorded right
+ * before the first chain kernel and right after the last (for a single-launch step,
+ * around that launch).
+ * Pass NULLs to turn it off (the default).  No synchronisation happens.
  */
 int dspark_set_timing_events(void* before_chain, void* after_chain);
 
