@@ -443,7 +443,9 @@ def dspark_get_launch_mode() -> int:
 
 
 def dspark_set_timing_events(before_chain=None, after_chain=None):
-    """Events (torch.cuda.Event or raw handles) that later dspark_step calls record around the chain."""
+    """Events (torch.cuda.Event or raw handles, already created) that later dspark_step calls on
+    this thread set around the chain: the pruned chain kernel's own start and stop, else
+    markers before and after the chain's launches."""
     def h(e):
         return None if e is None else (e if isinstance(e, int) else e.cuda_event)
     _check(lib().dspark_set_timing_events(h(before_chain), h(after_chain)))

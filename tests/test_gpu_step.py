@@ -68,6 +68,35 @@ def test_step_is_deterministic_and_equals_stagewise():
     assert np.all(a["ver_tokens"][a["b_star"]:] == -1)
 
 
+@pytest.mark.parametrize("name,form", [("mid", "pruned"), ("headline", "pruned"), ("headline", "dense")])
+def test_timing_events_leave_the_step_unchanged(name, form):
+    # With timing events set, the pruned chain's launch carries them (they take the kernel's
+    # own start and stop; Mid splits its requests, the Headline does not) and the dense form
+    # records them as markers: the step's results are the same as without, and the events
+    # bracket a positive time.
+    w = inputs.WORKLOADS[name]
+    gu.say(f"timing events {name} {form}")
+    ins = inputs.generate(w)
+    vc, dc = gu.forced_tables(w, ins)
+    with gu.chain_form(gu.FORMS[form]):
+        ch = gu.Chain(ins.base, ins.A, ins.Bmat, w.dtype, ins.prev0)
+        a, sa, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+        e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e1.record()
+        e2.record()  # the HIP events exist before the library sets them
+        torch.cuda.synchronize()
+        B.dspark_set_timing_events(e1, e2)
+        try:
+            b, sb, _ = gu.run_step(ch, ins.conf, w.n_sampling, w.T, w.R_all, vc, dc)
+        finally:
+            B.dspark_set_timing_events(None, None)
+    assert sa == sb == 0
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    ms = e1.elapsed_time(e2)
+    assert 0.0 < ms < 1000.0, ms
+
+
 def test_multi_step_inputs_change_the_result():
     w = inputs.WORKLOADS["small"]
     ins = inputs.generate(w)
