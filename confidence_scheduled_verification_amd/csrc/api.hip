@@ -98,6 +98,7 @@ dspark::CandArgs cand_args(const void* base, const dspark_markov_t* m, const int
     a.K = K;
     a.V = V;
     a.rank = rank;
+    a.item = dspark::cand_item(V);
     a.NC = dspark::cand_items_per_row(V);
     a.tokens = tokens;
     a.status = status;

@@ -29,8 +29,8 @@
 // see "One request over several workgroups" below).  Its eight waves (two per SIMD)
 // split the work:
 //
-// Streaming (waves 0-6).  The request's K*V base entries are items of 4096 entries (a row
-// is ceil(V/4096) items); a wave takes the next item from an LDS counter whenever it
+// Streaming (waves 0-6).  The request's K*V base entries are items of 4096 entries, 2048
+// in rows of at most 32768 (a row is ceil(V/item) items); a wave takes the next item from an LDS counter whenever it
 // starts a load, keeps the next item's loads in flight, and never waits for the other
 // waves.  For each item it folds the item's maximum into the row's maximum in LDS
 // and keeps, whole, every 8-entry group whose maximum clears the floor of the row's
@@ -60,7 +60,8 @@ namespace {
 
 constexpr int kQS = 7;                   // streaming waves (with the chain wave, two waves per SIMD)
 constexpr int kQT = (kQS + 1) * 64;      // threads per workgroup: the streaming waves and the chain wave
-constexpr int kQItem = kCandItem;        // base entries per item: 64 lanes x 8 loads x 8 entries
+// Items are LOADS x 512 entries: 64 lanes x LOADS 16-byte loads x 8 entries (LOADS = 8 for
+// items of kCandItemLong entries, 4 for kCandItemShort).
 constexpr int kQChunk = 64;              // kept groups per chunk of the pool
 constexpr int kQChunks = kCandGroups / kQChunk;  // chunks of the pool
 constexpr uint8_t kQUnset = 0xFF;        // chunk table: not taken yet
@@ -74,7 +75,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 static_assert(kQChunks <= 0xFE, "chunk numbers fit a byte beside the two marks");
-static_assert((long)kCandMaxItems * kQItem / 8 <= 65536, "group numbers within a row fit 16 bits");
+static_assert((long)kCandMaxItems * kCandItemLong / 8 <= 65536, "group numbers within a row fit 16 bits");
+static_assert(kCandItemLong == 8 * 512 && kCandItemShort == 4 * 512, "items are whole 512-entry loads");
 
 // Order-preserving image of a float in the unsigned integers (NaN above every number,
 // -0 equal to +0); never 0.
@@ -227,14 +229,14 @@ __device__ __forceinline__ void lds_writes_done() {
 // ---------------------------------------------------------------------------------
 // Streaming
 
-// Entries [v0, v0 + 4096) of a row into buf (8 groups of 8 entries per lane; entries past
-// V read as -inf).  VEC: 8 | V and an aligned base, so groups are 16-byte aligned and
+// Entries [v0, v0 + 512 LOADS) of a row into buf (LOADS groups of 8 entries per lane;
+// entries past V read as -inf).  VEC: 8 | V and an aligned base, so groups are 16-byte aligned and
 // wholly in or out of the row.
-template <bool VEC>
-__device__ __forceinline__ void load_item(u32x4 (&buf)[8], const uint16_t* __restrict__ p, int v0, int V) {
+template <bool VEC, int LOADS>
+__device__ __forceinline__ void load_item(u32x4 (&buf)[LOADS], const uint16_t* __restrict__ p, int v0, int V) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < LOADS; ++q) {
         const int e = v0 + q * 512 + lane * 8;
         if (VEC) {
             // every load is issued (past the row, at the row's start), so that the number of
@@ -251,10 +253,11 @@ __device__ __forceinline__ void load_item(u32x4 (&buf)[8], const uint16_t* __res
     }
 }
 
-// The maxima of an item's eight 8-entry groups (per lane).
-__device__ __forceinline__ void group_maxima(const u32x4 (&cur)[8], float (&gm)[8]) {
+// The maxima of an item's LOADS 8-entry groups (per lane).
+template <int LOADS>
+__device__ __forceinline__ void group_maxima(const u32x4 (&cur)[LOADS], float (&gm)[LOADS]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < LOADS; ++q) {
         float g = -__builtin_huge_valf();
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -303,20 +306,21 @@ __device__ __forceinline__ void take_chunks(QLds& L, int i, uint32_t at, uint32_
 // after it is returned).  A group of
 // -inf entries never wins unless the whole row is -inf, which is handled apart, so it is
 // never kept.
-__device__ __forceinline__ uint32_t keep_item(QLds& L, const u32x4 (&cur)[8], int i, int v0, float ab2) {
+template <int LOADS>
+__device__ __forceinline__ uint32_t keep_item(QLds& L, const u32x4 (&cur)[LOADS], int i, int v0, float ab2) {
     const int lane = threadIdx.x & 63;
     constexpr float kNegInf = -__builtin_huge_valf();
-    float gm[8];
-    group_maxima(cur, gm);
+    float gm[LOADS];
+    group_maxima<LOADS>(cur, gm);
     float m = gm[0];
 #pragma unroll
-    for (int q = 1; q < 8; ++q) m = __builtin_elementwise_maximum(m, gm[q]);
+    for (int q = 1; q < LOADS; ++q) m = __builtin_elementwise_maximum(m, gm[q]);
     const float mw = wave_max(m);
     if (mw != mw) {
         // the row's token is its first NaN, whatever the bias
         uint32_t first = 0xFFFFFFFFu;
 #pragma unroll
-        for (int q = 7; q >= 0; --q) {
+        for (int q = LOADS - 1; q >= 0; --q) {
             if (gm[q] != gm[q]) {
 #pragma unroll
                 for (int s = 7; s >= 0; --s) {
@@ -335,7 +339,7 @@ __device__ __forceinline__ uint32_t keep_item(QLds& L, const u32x4 (&cur)[8], in
         const float fl = cand_floor(unord32(now), ab2);
         uint32_t need = 0u;  // bit q: group q of this lane is kept
 #pragma unroll
-        for (int q = 0; q < 8; ++q) need |= (gm[q] >= fl && gm[q] > kNegInf) ? (1u << q) : 0u;
+        for (int q = 0; q < LOADS; ++q) need |= (gm[q] >= fl && gm[q] > kNegInf) ? (1u << q) : 0u;
         uint32_t total = 0;
         const uint32_t before = wave_excl_scan_small((uint32_t)__builtin_popcount(need), &total);
         if (total != 0u) {
@@ -352,7 +356,7 @@ __device__ __forceinline__ uint32_t keep_item(QLds& L, const u32x4 (&cur)[8], in
             const uint32_t g0 = ((uint32_t)v0 >> 3) + (uint32_t)lane;
             bool lost = false;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < LOADS; ++q) {
                 if (__ballot((need >> q) & 1u) == 0ull) continue;
                 if ((need >> q) & 1u) {
                     const uint32_t id = p / kQChunk == ca ? ida : idb;
@@ -575,9 +579,10 @@ __device__ __forceinline__ void import_row(QLds& L, const CandArgs& a, int r, in
 // loading one, so that waves which happen to be served faster take more, and tasks are
 // taken in order (rows complete in order).  Each item is loaded one item ahead (two
 // buffers in turn); a task that is no item (an import, or past the request) loads nothing
-// (v0 = V: every entry reads as -inf).
-template <bool VEC, int MODE>
+// (v0 = V: every entry reads as -inf).  Items are 512 LOADS entries.
+template <bool VEC, int MODE, int LOADS>
 __device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, int s, float ab2, uint32_t ep) {
+    constexpr int kItem = LOADS * 512;
     const int K = a.K, NC = a.NC, V = a.V;
     const int S = MODE == 0 ? 1 : a.S;
     const int n_own = share_items(s, NC, S);
@@ -594,16 +599,16 @@ __device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, 
         if ((threadIdx.x & 63) == 0) j = atomicAdd(&L.next, 1u);
         return (int)__builtin_amdgcn_readfirstlane(j);
     };
-    auto issue = [&](u32x4 (&buf)[8], int j) {
+    auto issue = [&](u32x4 (&buf)[LOADS], int j) {
         const int i = j / T, t = j - i * T;
         const bool ok = j < per_req && t < n_own;
-        load_item<VEC>(buf, rbase + (size_t)(ok ? i : 0) * V, ok ? item_of(t) * kQItem : V, V);
+        load_item<VEC, LOADS>(buf, rbase + (size_t)(ok ? i : 0) * V, ok ? item_of(t) * kItem : V, V);
     };
-    auto take = [&](const u32x4 (&buf)[8], int j) {
+    auto take = [&](const u32x4 (&buf)[LOADS], int j) {
         if (j < per_req) {
             const int i = j / T, t = j - i * T;
             if (t < n_own) {
-                const uint32_t done = keep_item(L, buf, i, item_of(t) * kQItem, ab2);
+                const uint32_t done = keep_item<LOADS>(L, buf, i, item_of(t) * kItem, ab2);
                 if constexpr (MODE == 1) {
                     if (done == (uint32_t)n_own) export_row(L, a, r * (a.S - 1) + s - 1, i, ep);
                 }
@@ -614,7 +619,7 @@ __device__ __forceinline__ void stream_tasks(QLds& L, const CandArgs& a, int r, 
     };
     // (one item ahead already reads at the device's rate, and the chain wave's own loads
     // then queue behind fewer of the streams' than with two)
-    u32x4 b0[8], b1[8];
+    u32x4 b0[LOADS], b1[LOADS];
     int j0 = claim(), j1;
     issue(b0, j0);
     while (j0 < per_req) {
@@ -883,7 +888,7 @@ __device__ __forceinline__ void run_chain(const CandArgs& a, QLds& L, int r, con
 // first R (S - 1) workgroups are the helpers (dispatched first, and they never wait for
 // another workgroup), the last R the owners.  The launch's epoch is one more than the
 // workspace's; the last workgroup to finish stores it there for the next launch.
-template <bool VEC>
+template <bool VEC, int LOADS>
 __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
     __shared__ QLds S;
     const HeaderView hv = header_view(a.hdr);
@@ -900,9 +905,9 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
         __syncthreads();
         const uint32_t ep = ep_lds;
         if (helper)
-            stream_tasks<VEC, 1>(S, a, r, s, hv.ab2, ep);
+            stream_tasks<VEC, 1, LOADS>(S, a, r, s, hv.ab2, ep);
         else if ((int)(threadIdx.x >> 6) < kQS)
-            stream_tasks<VEC, 2>(S, a, r, 0, hv.ab2, ep);
+            stream_tasks<VEC, 2, LOADS>(S, a, r, 0, hv.ab2, ep);
         else
             run_chain(a, S, r, hv);
         __syncthreads();
@@ -914,7 +919,7 @@ __global__ __launch_bounds__(kQT, 1) void cand_chain_kernel(CandArgs a) {
         reset_request(S, a.K);
         __syncthreads();
         if ((int)(threadIdx.x >> 6) < kQS)
-            stream_tasks<VEC, 0>(S, a, r, 0, hv.ab2, 0u);
+            stream_tasks<VEC, 0, LOADS>(S, a, r, 0, hv.ab2, 0u);
         else
             run_chain(a, S, r, hv);
         __syncthreads();  // the request's LDS is read before the next one is streamed into it
@@ -971,7 +976,10 @@ hipError_t launch_cand(const CandArgs& a, int num_cu, hipStream_t s, hipEvent_t 
     void* args[] = {&arg};
     // 16-byte loads of the base logits need 8 | V and an aligned base
     const bool vec = a.V % 8 == 0 && ((uintptr_t)a.base & 15u) == 0;
-    const void* fn = vec ? (const void*)cand_chain_kernel<true> : (const void*)cand_chain_kernel<false>;
+    if (a.item != kCandItemLong && a.item != kCandItemShort) return hipErrorInvalidValue;
+    const bool lng = a.item == kCandItemLong;
+    const void* fn = vec ? (lng ? (const void*)cand_chain_kernel<true, 8> : (const void*)cand_chain_kernel<true, 4>)
+                         : (lng ? (const void*)cand_chain_kernel<false, 8> : (const void*)cand_chain_kernel<false, 4>);
     if (start || stop) return hipExtLaunchKernel(fn, dim3(grid), dim3(kQT), args, 0, s, start, stop, 0);
     return hipLaunchKernel(fn, dim3(grid), dim3(kQT), args, 0, s);
 }

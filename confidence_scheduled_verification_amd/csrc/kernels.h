@@ -151,15 +151,20 @@ struct StepArgs {
 };
 
 // Candidate-pruned chain (cand.hip).  Limits of that path: K <= kCandMaxK positions and
-// V <= kCandMaxItems * 4096 entries per row.
+// V <= kCandMaxItems * kCandItemLong entries per row.  Rows of at most kCandShortRowMaxV
+// entries are streamed in items of kCandItemShort entries (a finer deal keeps more waves
+// busy when a row has few items), longer rows in items of kCandItemLong.
 constexpr int kCandMaxK = 32;
 constexpr int kCandMaxItems = 64;
-constexpr int kCandItem = 4096;           // base entries per streaming item
+constexpr int kCandItemLong = 4096;       // base entries per streaming item
+constexpr int kCandItemShort = 2048;
+constexpr int kCandShortRowMaxV = 32768;
 constexpr int kCandGroups = 8192;         // kept 8-entry groups a request's LDS pool holds
 constexpr int kCandMaxGroups = 256;       // workgroups of one launch at most
 constexpr size_t kMarkovHeaderBytes = 256;  // prepared state: bound scalars, then Bt
 
-inline int cand_items_per_row(int V) { return (V + kCandItem - 1) / kCandItem; }
+inline int cand_item(int V) { return V <= kCandShortRowMaxV ? kCandItemShort : kCandItemLong; }
+inline int cand_items_per_row(int V) { return (V + cand_item(V) - 1) / cand_item(V); }
 
 // With fewer requests than compute units a request is streamed by S <= kSplitMax
 // workgroups: its owner (which also runs the chain) and S - 1 helpers, each taking a
@@ -194,6 +199,7 @@ struct CandArgs {
     const void* hdr;   // prepared bound scalars (device)
     const int32_t* prev0;
     int R, K, V, rank, NC;
+    int item;  // base entries per item (cand_item(V)); NC = items per row
     int32_t* tokens;
     uint32_t* status;
     int S;                // workgroups per request (1: one workgroup takes whole requests)
