@@ -43,9 +43,10 @@
 // Chain (wave 7), concurrently, at raised issue priority.  Position by position it waits
 // for the row's count to reach its item count, lists the entries of the row's kept groups
 // that clear the row's final floor, and scores them with the key row of the previous
-// token, two lanes per candidate with the whole Bt rows of up to 64 candidates in flight
-// at once (x = value + the dot product, each lane's half by fused multiply-adds in
-// increasing k, then the halves added).  The key row of the next position is prefetched
+// token, eight lanes per candidate (each load instruction reads whole 128-byte lines of
+// eight Bt rows) with the Bt rows of up to 64 candidates in flight at once (x = value +
+// the dot product: each lane's chunks by fused multiply-adds in increasing k, then the
+// eight lanes' sums added as a tree).  The key row of the next position is prefetched
 // for the row's largest entry -- the token unless the bias reorders the top -- while the
 // row is scored, and loaded again only when that guess misses.  So the chain keeps up
 // with the streaming, and only the last row's scoring is left once the last item arrives.
@@ -641,30 +642,34 @@ __device__ __forceinline__ u32x2 row_quad(const uint16_t* __restrict__ M, int u,
     return 4 * lane < rank ? *(const u32x2*)(M + (size_t)u * rank + 4 * lane) : u32x2{0u, 0u};
 }
 
-// Candidates are scored two lanes each: lane pair (2c, 2c+1) takes candidate c, the even
-// lane rank entries [0, rank/2), the odd lane the rest.  kQHalf = the 16-byte groups a
-// lane holds (rank <= 256).
-constexpr int kQHalf = 16;
+// Candidates are scored eight lanes each: lanes 8c .. 8c+7 of the wave take candidate c of
+// a pass (8 candidates per pass).  A Bt row of rank entries is rank/8 16-byte chunks;
+// chunk j belongs to lane j mod 8, as its (j div 8)-th, so that each load instruction of
+// the pass reads whole 128-byte lines of the 8 rows.  kQRounds = the chunks a lane holds
+// per row (rank <= 256); kQPasses = the passes whose loads are in flight together.
+constexpr int kQRounds = 4;
+constexpr int kQPasses = 8;
 
-// This lane's half of Bt row v (rank/16 16-byte groups).
-__device__ __forceinline__ void load_bt_half(u32x4 (&bt)[kQHalf], const uint16_t* __restrict__ Bt, int v, int rank) {
-    const int half = threadIdx.x & 1, ng = rank / 16;
-    const u32x4* b = (const u32x4*)(Bt + (size_t)v * rank) + half * ng;
+// This lane's chunks of Bt row v.
+__device__ __forceinline__ void load_bt_part(u32x4 (&bt)[kQRounds], const uint16_t* __restrict__ Bt, int v, int rank) {
+    const int l = threadIdx.x & 7, nch = rank / 8;
+    const u32x4* b = (const u32x4*)(Bt + (size_t)v * rank);
 #pragma unroll
-    for (int g = 0; g < kQHalf; ++g) bt[g] = g < ng ? b[g] : u32x4{0u, 0u, 0u, 0u};
+    for (int g = 0; g < kQRounds; ++g) bt[g] = g * 8 + l < nch ? b[g * 8 + l] : u32x4{0u, 0u, 0u, 0u};
 }
 
-// x for this lane pair's entry: fl32(value + the dot product of the key row in L.akey and
-// the Bt row, each half by fused multiply-adds in increasing k, then the two halves
-// added).  Both lanes of the pair end with the same value.
-__device__ __forceinline__ float pair_x(const QLds& L, const u32x4 (&bt)[kQHalf], int rank, float value) {
-    const int half = threadIdx.x & 1, ng = rank / 16;
-    const u32x4* k = (const u32x4*)L.akey + half * ng;
+// x for this lane group's entry: fl32(value + the dot product of the key row in L.akey and
+// the Bt row).  Each lane sums its chunks' products by fused multiply-adds in increasing k;
+// the eight lanes' sums are then added as a tree (neighbours, then pairs, then quads), the
+// same way round in every lane, so that all eight end with the same value.
+__device__ __forceinline__ float oct_x(const QLds& L, const u32x4 (&bt)[kQRounds], int rank, float value) {
+    const int l = threadIdx.x & 7, nch = rank / 8;
+    const u32x4* k = (const u32x4*)L.akey;
     float acc = 0.f;
 #pragma unroll
-    for (int g = 0; g < kQHalf; ++g) {
-        if (g < ng) {
-            const u32x4 kv = k[g], bv = bt[g];
+    for (int g = 0; g < kQRounds; ++g) {
+        if (g * 8 + l < nch) {
+            const u32x4 kv = k[g * 8 + l], bv = bt[g];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 acc = __builtin_fmaf(__uint_as_float(kv[d] << 16), __uint_as_float(bv[d] << 16), acc);
@@ -672,45 +677,57 @@ __device__ __forceinline__ float pair_x(const QLds& L, const u32x4 (&bt)[kQHalf]
             }
         }
     }
-    const float other = dpp_f32(acc, kDppXor1);  // the pair's other lane
-    return value + (half ? other + acc : acc + other);
+    // lane pairs, then pairs of pairs, then the two quads (lane i <-> 7 - i); each sum is
+    // formed with the lower lanes' part first, so both partners compute the same value
+    float o = dpp_f32(acc, kDppXor1);
+    acc = (l & 1) ? o + acc : acc + o;
+    o = dpp_f32(acc, kDppXor2);
+    acc = (l & 2) ? o + acc : acc + o;
+    o = dpp_f32(acc, kDppHalfMirror);
+    acc = (l & 4) ? o + acc : acc + o;
+    return value + acc;
 }
 
-// Row `row` scored over the whole vocabulary with the key row in L.akey, 32 entries at a
+// Candidates c0 + 8p + (lane div 8), p < kQPasses, of a list of n scored into best: all
+// their Bt loads in flight together.  at(c) gives candidate c's (index, value bits) key as
+// the list stores it.
+template <typename At>
+__device__ __forceinline__ void score_passes(const QLds& L, uint32_t c0, uint32_t n, const uint16_t* __restrict__ Bt,
+                                             int rank, At at, uint64_t& best) {
+    const uint32_t grp = (threadIdx.x & 63) >> 3;
+    u32x4 bt[kQPasses][kQRounds];
+    uint64_t e[kQPasses];
+#pragma unroll
+    for (int p = 0; p < kQPasses; ++p) {
+        const uint32_t c = c0 + 8u * (uint32_t)p + grp;
+        e[p] = at(c < n ? c : c0);
+        if (c0 + 8u * (uint32_t)p < n) load_bt_part(bt[p], Bt, (int)(e[p] >> 32), rank);
+    }
+#pragma unroll
+    for (int p = 0; p < kQPasses; ++p) {
+        if (c0 + 8u * (uint32_t)p < n) {
+            const uint32_t c = c0 + 8u * (uint32_t)p + grp;
+            const float x = oct_x(L, bt[p], rank, __uint_as_float((uint32_t)e[p]));
+            if (c < n) best = umax64(best, argmax_key(x, (uint32_t)(e[p] >> 32)));
+        }
+    }
+}
+
+// Row `row` scored over the whole vocabulary with the key row in L.akey, 64 entries at a
 // time.  Returns the argmax key (every lane alike).
 __device__ __forceinline__ uint64_t dense_row(const QLds& L, const uint16_t* __restrict__ bp, int V,
                                               const uint16_t* __restrict__ Bt, int rank) {
-    const int pair = (threadIdx.x & 63) >> 1;
     uint64_t best = 0ull;
-    for (int v0 = 0; v0 < V; v0 += 32) {
-        const int v = v0 + pair < V ? v0 + pair : V - 1;
-        u32x4 bt[kQHalf];
-        load_bt_half(bt, Bt, v, rank);
-        const float x = pair_x(L, bt, rank, __uint_as_float((uint32_t)bp[v] << 16));
-        if (v0 + pair < V) best = umax64(best, argmax_key(x, (uint32_t)v));
-    }
+    auto at = [&](uint32_t v) -> uint64_t { return ((uint64_t)v << 32) | ((uint32_t)bp[v] << 16); };
+    for (uint32_t v0 = 0; v0 < (uint32_t)V; v0 += 8u * kQPasses) score_passes(L, v0, (uint32_t)V, Bt, rank, at, best);
     return wave_max_u64(best);
 }
 
-// Scores L.clist[0, n) with the key row in L.akey into best, 64 candidates at a time
-// (lane pair p takes candidates p and p + 32; all their Bt loads are in flight together).
+// Scores L.clist[0, n) with the key row in L.akey into best, 64 candidates at a time.
 __device__ __forceinline__ void score_list(const QLds& L, uint32_t n, const uint16_t* __restrict__ Bt, int rank,
                                            uint64_t& best) {
-    const uint32_t pair = (threadIdx.x & 63) >> 1;
-    for (uint32_t c0 = 0; c0 < n; c0 += 64) {
-        const uint32_t c = c0 + pair, c2 = c + 32;
-        const uint64_t e = c < n ? L.clist[c] : L.clist[c0];
-        const uint64_t e2 = c2 < n ? L.clist[c2] : L.clist[c0];
-        u32x4 bt[kQHalf], bt2[kQHalf];
-        load_bt_half(bt, Bt, (int)(e >> 32), rank);
-        if (c0 + 32 < n) load_bt_half(bt2, Bt, (int)(e2 >> 32), rank);
-        const float x = pair_x(L, bt, rank, __uint_as_float((uint32_t)e));
-        if (c < n) best = umax64(best, argmax_key(x, (uint32_t)(e >> 32)));
-        if (c0 + 32 < n) {
-            const float x2 = pair_x(L, bt2, rank, __uint_as_float((uint32_t)e2));
-            if (c2 < n) best = umax64(best, argmax_key(x2, (uint32_t)(e2 >> 32)));
-        }
-    }
+    auto at = [&](uint32_t c) -> uint64_t { return L.clist[c]; };
+    for (uint32_t c0 = 0; c0 < n; c0 += 8u * kQPasses) score_passes(L, c0, n, Bt, rank, at, best);
 }
 
 // Bound on the norm of the key row this wave holds (lane l: entries 4l .. 4l+3): the

@@ -165,8 +165,10 @@ int dspark_markov_prepare(dspark_markov_t* m, const void* A, const void* Bmat, i
  * DSPARK_PRUNED_MAX_K and V <= DSPARK_PRUNED_MAX_V runs the pruned chain by default:
  * one streaming pass over base keeps each row's entries within the bias bound of its
  * maximum (the only ones that can win), then every request's chain scores those
- * candidates alone (fp32 fused multiply-adds in increasing k over each half of the
- * rank, then the two halves added, lower half first).  Rows the bound cannot prune (a non-finite bound, more
+ * candidates alone (the rank split into 16-byte chunks dealt over eight lanes, chunk j
+ * to lane j mod 8; each lane's products summed by fp32 fused multiply-adds in increasing
+ * k, then the eight sums added as a tree: neighbours, pairs, quads, lower part first).
+ * Rows the bound cannot prune (a non-finite bound, more
  * candidates than the buffers hold) are scored over the whole vocabulary, so the
  * tokens never depend on how well the bound prunes.  Otherwise (and in the dense form)
  * bf16 products are summed in fp32 by the matrix cores over the whole vocabulary;
